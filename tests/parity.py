@@ -1,0 +1,63 @@
+"""Comparison gates for rotated Q/K (test helpers; no method arithmetic).
+
+fp32 gate: for every rotated element, |got - ref| / ||(ref_j, ref_{j+32})||_2 <= 2e-6, the pair
+norm being that of the reference pair (it equals the input pair's norm, a rotation preserves it, so
+the bound never divides by a value near zero; a pair of zeros must come out exactly zero).  Dims
+past the rotary part must be bit-identical.
+
+bf16 gate: the ordered-integer distance between the bf16 bit patterns of got and of the fp32 oracle
+rounded to bf16 is at most 1 (one ulp; -0 and +0 are the same point).  Dims past the rotary part
+bit-identical.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROT = 64
+HALF = 32
+FP32_TOL = 2e-6
+BF16_ULP = 1
+
+
+def pair_rel_err(got, ref, rot: int = ROT) -> np.ndarray:
+    got = np.asarray(got, np.float64)[..., :rot]
+    ref = np.asarray(ref, np.float64)[..., :rot]
+    h = rot // 2
+    norm = np.sqrt(ref[..., :h] ** 2 + ref[..., h:] ** 2)
+    norm = np.concatenate([norm, norm], axis=-1)
+    diff = np.abs(got - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(norm > 0, diff / norm, np.where(diff > 0, np.inf, 0.0))
+    return err
+
+
+def check_fp32(got, ref, tol: float = FP32_TOL, rot: int = ROT):
+    got = np.asarray(got, np.float32)
+    ref = np.asarray(ref, np.float32)
+    err = pair_rel_err(got, ref, rot)
+    worst = float(err.max()) if err.size else 0.0
+    tail_ok = np.array_equal(got[..., rot:].view(np.uint32), ref[..., rot:].view(np.uint32))
+    absmax = float(np.abs(ref[..., :rot]).max()) if err.size else 0.0
+    scaled = float(np.abs(got[..., :rot].astype(np.float64) - ref[..., :rot]).max() / absmax) if absmax else 0.0
+    return (worst <= tol and tail_ok), {"max_pair_rel": worst, "tail_bit_exact": tail_ok,
+                                        "max_abs_over_absmax": scaled}
+
+
+def _ordered(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b, np.uint16).astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def bf16_ulp_dist(got_bits, ref_bits) -> np.ndarray:
+    return np.abs(_ordered(got_bits) - _ordered(ref_bits))
+
+
+def check_bf16(got_bits, ref_bits, max_ulp: int = BF16_ULP, rot: int = ROT):
+    got_bits = np.asarray(got_bits, np.uint16)
+    ref_bits = np.asarray(ref_bits, np.uint16)
+    d = bf16_ulp_dist(got_bits[..., :rot], ref_bits[..., :rot])
+    worst = int(d.max()) if d.size else 0
+    tail_ok = np.array_equal(got_bits[..., rot:], ref_bits[..., rot:])
+    return (worst <= max_ulp and tail_ok), {"max_ulp": worst, "n_off_by_one": int((d == 1).sum()),
+                                           "tail_bit_exact": tail_ok}

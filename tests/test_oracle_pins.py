@@ -1,0 +1,355 @@
+"""Pins that hold the CPU oracle to the pages and to mathematics (not to itself).
+
+Every pin is chosen so that a plausible slip in the oracle -- a dropped frame token, a wrong shift,
+an off-by-one in the grid, a swapped plane, a wrong sign in the rotation, the wrong rotary pairing,
+a wrong frequency exponent -- fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from canvas_rope_rotary_amd import synth
+from parity import check_fp32, pair_rel_err
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden")
+MARKER = synth.IMAGE_ID
+
+
+def _one(n, origin, seed=0):
+    ids = synth.prompt_ids(synth.rng(seed, 99), n, origin)
+    pl, st, am, og = oracle.planes(ids, [0, n], MARKER)
+    return ids, pl, int(st[0]), int(am[0]), int(og[0])
+
+
+# ---------------------------------------------------------------- values printed on the pages ---
+
+def test_worked_example_start_amount():
+    """Card: O = 6, 6, 6, 17 -> start = 73, 73, 73, 84, amount = 58."""
+    g = json.load(open(os.path.join(GOLDEN, "canvas_worked_example.json")))
+    for row in g["image_prompts"]:
+        _, _, st, am, og = _one(160, row["origin"])
+        assert (og, st, am) == (row["origin"], row["start"], row["amount"])
+        # zoo page / kit: start = index where the 64 pads begin + 66
+        assert st == (row["origin"] + 1) + g["pads_begin_plus"]
+
+
+def test_worked_example_planes_o6():
+    """Rows of the canvas table read off by hand for O = 6 (tests/golden/canvas_planes_o6.txt)."""
+    rows = []
+    for line in open(os.path.join(GOLDEN, "canvas_planes_o6.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            rows.append([int(v) for v in line.split()[:4]])
+    _, pl, st, am, _ = _one(110, 6)
+    assert (st, am) == (73, 58)
+    for p, t, h, w in rows:
+        assert tuple(pl[:, p]) == (t, h, w), p
+
+
+def test_text_only_sentinel():
+    """Card: a text-only prompt sends start = 2^30, amount = 0; every position gets (p, p, p)."""
+    g = json.load(open(os.path.join(GOLDEN, "canvas_worked_example.json")))["text_only"]
+    for n in (1, 2, 67, 500):
+        _, pl, st, am, og = _one(n, None)
+        assert (st, am, og) == (g["start"], g["amount"], -1)
+        ramp = np.arange(n, dtype=np.int32)
+        for r in range(3):
+            np.testing.assert_array_equal(pl[r], ramp)
+
+
+def test_amount_identity():
+    """amount = start - (O + 9), 9 = max(H, W) + 1 over the canvas (card, start/amount paragraph)."""
+    g = json.load(open(os.path.join(GOLDEN, "canvas_worked_example.json")))
+    for o in (0, 1, 6, 17, 300, 4000):
+        _, pl, st, am, og = _one(o + 100, o)
+        assert am == st - (o + g["extent_plus_one"])
+        frame = pl[1:, o:st]
+        assert int(frame.max()) + 1 == o + g["extent_plus_one"]
+
+
+# ---------------------------------------------------------------- brute force on the canvas ---
+
+def _grid_table():
+    """The 8x8 merged grid as a [64, 2] (row, col) table built by nested loops, row-major
+    (card: "k = 0..63, row-major over the 8x8 merged grid")."""
+    t = []
+    for r in range(8):
+        for c in range(8):
+            t.append((r, c))
+    return np.array(t, np.int32)
+
+
+def test_grid_enumeration():
+    o = 10
+    _, pl, *_ = _one(200, o)
+    rows = pl[:, o + 1:o + 65]
+    assert (rows[0] == o).all()
+    hw = np.stack([rows[1] - o, rows[2] - o], axis=1)
+    np.testing.assert_array_equal(hw, _grid_table())
+    assert len({tuple(x) for x in hw}) == 64
+
+
+def _walk_planes(n, origin):
+    """Independent formulation: walk the prompt token by token.  Text counts up one position per
+    token; the frame sits on a canvas at O ([64,2] grid table, </image> one past the grid's corner,
+    the "\\n" back at the origin); the text after the frame resumes one past the largest canvas
+    coordinate and counts up again ("the text after it resumes past the canvas", card "What it is")."""
+    out = np.zeros((3, n), np.int32)
+    grid = _grid_table()
+    if origin is None:
+        origin = n
+    nxt = 0
+    canvas_max = None
+    for p in range(n):
+        i = p - origin
+        if p < origin:
+            v = (nxt, nxt, nxt)
+            nxt += 1
+        elif i == 0:
+            v = (origin, origin - 1, origin - 1)
+        elif 1 <= i <= 64:
+            r, c = grid[i - 1]
+            v = (origin, origin + r, origin + c)
+        elif i == 65:
+            v = (origin, origin + 8, origin + 8)
+        elif i == 66:
+            v = (origin, origin, origin)
+        else:
+            if canvas_max is None:
+                canvas_max = max(int(out[:, origin:p].max()), origin)
+                nxt = canvas_max + 1
+            v = (nxt, nxt, nxt)
+            nxt += 1
+        out[:, p] = v
+    return out
+
+
+@pytest.mark.parametrize("n", list(range(1, 161, 7)) + [66, 67, 68, 160])
+def test_brute_force_all_origins(n):
+    """For every origin that fits (and frames cut off by the end, and no marker at all), the oracle
+    equals the token walk bit for bit."""
+    origins = [None] + list(range(0, n))
+    for o in origins:
+        _, pl, st, am, og = _one(n, o, seed=n)
+        np.testing.assert_array_equal(pl, _walk_planes(n, o), err_msg=f"n={n} O={o}")
+
+
+def test_invariants_random_batch():
+    b = synth.random_batch(7, 200, max_len=400, text_frac=0.3)
+    pl, st, am, og = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    for s in range(b.n_seqs):
+        lo, hi = b.cu_seqlens[s], b.cu_seqlens[s + 1]
+        T = pl[0, lo:hi]
+        assert (np.diff(T) >= 0).all()
+        o = og[s]
+        if o < 0:
+            assert st[s] == 1 << 30 and am[s] == 0
+            continue
+        assert am[s] == 58 and st[s] == o + 67
+        seg = T[o:min(o + 67, hi - lo)]
+        assert (seg == o).all()
+        if st[s] < hi - lo:
+            assert pl[:, lo + st[s]].tolist() == [o + 9] * 3
+
+
+def test_first_marker_wins():
+    ids = synth.prompt_ids(synth.rng(1, 98), 300, 20, extra_markers=(150,))
+    pl, st, am, og = oracle.planes(ids, [0, 300], MARKER)
+    assert og[0] == 20 and st[0] == 87
+    assert pl[:, 150].tolist() == [92, 92, 92]
+
+
+# ---------------------------------------------------------------- sections and frequencies ---
+
+def test_section_masks():
+    """Card "What it is": planes share the frequencies in interleaved sections [11, 11, 10]."""
+    sel = [oracle.plane_of_freq(j) for j in range(32)]
+    assert [sel.count(r) for r in range(3)] == [11, 11, 10]
+    assert sel[:30] == [0, 1, 2] * 10          # interleaved T, H, W
+    assert sel[30:] == [0, 1]
+
+
+def test_inv_freq_matches_fp32_torch_construction():
+    """The oracle's table equals the fp32 buffer a torch rotary builds (fp32 exponent, fp32 pow,
+    fp32 reciprocal) for theta = 1e7, 64 rotary dims."""
+    hf = (1.0 / (1e7 ** (torch.arange(0, 64, 2, dtype=torch.int64).float() / 64))).numpy()
+    np.testing.assert_array_equal(oracle.inv_freq(1e7, 64).view(np.uint32), hf.view(np.uint32))
+
+
+def test_inv_freq_closed_forms():
+    f = oracle.inv_freq(1e7, 64).astype(np.float64)
+    assert f[0] == 1.0
+    assert (np.diff(f) < 0).all()
+    # theta^(-1/2) at j = 16
+    assert abs(f[16] - 1.0 / math.sqrt(1e7)) <= 1.2e-7 * f[16]
+    # inv[j] * inv[32 - j] = theta^(-1)
+    for j in range(1, 32):
+        assert abs(f[j] * f[32 - j] - 1e-7) <= 3e-7 * 1e-7, j
+    # consecutive ratio theta^(-1/32)
+    r = 1e7 ** (-1.0 / 32)
+    assert np.max(np.abs(f[1:] / f[:-1] - r)) <= 3e-7
+
+
+# ---------------------------------------------------------------- rotation closed forms ---
+
+def _rand_heads(seed, T, H=3, D=256):
+    return synth.normal(seed, 50, T * H * D).reshape(T, H, D)
+
+
+def test_zero_positions_identity():
+    x = _rand_heads(1, 5)
+    y = oracle.rotate(x, np.zeros((3, 5), np.int32))
+    np.testing.assert_array_equal(y.view(np.uint32), x.view(np.uint32))
+
+
+def test_unit_vectors_rotate_half():
+    """e_j -> (cos a_j at dim j, sin a_j at dim j+32); e_{j+32} -> (-sin a_j, cos a_j)."""
+    p = 1234
+    inv = oracle.inv_freq(1e7, 64)
+    for j in (0, 1, 2, 15, 31):
+        x = np.zeros((2, 1, 256), np.float32)
+        x[0, 0, j] = 1.0
+        x[1, 0, j + 32] = 1.0
+        y = oracle.rotate(x, np.full((3, 2), p, np.int32))
+        a = float(np.float32(np.float32(p) * inv[j]))
+        c, s = math.cos(a), math.sin(a)
+        assert abs(y[0, 0, j] - c) < 1e-7 and abs(y[0, 0, j + 32] - s) < 1e-7
+        assert abs(y[1, 0, j] + s) < 1e-7 and abs(y[1, 0, j + 32] - c) < 1e-7
+        others = np.delete(np.arange(256), [j, j + 32])
+        assert (y[:, 0, others] == 0).all()
+
+
+def test_one_hot_planes_move_only_their_sections():
+    x = _rand_heads(2, 1)
+    sel = np.array([oracle.plane_of_freq(j) for j in range(32)])
+    for plane in range(3):
+        pl = np.zeros((3, 1), np.int32)
+        pl[plane] = 1000
+        y = oracle.rotate(x, pl)
+        moved = ~np.isclose(y[0, :, :32], x[0, :, :32], rtol=0, atol=0) | ~np.isclose(
+            y[0, :, 32:64], x[0, :, 32:64], rtol=0, atol=0)
+        moved_freqs = moved.any(axis=0)
+        np.testing.assert_array_equal(moved_freqs, sel == plane)
+
+
+def test_inverse_rotation_and_norm():
+    """Rotating by planes then by the negated planes returns x; pair norms are preserved."""
+    T = 64
+    x = _rand_heads(3, T)
+    g = synth.rng(3, 97)
+    pl = g.integers(-30000, 30000, size=(3, T)).astype(np.int32)
+    y = oracle.rotate(x, pl)
+    z = oracle.rotate(y, -pl)
+    assert pair_rel_err(z, x).max() <= 2e-7
+    n_in = np.hypot(x[..., :32].astype(np.float64), x[..., 32:64])
+    n_out = np.hypot(y[..., :32].astype(np.float64), y[..., 32:64])
+    assert np.max(np.abs(n_out - n_in) / n_in) <= 2e-7
+    np.testing.assert_array_equal(y[..., 64:], x[..., 64:])
+
+
+def _rope_1d_torch(x, pos, theta=1e7, rot=64):
+    """Textbook 1-D RoPE, rotate-half convention, in plain torch fp32 (the text decoder's rotary)."""
+    xt = torch.from_numpy(x)
+    # the model's rotary keeps inv_freq as an fp32 buffer built in fp32 arithmetic
+    inv = 1.0 / (theta ** (torch.arange(0, rot, 2, dtype=torch.int64).float() / rot))
+    ang = torch.from_numpy(pos.astype(np.float32))[:, None] * inv[None, :]
+    emb = torch.cat([ang, ang], dim=-1)
+    cos, sin = emb.cos()[:, None, :], emb.sin()[:, None, :]
+    r = xt[..., :rot]
+    x1, x2 = r[..., : rot // 2], r[..., rot // 2:]
+    rh = torch.cat([-x2, x1], dim=-1)
+    out = xt.clone()
+    out[..., :rot] = r * cos + rh * sin
+    return out.numpy()
+
+
+def test_text_only_equals_1d_rope():
+    """Zoo page: with start = 2^30 and amount = 0 the module equals the plain text decoder; a
+    text-only prompt's M-RoPE is the textbook 1-D RoPE."""
+    n = 3000
+    ids, pl, st, am, og = _one(n, None)
+    x = _rand_heads(4, n)
+    y = oracle.rotate(x, pl)
+    ref = _rope_1d_torch(x, np.arange(n))
+    err = pair_rel_err(y, ref)
+    # the torch reference computes cos/sin in fp32 (|angle| up to 3000 rad): a few fp32 ulps of the
+    # angle's magnitude at most.
+    assert err.max() < 2e-6
+    np.testing.assert_array_equal(y[..., 64:], x[..., 64:])
+
+
+def test_matrix_form():
+    """Rotation as an explicit 64x64 matrix (block rotation of pairs (j, j+32)) times x."""
+    T = 16
+    x = _rand_heads(5, T, H=2)
+    g = synth.rng(5, 96)
+    pl = g.integers(0, 20000, size=(3, T)).astype(np.int32)
+    y = oracle.rotate(x, pl)
+    inv = oracle.inv_freq(1e7, 64)
+    for t in range(T):
+        R = np.zeros((64, 64))
+        for j in range(32):
+            pos = pl[oracle.plane_of_freq(j), t]
+            a = float(np.float32(np.float32(pos) * inv[j]))
+            R[j, j], R[j, j + 32] = math.cos(a), -math.sin(a)
+            R[j + 32, j], R[j + 32, j + 32] = math.sin(a), math.cos(a)
+        ref = x[t, :, :64].astype(np.float64) @ R.T
+        assert np.max(np.abs(y[t, :, :64] - ref)) < 1e-6
+
+
+# ---------------------------------------------------------------- decode and rounding ---
+
+def test_decode_matches_prefill_planes():
+    """Generated tokens sit at p - amount on all planes: a decode step at position p equals the
+    prefill rotation of the token at position p of the same image prompt."""
+    n, o = 400, 30
+    ids, pl, st, am, og = _one(n, o)
+    p = 350
+    x = _rand_heads(6, 1, H=3)
+    xk = _rand_heads(7, 1, H=2)
+    ref_q = oracle.rotate(x, pl[:, p:p + 1])
+    ref_k = oracle.rotate(xk, pl[:, p:p + 1])
+    cache = np.zeros((4, 16, 2, 256), np.float32)
+    qo = oracle.decode(x, xk, [p], [am], cache, [2 * 16 + 5], 16)
+    np.testing.assert_array_equal(qo, ref_q)
+    np.testing.assert_array_equal(cache[2, 5], ref_k[0])
+    assert (cache[[0, 1, 3]] == 0).all() and (np.delete(cache[2], 5, axis=0) == 0).all()
+
+
+def test_round_bf16_against_torch():
+    x = synth.normal(8, 51, 100000)
+    x[:4] = [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]   # ties to even
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.round_bf16(x), ref)
+
+
+# ---------------------------------------------------------------- red arms ---
+
+def test_red_arms_fail():
+    """Zoo page: amount + 1 and 1-D planes must fail the plane gate and the rotation gate on every
+    image prompt that has text after the frame."""
+    b = synth.random_batch(11, 40, max_len=400, min_len=120, text_frac=0.0)
+    pl, st, am, og = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    L = b.n_tokens
+    x = _rand_heads(9, L, H=1)
+    y = oracle.rotate(x, pl)
+    for s in range(b.n_seqs):
+        lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
+        if og[s] < 0 or st[s] >= hi - lo:
+            continue
+        sl = slice(lo, hi)
+        p = np.arange(hi - lo, dtype=np.int32)
+        wrong_shift = pl[:, sl].copy()
+        wrong_shift[:, p >= st[s]] -= 1          # amount + 1
+        one_d = np.stack([p, p, p])
+        for arm in (wrong_shift, one_d):
+            assert not np.array_equal(arm, pl[:, sl])
+            ya = oracle.rotate(x[sl], arm)
+            ok, _ = check_fp32(ya, y[sl])
+            assert not ok
