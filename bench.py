@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the canvas M-RoPE hot path on one MI355X.
+
+A step is one pass of the whole prefill path over one batch: mrope_planes (token ids -> first
+marker per sequence -> (T, H, W) planes, start, amount) and mrope_apply (rotate-half of the first
+64 dims of Q [L, 8, 256] and K [L, 2, 256], bf16, in place).  Workload: 64 image prompts of 4096
+tokens (262,144 tokens), <image> at O ~ U{0..512}, Q/K ~ N(0, 1) from a fixed seed, inputs resident
+in HBM before the timed region.
+
+Prints one JSON line: tokens/s over the timed steps, the roofline of the dominant kernel
+(mrope_apply: algorithmic bytes / mean launch time from HIP events on its stream, against 8 TB/s),
+and the CPU oracle timed on this host over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "canvas M-RoPE Q+K tokens/sec and achieved HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "mrope_apply_64x4096_bf16_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "canvas_rope_rotary_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes_apply(tokens: int, heads: int = 10, rot_dim: int = 64, elem: int = 2) -> int:
+    """Bytes mrope_apply must move in place: the rotated dims of every head read and written once,
+    plus the three int32 planes of every token read once."""
+    return tokens * (heads * rot_dim * elem * 2 + 3 * 4)
+
+
+def algorithmic_bytes_planes(tokens: int) -> int:
+    """ids read (4 B) and three int32 planes written (12 B) per token."""
+    return tokens * 16
+
+
+def traffic_from_counters(launch_tokens: int):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, scaled by the
+    copy-kernel calibration -- only if it was taken on the current kernel sources."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_hash() or c.get("tokens") != launch_tokens:
+        return None
+    return int(c["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(b, qn, kn, min_seconds: float = 10.0, max_passes: int = 8):
+    """The oracle, as it stands, over the whole workload on this host's cores (single-threaded),
+    repeated until at least `min_seconds` of work; tokens/s."""
+    import numpy as np
+
+    import oracle
+    from canvas_rope_rotary_amd import synth
+
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        pl, st, am, og = oracle.planes(b.ids, b.cu_seqlens, synth.IMAGE_ID)
+        for x in (qn, kn):
+            y = oracle.rotate(synth.bf16_bits_to_f32(x), pl)
+            oracle.round_bf16(y)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or passes >= max_passes:
+            break
+    del np
+    return {"value": passes * b.n_tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole workload ({b.n_tokens} tokens, planes + Q/K rotation + bf16 rounding), "
+                      f"{passes} pass(es), {el:.1f} s, one thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the method shards by "
+              "sequence or head with no communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import canvas_rope_rotary_amd as mr
+    from canvas_rope_rotary_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mr._lib.load()
+
+    b = synth.config2()
+    log(f"workload {b.name}: {b.n_tokens} tokens, {b.n_seqs} sequences; generating inputs")
+    qn, kn = b.qk()
+    ids = torch.from_numpy(b.ids).to(dev)
+    cu = torch.from_numpy(b.cu_seqlens).to(dev)
+    q = torch.from_numpy(qn.view(np.int16)).view(torch.bfloat16).to(dev)
+    k = torch.from_numpy(kn.view(np.int16)).view(torch.bfloat16).to(dev)
+    L = b.n_tokens
+    planes = torch.empty((3, L), dtype=torch.int32, device=dev)
+    start = torch.empty(b.n_seqs, dtype=torch.int32, device=dev)
+    amount = torch.empty_like(start)
+    origin = torch.empty_like(start)
+    flags = torch.empty_like(start)
+    ws = mr.Workspace(L, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        mr.planes(ids, cu, synth.IMAGE_ID, out=planes, start=start, amount=amount, origin=origin,
+                  seq_flags=flags, workspace=ws)
+        if ev is not None:
+            ev[0].record(stream)
+        mr.apply(q, k, planes)
+        if ev is not None:
+            ev[1].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    apply_ms = [a.elapsed_time(bb) for a, bb in evs]
+    apply_mean_s = sum(apply_ms) / len(apply_ms) / 1e3
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step), "
+        f"mrope_apply {apply_mean_s * 1e6:.1f} us/launch")
+
+    # planes kernel alone (context, not the roofline)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for _ in range(args.steps):
+        mr.planes(ids, cu, synth.IMAGE_ID, out=planes, start=start, amount=amount, origin=origin,
+                  seq_flags=flags, workspace=ws)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    planes_us = p0.elapsed_time(p1) / args.steps * 1e3
+
+    # plain device-to-device copy of 1 GiB: the practical streaming ceiling on this machine (context)
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 2 * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del src, dst
+
+    ab = algorithmic_bytes_apply(L)
+    achieved = ab / apply_mean_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": L * args.steps / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "64 image prompts x 4096 tokens, bf16: planes from int32 ids + in-place "
+                               "rotary of Q[262144,8,256] and K[262144,2,256]",
+                   "tokens": L, "seqs": b.n_seqs, "q_heads": 8, "k_heads": 2, "head_dim": 256, "rot_dim": 64,
+                   "theta": 1e7, "sections": [11, 11, 10]},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(L),
+                     "kernel": "mrope_apply", "algorithmic_bytes_per_launch": ab,
+                     "mean_launch_us": apply_mean_s * 1e6},
+        "kernels_us": {"mrope_planes": planes_us, "mrope_apply": apply_mean_s * 1e6},
+        "planes_gbs": algorithmic_bytes_planes(L) / (planes_us / 1e6) / 1e9,
+        "copy_ceiling_gbs": copy_gbs,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(b, qn, kn, min_seconds=args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,286 @@
+"""ctypes binding of libmrope.so: argument checks and marshalling only (see include/mrope.h)."""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmrope.so")
+_lib = None
+
+MROPE_F32 = 0
+MROPE_BF16 = 1
+TEXT_ONLY_START = 1 << 30
+ROT_DIM = 64
+
+# every symbol include/mrope.h declares
+EXPORTS = ("mrope_abi_version", "mrope_status_string", "mrope_last_error", "mrope_workspace_bytes",
+           "mrope_workspace_init", "mrope_planes", "mrope_apply", "mrope_apply_ids", "mrope_decode")
+
+
+class MarkerFlags(enum.IntFlag):
+    MULTI_MARKER = 1
+    FRAME_OVERRUN = 2
+    LOOKBACK_TIMEOUT = 4
+
+
+class MropeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libmrope.so (built in-tree by canvas_rope_rotary_amd.build).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m canvas_rope_rotary_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, U64, F64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+    lib.mrope_abi_version.argtypes = []
+    lib.mrope_abi_version.restype = ctypes.c_int
+    lib.mrope_status_string.argtypes = [ctypes.c_int]
+    lib.mrope_status_string.restype = ctypes.c_char_p
+    lib.mrope_last_error.argtypes = []
+    lib.mrope_last_error.restype = ctypes.c_char_p
+    lib.mrope_workspace_bytes.argtypes = [I64]
+    lib.mrope_workspace_bytes.restype = U64
+    lib.mrope_workspace_init.argtypes = [P, U64, P]
+    lib.mrope_workspace_init.restype = ctypes.c_int
+    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, P, I64, P, P, P, P, P, U64, P]
+    lib.mrope_planes.restype = ctypes.c_int
+    lib.mrope_apply.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, P, I64, F64, P, P, P]
+    lib.mrope_apply.restype = ctypes.c_int
+    lib.mrope_apply_ids.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
+                                    P, P, I32, I32, P, I64, P, P, P, P, P, U64, P]
+    lib.mrope_apply_ids.restype = ctypes.c_int
+    lib.mrope_decode.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I32, P, P, P, P, I32, I64, I64, I64, I64,
+                                 I32, I32, I32, F64, P]
+    lib.mrope_decode.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load()
+        raise MropeError(status, f"{lib.mrope_status_string(status).decode()}: {lib.mrope_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MROPE_BF16
+    if t.dtype == torch.float32:
+        return MROPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _require_cuda(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on a CUDA (HIP) device")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _heads(t: torch.Tensor, name: str):
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [tokens, heads, head_dim]")
+    if t.stride(2) != 1:
+        raise ValueError(f"{name}: head_dim must be contiguous")
+    return t.stride(0), t.stride(1), t.shape[1], t.shape[2]
+
+
+def _i32_vec(t: torch.Tensor, name: str, n: int | None = None):
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 1-D int32 tensor")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements")
+    return t
+
+
+def cu_seqlens_from_lens(lens: torch.Tensor) -> torch.Tensor:
+    """Sequence lengths [n] -> cu_seqlens [n + 1] int32 (0, then the running sum)."""
+    out = torch.zeros(lens.numel() + 1, dtype=torch.int32, device=lens.device)
+    torch.cumsum(lens.to(torch.int32), 0, out=out[1:])
+    return out
+
+
+class Workspace:
+    """Device workspace of the plane-deriving calls, zero-filled once, reusable across calls on one
+    stream (the library keeps it consistent between calls)."""
+
+    def __init__(self, n_tokens: int, device=None):
+        self.device = torch.device(device if device is not None else "cuda")
+        self.capacity = 0
+        self.buf = None
+        self.ensure(n_tokens)
+
+    def ensure(self, n_tokens: int):
+        need = int(load().mrope_workspace_bytes(int(n_tokens)))
+        if self.buf is not None and need <= self.capacity:
+            return self
+        buf = torch.zeros(need + 256, dtype=torch.uint8, device=self.device)
+        off = (-buf.data_ptr()) % 256
+        self.buf = buf
+        self.view = buf[off:off + need]
+        self.capacity = need
+        return self
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.view.data_ptr())
+
+
+_default_ws: dict = {}
+
+
+def _workspace(ws, n_tokens, device):
+    if ws is None:
+        ws = _default_ws.get(device)
+        if ws is None:
+            ws = _default_ws[device] = Workspace(n_tokens, device)
+    return ws.ensure(n_tokens)
+
+
+def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078, *, out=None, start=None,
+           amount=None, origin=None, seq_flags=None, workspace: Workspace | None = None):
+    """Canvas planes from token ids.  Returns (planes [3, L] int32, start [n], amount [n], origin [n],
+    seq_flags [n]).  cu_seqlens[-1] must equal len(ids)."""
+    dev = _require_cuda(ids, cu_seqlens, out, start, amount, origin, seq_flags)
+    _i32_vec(ids, "ids")
+    _i32_vec(cu_seqlens, "cu_seqlens")
+    L = ids.numel()
+    n = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty((3, L), dtype=torch.int32, device=dev)
+    if out.dtype != torch.int32 or out.dim() != 2 or out.shape[0] != 3 or out.shape[1] < L or out.stride(1) != 1:
+        raise ValueError("out must be an int32 [3, >= L] tensor with unit column stride")
+    mk = lambda t, name: _i32_vec(t, name, n) if t is not None else torch.empty(n, dtype=torch.int32, device=dev)
+    start, amount, origin, seq_flags = (mk(start, "start"), mk(amount, "amount"), mk(origin, "origin"),
+                                        mk(seq_flags, "seq_flags"))
+    ws = _workspace(workspace, L, dev)
+    with torch.cuda.device(dev):
+        _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), _ptr(out), out.stride(0),
+                                   _ptr(start), _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr,
+                                   ws.capacity, _stream(dev)))
+    return out, start, amount, origin, seq_flags
+
+
+def _qk_args(q, k, q_out, k_out):
+    dt = _dtype_code(q)
+    if k is not None and k.dtype != q.dtype:
+        raise TypeError("q and k must have the same dtype")
+    qt, qh, nq, D = _heads(q, "q")
+    if k is not None:
+        kt, kh, nk, Dk = _heads(k, "k")
+        if Dk != D or k.shape[0] != q.shape[0]:
+            raise ValueError("q and k must have the same tokens and head_dim")
+    else:
+        kt = kh = nk = 0
+    for o, src, name in ((q_out, q, "q_out"), (k_out, k, "k_out")):
+        if o is not None:
+            if src is None or o.shape != src.shape or o.stride() != src.stride() or o.dtype != src.dtype:
+                raise ValueError(f"{name} must match its input's shape, strides and dtype")
+    return dt, qt, qh, nq, kt, kh, nk, D
+
+
+def apply(q: torch.Tensor, k: torch.Tensor | None, planes_: torch.Tensor, theta: float = 1e7, *, q_out=None,
+          k_out=None, rot_dim: int = ROT_DIM):
+    """Rotate Q and K ([T, heads, head_dim], bf16 or fp32) with planes [3, >= T] int32.  In place
+    unless q_out / k_out are given (then full heads are written there).  Returns (q, k) as written."""
+    dev = _require_cuda(q, k, planes_, q_out, k_out)
+    dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, q_out, k_out)
+    T = q.shape[0]
+    if planes_.dtype != torch.int32 or planes_.dim() != 2 or planes_.shape[0] != 3 or planes_.shape[1] < T \
+            or planes_.stride(1) != 1:
+        raise ValueError("planes must be an int32 [3, >= tokens] tensor with unit column stride")
+    with torch.cuda.device(dev):
+        _check(load().mrope_apply(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, _ptr(planes_),
+                                  planes_.stride(0), float(theta), _ptr(q_out), _ptr(k_out), _stream(dev)))
+    return (q_out if q_out is not None else q), (k_out if k_out is not None else k)
+
+
+def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seqlens: torch.Tensor,
+              marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
+              origin=None, seq_flags=None, q_out=None, k_out=None, workspace: Workspace | None = None,
+              rot_dim: int = ROT_DIM):
+    """Plane derivation fused with the rotation, one launch.  Returns (start, amount, origin,
+    seq_flags, planes_out or None)."""
+    dev = _require_cuda(q, k, ids, cu_seqlens, planes_out, start, amount, origin, seq_flags, q_out, k_out)
+    dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, q_out, k_out)
+    _i32_vec(ids, "ids", q.shape[0])
+    _i32_vec(cu_seqlens, "cu_seqlens")
+    T = q.shape[0]
+    n = cu_seqlens.numel() - 1
+    ps = 0
+    if planes_out is not None:
+        if planes_out.dtype != torch.int32 or planes_out.dim() != 2 or planes_out.shape[0] != 3 \
+                or planes_out.shape[1] < T or planes_out.stride(1) != 1:
+            raise ValueError("planes_out must be an int32 [3, >= tokens] tensor with unit column stride")
+        ps = planes_out.stride(0)
+    mk = lambda t, name: _i32_vec(t, name, n) if t is not None else torch.empty(n, dtype=torch.int32, device=dev)
+    start, amount, origin, seq_flags = (mk(start, "start"), mk(amount, "amount"), mk(origin, "origin"),
+                                        mk(seq_flags, "seq_flags"))
+    ws = _workspace(workspace, T, dev)
+    with torch.cuda.device(dev):
+        _check(load().mrope_apply_ids(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, float(theta),
+                                      _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
+                                      _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
+                                      _ptr(seq_flags), ws.ptr, ws.capacity, _stream(dev)))
+    return start, amount, origin, seq_flags, planes_out
+
+
+def decode(q: torch.Tensor, k: torch.Tensor | None, pos: torch.Tensor, amount: torch.Tensor,
+           k_cache: torch.Tensor | None, slot_mapping: torch.Tensor | None, theta: float = 1e7, *,
+           rot_dim: int = ROT_DIM):
+    """One generated token per sequence: rotate q [S, Hq, D] in place at plane pos - amount; rotate
+    k [S, Hk, D] and write it into k_cache [num_blocks, block_size, Hk, D] at slot_mapping (int64,
+    slot < 0 skips)."""
+    dev = _require_cuda(q, k, pos, amount, k_cache, slot_mapping)
+    dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, None, None)
+    S = q.shape[0]
+    _i32_vec(pos, "pos", S)
+    _i32_vec(amount, "amount", S)
+    if nk:
+        if k_cache is None or slot_mapping is None:
+            raise ValueError("k_cache and slot_mapping are required with k")
+        if k_cache.dim() != 4 or k_cache.shape[2] != nk or k_cache.shape[3] != D or k_cache.stride(3) != 1 \
+                or k_cache.dtype != q.dtype:
+            raise ValueError("k_cache must be [num_blocks, block_size, n_k_heads, head_dim] of q's dtype")
+        if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or slot_mapping.numel() != S \
+                or not slot_mapping.is_contiguous():
+            raise ValueError("slot_mapping must be a contiguous int64 [S] tensor")
+        nb, bs = k_cache.shape[0], k_cache.shape[1]
+        cb, ct, ch = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    else:
+        nb, bs, cb, ct, ch = 0, 1, 0, 0, 0
+    with torch.cuda.device(dev):
+        _check(load().mrope_decode(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, S, _ptr(pos), _ptr(amount),
+                                   _ptr(k_cache), _ptr(slot_mapping), bs, nb, cb, ct, ch, D, rot_dim, dt,
+                                   float(theta), _stream(dev)))
+    return q, k_cache

@@ -1,0 +1,71 @@
+// Internal launch interface between the C ABI (mrope_abi.hip) and the kernels (mrope_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mrope {
+
+constexpr int kMaxHeads = 64;
+constexpr int kTile = 64;               // tokens per scan tile: one wavefront, one lane per token
+constexpr size_t kWsHeaderBytes = 256;  // ticket, finish counter, epoch (+ padding)
+
+// Rotary constants: 32 fp32 inverse frequencies and the plane each frequency reads, 2 bits per
+// frequency (0 = T, 1 = H, 2 = W).
+struct Rotary {
+    float inv_freq[32];
+    uint64_t plane_sel;
+};
+
+// Q/K heads of one call.  Element (t, h, d) of q is at q + t*q_tok + h*q_head + d (elements).
+struct Heads {
+    void *q;
+    void *k;
+    void *q_out;   // nullptr: in place
+    void *k_out;
+    int64_t q_tok, q_head, k_tok, k_head;
+    int32_t nq, nk;
+    int32_t head_dim;
+    int64_t n_tokens;
+};
+
+// Plane derivation: ids + packed sequences -> planes / scalars through a workspace.
+struct Scan {
+    const int32_t *ids;
+    const int32_t *cu;
+    int32_t n_seqs;
+    int32_t marker;
+    int64_t n_tokens;
+    int32_t *planes;     // nullable in the fused kernel
+    int64_t plane_stride;
+    int32_t *start;      // nullable
+    int32_t *amount;     // nullable
+    int32_t *origin;     // nullable
+    int32_t *flags;      // nullable
+    void *workspace;
+};
+
+struct DecodeArgs {
+    void *q;
+    const void *k;
+    int64_t q_tok, q_head, k_tok, k_head;
+    int32_t nq, nk, head_dim;
+    int32_t n_seqs;
+    const int32_t *pos;
+    const int32_t *amount;
+    void *cache;
+    const int64_t *slots;
+    int32_t block_size;
+    int64_t num_slots;
+    int64_t c_block, c_tok, c_head;
+};
+
+hipError_t launch_workspace_init(void *ws, size_t bytes, hipStream_t stream);
+hipError_t launch_text_scalars(const Scan &s, hipStream_t stream);
+hipError_t launch_planes(const Scan &s, hipStream_t stream);
+hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t plane_stride, bool bf16,
+                        hipStream_t stream);
+hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, bool bf16, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, bool bf16, hipStream_t stream);
+
+}  // namespace mrope

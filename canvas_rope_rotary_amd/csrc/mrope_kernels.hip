@@ -1,0 +1,683 @@
+// libmrope kernels for gfx950 (CDNA4, wave64).
+//
+// What is computed (the pages):
+//   Hugging Face card "MiniCPM-V-4.7-1B -- Core AI", section "How the VLM rides the text-only engine":
+//   the canvas table (planes per position for one 448x448 image after plain text), start and amount;
+//   section "What it is": three planes T, H, W sharing the rotary frequencies in interleaved sections
+//   [11, 11, 10].  Core AI model-zoo page "MiniCPM-V-4.7-1B: canvas M-RoPE on the Qwen3.5 hybrid, on
+//   Core AI", section "The canvas rule and why the gate is on the planes".
+//
+// Kernels
+//   planes_kernel     ids -> first marker per sequence (ballot + decoupled look-back) -> planes, scalars
+//   apply_kernel      planes -> cos/sin on the fly -> rotate-half of Q and K (the HBM stream)
+//   apply_ids_kernel  the two above in one launch; planes stay in LDS
+//   decode_kernel     one token per sequence: Q in place, K rotated and scattered to a paged cache
+//
+// Thread layout of the rotary kernels: four lanes per token, lane quarter q4 owns frequencies
+// 8*q4 .. 8*q4+7, i.e. dims [8*q4, 8*q4+8) and [32+8*q4, 32+8*q4+8) of every head.  A lane computes
+// its 8 (cos, sin) pairs once and applies them to all heads of its token, so each sincos is done once
+// per token, with no LDS traffic and no cross-lane exchange.  Each head is one 128-byte line (bf16):
+// the four lanes of a token read it as two 64-byte runs.
+#include "mrope_internal.h"
+#include "mrope_math.h"
+
+namespace mrope {
+namespace {
+
+// ------------------------------------------------------------------ the canvas rule ------------
+constexpr int kGrid = 8;                      // 8x8 merged grid of one 448x448 image
+constexpr int kRows = kGrid * kGrid;          // 64 image rows, row-major
+constexpr int kFrameLen = 1 + kRows + 1 + 1;  // <image>, rows, </image>, "\n"  -> start = O + 67
+constexpr int kExtent = kGrid + 1;            // largest H/W offset on the canvas (</image>) + 1
+constexpr int kAmount = kFrameLen - kExtent;  // amount = start - (O + 9) = 58
+constexpr int32_t kTextStart = 1 << 30;       // text-only prompt: start = 2^30, amount = 0
+constexpr int32_t kNone = 0x7fffffff;         // "no marker"
+
+// Planes of position p; o = in-sequence index of the first marker at or before p, kNone if none.
+__device__ __forceinline__ void canvas_planes(int32_t p, int32_t o, int32_t &t, int32_t &h, int32_t &w)
+{
+    if (o == kNone) {
+        t = h = w = p;
+        return;
+    }
+    const int32_t d = p - o;
+    if (d >= kFrameLen) {
+        t = h = w = p - kAmount;
+        return;
+    }
+    t = o;
+    if (d == 0) {                 // <image>
+        h = w = o - 1;
+    } else if (d <= kRows) {      // image row k = d - 1
+        h = o + ((d - 1) >> 3);
+        w = o + ((d - 1) & 7);
+    } else if (d == kRows + 1) {  // </image>
+        h = w = o + kGrid;
+    } else {                      // the "\n" after </image>
+        h = w = o;
+    }
+}
+
+// ------------------------------------------------------------------ workspace ------------------
+struct WsHeader {
+    uint32_t ticket;  // next tile index to hand out
+    uint32_t done;    // participants finished in this launch
+    uint32_t epoch;   // launch counter; tags the status words of this launch
+    uint32_t error;   // sticky: bit 0 = a look-back gave up
+};
+
+// status word of a tile: [63:34] epoch | [33:32] flag | [31] multi | [30:0] first marker (global idx)
+constexpr uint64_t kAgg = 1;   // value covers only this tile's part of its last sequence
+constexpr uint64_t kIncl = 2;  // value covers the whole sequence up to the end of this tile
+constexpr uint32_t kEpochMask = 0x3fffffffu;
+constexpr uint32_t kSpinLimit = 1u << 21;
+
+__device__ __forceinline__ uint64_t status_word(uint32_t epoch, uint64_t flag, bool multi, int32_t first)
+{
+    return ((uint64_t)(epoch & kEpochMask) << 34) | (flag << 32) | ((uint64_t)(multi ? 1u : 0u) << 31) |
+           (uint64_t)((uint32_t)first & 0x7fffffffu);
+}
+
+__device__ __forceinline__ uint64_t *status_array(void *ws)
+{
+    return reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + kWsHeaderBytes);
+}
+
+template <typename T>
+__device__ __forceinline__ T aload(T *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void astore(T *p, T v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One participant (a wave or a workgroup) of a scan launch is done with the workspace.  The last
+// one resets the ticket and finish counters and advances the epoch for the next launch.
+__device__ __forceinline__ void finish_participant(WsHeader *hdr, uint32_t participants, uint32_t epoch)
+{
+    const uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == participants - 1) {
+        astore(&hdr->ticket, 0u);
+        astore(&hdr->done, 0u);
+        astore(&hdr->epoch, (epoch + 1u) & kEpochMask);
+    }
+}
+
+// ------------------------------------------------------------------ wave helpers ---------------
+__device__ __forceinline__ int32_t wave_min(int32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Largest s in [0, n_seqs] with cu[s] <= g (n_seqs when g is past the last sequence), -1 if none.
+__device__ __forceinline__ int32_t seq_of(const int32_t *cu, int32_t n_seqs, int64_t g)
+{
+    int32_t lo = 0, hi = n_seqs + 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if ((int64_t)cu[mid] <= g)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo - 1;
+}
+
+// Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan with Decoupled
+// Look-back", 2016) with a (first marker, more-than-one) operator.  The whole wave reads the status
+// words of the 64 preceding tiles at once; it combines everything up to the nearest tile that holds
+// an inclusive value, or slides 64 tiles further back when none does.  The tile where the sequence
+// begins always publishes an inclusive value, so the walk ends there.  Every wait is bounded.
+__device__ void lookback(const uint64_t *status, int64_t tile, uint32_t epoch, int lane, int32_t &first,
+                         bool &multi, bool &timed_out)
+{
+    first = kNone;
+    multi = false;
+    timed_out = false;
+    int64_t base = tile - 1;
+    uint32_t spins = 0;
+    const uint32_t ep = epoch & kEpochMask;
+    while (true) {
+        const int64_t idx = base - lane;
+        const uint64_t w = idx >= 0 ? aload(const_cast<uint64_t *>(status) + idx) : status_word(ep, kIncl, false, kNone);
+        const uint64_t flag = (w >> 32) & 3u;
+        const bool ready = (uint32_t)(w >> 34) == ep && flag != 0;
+        const uint64_t incl_mask = __ballot(ready && flag == kIncl);
+        const uint64_t ready_mask = __ballot(ready);
+        const int lim = incl_mask ? __builtin_ctzll(incl_mask) : 63;
+        const uint64_t need = lim >= 63 ? ~0ull : ((2ull << lim) - 1);
+        if ((ready_mask & need) == need) {
+            const bool use = lane <= lim;
+            const int32_t v = use ? (int32_t)(w & 0x7fffffffu) : kNone;
+            const uint64_t has = __ballot(use && v != kNone);
+            const bool mm = __ballot(use && ((w >> 31) & 1u)) != 0;
+            const int cnt = __builtin_popcountll(has) + (first != kNone ? 1 : 0);
+            multi = multi || mm || cnt >= 2;
+            first = min(first, wave_min(v));
+            if (incl_mask) return;
+            base -= 64;
+        } else {
+            if (++spins > kSpinLimit) {
+                timed_out = true;
+                return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+}
+
+struct TokenPos {
+    int32_t p;      // position in its sequence
+    int32_t o;      // in-sequence index of the first marker at or before p, kNone if none
+    bool valid;     // the token belongs to a sequence
+};
+
+__device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t origin, bool multi, int64_t len,
+                                              bool timed_out)
+{
+    const bool img = origin >= 0;
+    if (sc.start) sc.start[s] = img ? origin + kFrameLen : kTextStart;
+    if (sc.amount) sc.amount[s] = img ? kAmount : 0;
+    if (sc.origin) sc.origin[s] = img ? origin : -1;
+    if (sc.flags)
+        sc.flags[s] = (multi ? 1 : 0) | ((img && (int64_t)origin + kFrameLen > len) ? 2 : 0) | (timed_out ? 4 : 0);
+}
+
+// Scan of one 64-token tile by one full wave, lane i <-> token tile*64 + i.  Publishes the tile's
+// status word, looks back when the tile's first sequence began earlier, writes the scalars of every
+// sequence that ends in the tile, and returns each lane's position and canvas origin.
+__device__ TokenPos scan_tile(const Scan &sc, uint64_t *status, WsHeader *hdr, int64_t tile, uint32_t epoch, int lane)
+{
+    const int64_t t0 = tile * kTile;
+    const int64_t g = t0 + lane;
+    const bool in_range = g < sc.n_tokens;
+    const int32_t s = in_range ? seq_of(sc.cu, sc.n_seqs, g) : -1;
+    const bool in_seq = in_range && s >= 0 && s < sc.n_seqs;
+    int64_t sb = 0, se = 0;
+    if (in_seq) {
+        sb = sc.cu[s];
+        se = sc.cu[s + 1];
+    }
+    const bool is_marker = in_seq && sc.ids[g] == sc.marker;
+    const uint64_t mk = __ballot(is_marker);
+
+    // lanes of this token's sequence inside the tile: [lo, hi), always containing the lane itself
+    int lo = lane, hi = lane + 1;
+    if (in_seq) {
+        lo = (int)max<int64_t>(0, min<int64_t>(sb - t0, lane));
+        hi = (int)min<int64_t>(kTile, max<int64_t>(se - t0, lane + 1));
+    }
+    const uint64_t seg = (hi >= 64 ? ~0ull : ((1ull << hi) - 1)) & ~((1ull << lo) - 1);
+    const uint64_t m = mk & seg;
+    int32_t first = m ? (int32_t)(t0 + __builtin_ctzll(m)) : kNone;
+    bool multi = __builtin_popcountll(m) >= 2;
+
+    const int last = (int)min<int64_t>(kTile - 1, sc.n_tokens - 1 - t0);
+    const int32_t first_last = __shfl(first, last);
+    const bool multi_last = __shfl((int)multi, last) != 0;
+    const int32_t s_last = __shfl(s, last);
+    const int32_t s0 = __shfl(s, 0);
+    const bool need_carry = __shfl((int)(in_seq && sb < t0), 0) != 0;
+    const bool last_open = need_carry && s_last == s0;  // the tile's last sequence began before it
+
+    if (lane == 0)
+        astore(status + tile, status_word(epoch, last_open ? kAgg : kIncl, multi_last, first_last));
+
+    bool timed_out = false;
+    if (need_carry) {
+        int32_t cf;
+        bool cm;
+        lookback(status, tile, epoch, lane, cf, cm, timed_out);
+        if (last_open && lane == 0) {
+            const bool mm = cm || multi_last || (cf != kNone && first_last != kNone);
+            astore(status + tile, status_word(epoch, kIncl, mm, min(cf, first_last)));
+        }
+        if (in_seq && s == s0) {
+            multi = multi || cm || (cf != kNone && first != kNone);
+            first = min(first, cf);
+        }
+        if (timed_out && lane == 0) atomicOr(&hdr->error, 1u);
+    }
+
+    TokenPos r;
+    r.valid = in_seq;
+    r.p = (int32_t)(g - sb);
+    r.o = (in_seq && first != kNone && first <= g) ? (int32_t)(first - sb) : kNone;
+
+    if (in_seq && g == se - 1) {
+        write_scalars(sc, s, first == kNone ? -1 : (int32_t)(first - sb), multi, se - sb, timed_out && s == s0);
+        for (int32_t s2 = s + 1; s2 < sc.n_seqs && sc.cu[s2 + 1] == sc.cu[s2]; ++s2)
+            write_scalars(sc, s2, -1, false, 0, false);
+    }
+    if (in_seq && g == 0)
+        for (int32_t s2 = 0; s2 < s; ++s2) write_scalars(sc, s2, -1, false, 0, false);
+    return r;
+}
+
+// ------------------------------------------------------------------ element I/O ----------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    const f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// 8 consecutive elements as raw 16-byte words: one for bf16, two for fp32.
+template <bool BF16>
+struct Raw8 {
+    uint4 w[BF16 ? 1 : 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load8(const void *base, int64_t elem)
+{
+    Raw8<BF16> r;
+    if constexpr (BF16) {
+        r.w[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
+    } else {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
+        r.w[0] = p[0];
+        r.w[1] = p[1];
+    }
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store8(void *base, int64_t elem, const Raw8<BF16> &r)
+{
+    if constexpr (BF16) {
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + elem) = r.w[0];
+    } else {
+        uint4 *p = reinterpret_cast<uint4 *>(static_cast<float *>(base) + elem);
+        p[0] = r.w[0];
+        p[1] = r.w[1];
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16> &r, float (&x)[8])
+{
+    if constexpr (BF16) {
+        const uint32_t u[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(u[i] << 16);
+            x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    } else {
+        const uint32_t u[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(u[i]);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> pack8(const float (&y)[8])
+{
+    Raw8<BF16> r;
+    if constexpr (BF16) {
+        r.w[0] = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                            pack_bf16x2(y[6], y[7]));
+    } else {
+        r.w[0] = make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3]));
+        r.w[1] = make_uint4(__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7]));
+    }
+    return r;
+}
+
+// ------------------------------------------------------------------ rotary ---------------------
+// (cos, sin) of the 8 frequencies of quarter q4 for planes (pt, ph, pw).
+__device__ __forceinline__ void quarter_sincos(const Rotary &rot, int q4, int32_t pt, int32_t ph, int32_t pw,
+                                               float (&c)[8], float (&s)[8])
+{
+    const uint32_t sel = (uint32_t)(rot.plane_sel >> (16 * q4));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t pl = (sel >> (2 * i)) & 3u;
+        const int32_t pos = pl == 1u ? ph : (pl == 2u ? pw : pt);
+        const float f = q4 == 0 ? rot.inv_freq[i]
+                      : q4 == 1 ? rot.inv_freq[8 + i]
+                      : q4 == 2 ? rot.inv_freq[16 + i]
+                                : rot.inv_freq[24 + i];
+        const float a = (float)pos * f;
+        sincos_angle(a, &s[i], &c[i]);
+    }
+}
+
+// Rotate-half on 8 pairs: lo holds dims j, hi holds dims j + 32.
+template <bool BF16>
+__device__ __forceinline__ void rotate8(Raw8<BF16> &lo, Raw8<BF16> &hi, const float (&c)[8], const float (&s)[8])
+{
+    float a[8], b[8];
+    unpack8<BF16>(lo, a);
+    unpack8<BF16>(hi, b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x1 = a[i], x2 = b[i];
+        a[i] = __builtin_fmaf(x1, c[i], -(x2 * s[i]));
+        b[i] = __builtin_fmaf(x2, c[i], x1 * s[i]);
+    }
+    lo = pack8<BF16>(a);
+    hi = pack8<BF16>(b);
+}
+
+// Copy this quarter's share of the dims past the rotary part (out-of-place calls only).
+template <bool BF16>
+__device__ __forceinline__ void copy_tail(const void *src, void *dst, int64_t off, int head_dim, int q4)
+{
+    for (int d = 64 + 8 * q4; d < head_dim; d += 32) store8<BF16>(dst, off + d, load8<BF16>(src, off + d));
+}
+
+// All heads of one token-quarter: loads first (all in flight), then sincos, then rotate + store.
+template <bool BF16, int NQ, int NK>
+__device__ __forceinline__ void rotate_token_fixed(const Heads &hd, int64_t g, int q4, const float (&c)[8],
+                                                   const float (&s)[8], Raw8<BF16> (&ql)[NQ], Raw8<BF16> (&qh)[NQ],
+                                                   Raw8<BF16> (&kl)[NK], Raw8<BF16> (&kh)[NK])
+{
+    void *qo = hd.q_out ? hd.q_out : hd.q;
+    void *ko = hd.k_out ? hd.k_out : hd.k;
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+        const int64_t off = g * hd.q_tok + h * hd.q_head + 8 * q4;
+        rotate8<BF16>(ql[h], qh[h], c, s);
+        store8<BF16>(qo, off, ql[h]);
+        store8<BF16>(qo, off + 32, qh[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < NK; ++h) {
+        const int64_t off = g * hd.k_tok + h * hd.k_head + 8 * q4;
+        rotate8<BF16>(kl[h], kh[h], c, s);
+        store8<BF16>(ko, off, kl[h]);
+        store8<BF16>(ko, off + 32, kh[h]);
+    }
+    if (hd.q_out) {
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) copy_tail<BF16>(hd.q, hd.q_out, g * hd.q_tok + h * hd.q_head, hd.head_dim, q4);
+#pragma unroll
+        for (int h = 0; h < NK; ++h) copy_tail<BF16>(hd.k, hd.k_out, g * hd.k_tok + h * hd.k_head, hd.head_dim, q4);
+    }
+}
+
+template <bool BF16, int NQ, int NK>
+__device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int q4, Raw8<BF16> (&ql)[NQ],
+                                                 Raw8<BF16> (&qh)[NQ], Raw8<BF16> (&kl)[NK], Raw8<BF16> (&kh)[NK])
+{
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) {
+        const int64_t off = g * hd.q_tok + h * hd.q_head + 8 * q4;
+        ql[h] = load8<BF16>(hd.q, off);
+        qh[h] = load8<BF16>(hd.q, off + 32);
+    }
+#pragma unroll
+    for (int h = 0; h < NK; ++h) {
+        const int64_t off = g * hd.k_tok + h * hd.k_head + 8 * q4;
+        kl[h] = load8<BF16>(hd.k, off);
+        kh[h] = load8<BF16>(hd.k, off + 32);
+    }
+}
+
+// Any head counts: one head at a time.
+template <bool BF16>
+__device__ __forceinline__ void rotate_token_any(const Heads &hd, int64_t g, int q4, const float (&c)[8],
+                                                 const float (&s)[8])
+{
+    for (int hh = 0; hh < hd.nq + hd.nk; ++hh) {
+        const bool isq = hh < hd.nq;
+        const int h = isq ? hh : hh - hd.nq;
+        void *src = isq ? hd.q : hd.k;
+        void *dst = isq ? (hd.q_out ? hd.q_out : hd.q) : (hd.k_out ? hd.k_out : hd.k);
+        const int64_t base = isq ? g * hd.q_tok + h * hd.q_head : g * hd.k_tok + h * hd.k_head;
+        const int64_t off = base + 8 * q4;
+        Raw8<BF16> lo = load8<BF16>(src, off), hi = load8<BF16>(src, off + 32);
+        rotate8<BF16>(lo, hi, c, s);
+        store8<BF16>(dst, off, lo);
+        store8<BF16>(dst, off + 32, hi);
+        if (hd.q_out) copy_tail<BF16>(src, dst, base, hd.head_dim, q4);
+    }
+}
+
+// ------------------------------------------------------------------ kernels --------------------
+constexpr int kBlock = 256;           // 4 waves
+constexpr int kTokPerBlock = kBlock / 4;
+
+template <bool BF16, int NQ, int NK>
+__global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
+                                                       int64_t ps)
+{
+    const int tid = threadIdx.x;
+    const int q4 = tid & 3;
+    const int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 2);
+    if (g >= hd.n_tokens) return;
+    const int32_t pt = planes[g], ph = planes[ps + g], pw = planes[2 * ps + g];
+    float c[8], s[8];
+    if constexpr (NQ > 0 && NK > 0) {
+        Raw8<BF16> ql[NQ], qh[NQ], kl[NK], kh[NK];
+        load_token_fixed<BF16, NQ, NK>(hd, g, q4, ql, qh, kl, kh);
+        quarter_sincos(rot, q4, pt, ph, pw, c, s);
+        rotate_token_fixed<BF16, NQ, NK>(hd, g, q4, c, s, ql, qh, kl, kh);
+    } else {
+        quarter_sincos(rot, q4, pt, ph, pw, c, s);
+        rotate_token_any<BF16>(hd, g, q4, c, s);
+    }
+}
+
+__global__ __launch_bounds__(kTile) void planes_kernel(Scan sc, uint32_t n_tiles)
+{
+    const int lane = threadIdx.x;
+    WsHeader *hdr = static_cast<WsHeader *>(sc.workspace);
+    uint64_t *status = status_array(sc.workspace);
+    uint32_t tk = 0, ep = 0;
+    if (lane == 0) {
+        tk = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ep = aload(&hdr->epoch);
+    }
+    tk = __shfl(tk, 0);
+    ep = __shfl(ep, 0);
+    if (tk < n_tiles) {
+        const TokenPos r = scan_tile(sc, status, hdr, tk, ep, lane);
+        if (r.valid) {
+            int32_t t, h, w;
+            canvas_planes(r.p, r.o, t, h, w);
+            const int64_t g = (int64_t)tk * kTile + lane;
+            sc.planes[g] = t;
+            sc.planes[sc.plane_stride + g] = h;
+            sc.planes[2 * sc.plane_stride + g] = w;
+        }
+    }
+    if (lane == 0) finish_participant(hdr, n_tiles, ep);
+}
+
+template <bool BF16, int NQ, int NK>
+__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, uint32_t n_tiles)
+{
+    __shared__ uint32_t s_tile, s_epoch;
+    __shared__ int32_t s_pl[3][kTile];
+    __shared__ int32_t s_ok[kTile];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int q4 = tid & 3;
+    WsHeader *hdr = static_cast<WsHeader *>(sc.workspace);
+    if (tid == 0) {
+        s_tile = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_epoch = aload(&hdr->epoch);
+    }
+    __syncthreads();
+    const uint32_t tile = s_tile, ep = s_epoch;
+    const bool live = tile < n_tiles;
+    const int64_t g = (int64_t)tile * kTile + (tid >> 2);
+    const bool tok_ok = live && g < hd.n_tokens;
+
+    // Q/K loads go out before the scan so the look-back hides behind them.
+    constexpr bool kFixed = NQ > 0 && NK > 0;
+    constexpr int AQ = kFixed ? NQ : 1, AK = kFixed ? NK : 1;
+    Raw8<BF16> ql[AQ], qh[AQ], kl[AK], kh[AK];
+    if constexpr (kFixed) {
+        if (tok_ok) load_token_fixed<BF16, AQ, AK>(hd, g, q4, ql, qh, kl, kh);
+    }
+
+    if (tid < 64) {
+        int32_t t = 0, h = 0, w = 0;
+        bool ok = false;
+        if (live) {
+            const TokenPos r = scan_tile(sc, status_array(sc.workspace), hdr, tile, ep, lane);
+            ok = r.valid;
+            if (ok) {
+                canvas_planes(r.p, r.o, t, h, w);
+                if (sc.planes) {
+                    const int64_t gg = (int64_t)tile * kTile + lane;
+                    sc.planes[gg] = t;
+                    sc.planes[sc.plane_stride + gg] = h;
+                    sc.planes[2 * sc.plane_stride + gg] = w;
+                }
+            }
+        }
+        s_pl[0][lane] = t;
+        s_pl[1][lane] = h;
+        s_pl[2][lane] = w;
+        s_ok[lane] = ok;
+    }
+    __syncthreads();
+    if (tid == 0) finish_participant(hdr, n_tiles, ep);
+
+    const int tl = tid >> 2;
+    if (!tok_ok || !s_ok[tl]) return;
+    float c[8], s[8];
+    quarter_sincos(rot, q4, s_pl[0][tl], s_pl[1][tl], s_pl[2][tl], c, s);
+    if constexpr (kFixed) {
+        rotate_token_fixed<BF16, AQ, AK>(hd, g, q4, c, s, ql, qh, kl, kh);
+    } else {
+        rotate_token_any<BF16>(hd, g, q4, c, s);
+    }
+}
+
+// One wave per sequence.  Work items of a wave: Q rotation (nq*4 quarters, in place), K rotation
+// (nk*4 quarters, to the cache) and K pass-through copies (16-byte chunks past the rotary dims).
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t s = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    if (s >= d.n_seqs) return;
+    const int32_t plane = d.pos[s] - d.amount[s];
+    const int64_t slot = d.slots[s];
+    const bool wr = slot >= 0 && slot < d.num_slots;
+    const int64_t cbase = wr ? (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok : 0;
+    const int nrq = d.nq * 4, nrk = d.nk * 4;
+    const int chunks = (d.head_dim - 64) / 8;
+    const int total = nrq + nrk + d.nk * chunks;
+    for (int it = lane; it < total; it += 64) {
+        if (it < nrq + nrk) {
+            const bool isq = it < nrq;
+            const int h = (isq ? it : it - nrq) >> 2;
+            const int q4 = it & 3;
+            const int64_t off = isq ? s * d.q_tok + h * d.q_head + 8 * q4 : s * d.k_tok + h * d.k_head + 8 * q4;
+            const void *src = isq ? d.q : d.k;
+            Raw8<BF16> lo = load8<BF16>(src, off), hi = load8<BF16>(src, off + 32);
+            float c[8], sn[8];
+            quarter_sincos(rot, q4, plane, plane, plane, c, sn);
+            rotate8<BF16>(lo, hi, c, sn);
+            if (isq) {
+                store8<BF16>(d.q, off, lo);
+                store8<BF16>(d.q, off + 32, hi);
+            } else if (wr) {
+                const int64_t co = cbase + h * d.c_head + 8 * q4;
+                store8<BF16>(d.cache, co, lo);
+                store8<BF16>(d.cache, co + 32, hi);
+            }
+        } else if (wr) {
+            const int c = it - nrq - nrk;
+            const int h = c / chunks;
+            const int e = 64 + (c % chunks) * 8;
+            store8<BF16>(d.cache, cbase + h * d.c_head + e, load8<BF16>(d.k, s * d.k_tok + h * d.k_head + e));
+        }
+    }
+}
+
+__global__ void zero_kernel(uint32_t *p, size_t words)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+__global__ void text_scalars_kernel(Scan sc)
+{
+    const int32_t s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < sc.n_seqs) write_scalars(sc, s, -1, false, 0, false);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers ------------------
+hipError_t launch_workspace_init(void *ws, size_t bytes, hipStream_t stream)
+{
+    const size_t words = bytes / 4;
+    const size_t want = (words + 255) / 256;
+    const unsigned blocks = (unsigned)(want > 1024 ? 1024 : (want ? want : 1));
+    if (words) zero_kernel<<<blocks, 256, 0, stream>>>(static_cast<uint32_t *>(ws), words);
+    return hipGetLastError();
+}
+
+hipError_t launch_text_scalars(const Scan &s, hipStream_t stream)
+{
+    text_scalars_kernel<<<(s.n_seqs + 255) / 256, 256, 0, stream>>>(s);
+    return hipGetLastError();
+}
+
+hipError_t launch_planes(const Scan &s, hipStream_t stream)
+{
+    const uint32_t n_tiles = (uint32_t)((s.n_tokens + kTile - 1) / kTile);
+    planes_kernel<<<n_tiles, kTile, 0, stream>>>(s, n_tiles);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, hipStream_t st)
+{
+    const unsigned blocks = (unsigned)((h.n_tokens + kTokPerBlock - 1) / kTokPerBlock);
+    if (h.nq == 8 && h.nk == 2)
+        apply_kernel<BF16, 8, 2><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
+    else
+        apply_kernel<BF16, 0, 0><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, bool bf16,
+                        hipStream_t stream)
+{
+    return bf16 ? apply_dispatch<true>(h, r, planes, ps, stream) : apply_dispatch<false>(h, r, planes, ps, stream);
+}
+
+template <bool BF16>
+static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, hipStream_t st)
+{
+    const uint32_t n_tiles = (uint32_t)((h.n_tokens + kTile - 1) / kTile);
+    if (h.nq == 8 && h.nk == 2)
+        apply_ids_kernel<BF16, 8, 2><<<n_tiles, kBlock, 0, st>>>(h, r, s, n_tiles);
+    else
+        apply_ids_kernel<BF16, 0, 0><<<n_tiles, kBlock, 0, st>>>(h, r, s, n_tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, bool bf16, hipStream_t stream)
+{
+    return bf16 ? apply_ids_dispatch<true>(h, r, s, stream) : apply_ids_dispatch<false>(h, r, s, stream);
+}
+
+hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, bool bf16, hipStream_t stream)
+{
+    const unsigned blocks = (unsigned)((d.n_seqs + 3) / 4);
+    if (bf16)
+        decode_kernel<true><<<blocks, kBlock, 0, stream>>>(d, r);
+    else
+        decode_kernel<false><<<blocks, kBlock, 0, stream>>>(d, r);
+    return hipGetLastError();
+}
+
+}  // namespace mrope

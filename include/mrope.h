@@ -1,0 +1,182 @@
+/*
+ * libmrope -- canvas M-RoPE for MI355X (gfx950): position planes from token ids, and the
+ * interleaved multi-section rotary embedding of Q and K, for prefill and decode.
+ *
+ * What is computed is defined on two pages:
+ *   [card]  Hugging Face card "MiniCPM-V-4.7-1B -- Core AI" (mlboydaisuke/MiniCPM-V-4.7-1B-CoreAI):
+ *           section "What it is" (three planes T, H, W in interleaved sections [11, 11, 10]) and
+ *           section "How the VLM rides the text-only engine" (the canvas table; start and amount;
+ *           the keyCache shape [6, 1, 2, -1, 256]: 2 KV heads of 256 dims; id layout).
+ *   [zoo]   Core AI model-zoo page "MiniCPM-V-4.7-1B: canvas M-RoPE on the Qwen3.5 hybrid, on Core
+ *           AI", section "The canvas rule and why the gate is on the planes".
+ * Not on the pages, taken from the model configuration: rotate-half over the first 64 dims of each
+ * head (32 frequencies), theta = 1e7, and frequency j reading plane H if j%3==1 && j<33, W if
+ * j%3==2 && j<30, else T.
+ *
+ * Conventions for every entry point
+ *   - Pointers to tensors are DEVICE pointers owned by the caller.  The library allocates no
+ *     device memory and keeps no mutable global state; the only state that crosses calls lives in
+ *     the caller's workspace (see mrope_workspace_bytes).
+ *   - Every call enqueues its work on `stream` (a hipStream_t; NULL = the null stream) and returns
+ *     without synchronising.  Calls issue no memset and no allocation, so they can be captured in a
+ *     HIP graph.
+ *   - Arguments are checked on the host before anything is enqueued; a bad argument returns a
+ *     status != MROPE_OK and enqueues nothing.  A failed launch returns MROPE_ERR_HIP.
+ *     mrope_last_error() gives a one-line description of the last failure on the calling thread.
+ *   - Strides are in ELEMENTS of the tensor's dtype.  Q and K element (t, h, d) is at
+ *     t*tok_stride + h*head_stride + d; d is contiguous.
+ *   - Data-dependent conditions (two image markers in a sequence, a frame running past the end of
+ *     its sequence) are reported per sequence in the optional seq_flags array, never by a status.
+ *   - Calls that share a workspace must be ordered (same stream, or synchronised); concurrent calls
+ *     on one workspace race.
+ */
+#ifndef MROPE_H
+#define MROPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MROPE_ABI_VERSION 1
+
+typedef enum {
+    MROPE_OK = 0,
+    MROPE_ERR_ARG = 1,         /* NULL pointer, negative size, bad stride, bad theta, ...         */
+    MROPE_ERR_ALIGN = 2,       /* Q/K/cache pointer or stride breaks 16-byte vector alignment     */
+    MROPE_ERR_UNSUPPORTED = 3, /* rot_dim != 64, head_dim not in [64, 1024], head count > 64, dtype */
+    MROPE_ERR_WORKSPACE = 4,   /* workspace NULL, too small or misaligned                          */
+    MROPE_ERR_HIP = 5          /* the HIP runtime reported an error for a launch                   */
+} mrope_status;
+
+typedef enum {
+    MROPE_F32 = 0,   /* float32 Q/K/cache */
+    MROPE_BF16 = 1   /* bfloat16 Q/K/cache; math in fp32, one round-to-nearest-even per output */
+} mrope_dtype;
+
+/* seq_flags bits (optional per-sequence output of the plane-deriving calls). */
+#define MROPE_SEQ_MULTI_MARKER 1u /* more than one <image> marker; planes follow the first frame */
+#define MROPE_SEQ_FRAME_OVERRUN 2u /* the frame (67 tokens from the marker) runs past the end     */
+#define MROPE_SEQ_LOOKBACK_TIMEOUT 4u /* a scan tile gave up waiting for its predecessor (workspace
+                                         not initialised or shared by concurrent calls)            */
+
+/* Text-only sequences get start = 2^30 and amount = 0 (card, start/amount paragraph). */
+#define MROPE_TEXT_ONLY_START (1 << 30)
+
+int mrope_abi_version(void);
+
+/* Static string for a status code; never NULL. */
+const char *mrope_status_string(int status);
+
+/* Description of the last non-OK status returned on the calling thread ("" if none). */
+const char *mrope_last_error(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Workspace for the calls that derive planes from ids (mrope_planes, mrope_apply_ids).
+ *
+ * Returns the bytes needed for n_tokens packed tokens.  The workspace must be 256-byte aligned
+ * device memory, and must be zero-filled (or passed once through mrope_workspace_init) before its
+ * first use.  Each call leaves it ready for the next one; do not clear it between calls.  It holds
+ * a tile ticket counter, a finish counter, an epoch and one 64-bit status word per 64-token tile.
+ * ------------------------------------------------------------------------------------------- */
+size_t mrope_workspace_bytes(int64_t n_tokens);
+
+/* Zero-fill `bytes` of workspace with a kernel (no memset node) on `stream`. */
+mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mrope_planes -- canvas position planes from token ids ([card] canvas table; [zoo] canvas rule).
+ *
+ * ids        [n_tokens] int32, packed sequences (token t of sequence s is ids[cu_seqlens[s] + t]).
+ * cu_seqlens [n_seqs + 1] int32, cu_seqlens[0] = 0, non-decreasing, cu_seqlens[n_seqs] == n_tokens
+ *            (n_tokens is passed explicitly so the host never reads device memory).  Empty
+ *            sequences are allowed.
+ * marker_id  the <image> token id (248078 for the model's tokenizer).
+ * planes     [3][plane_stride] int32 out: row 0 = T, row 1 = H, row 2 = W; plane_stride >= n_tokens.
+ *            For position p of a sequence whose first marker is at O:
+ *              p < O or no marker     -> (p, p, p)
+ *              p == O                 -> (O, O-1, O-1)
+ *              p == O+1+k, k < 64     -> (O, O + k/8, O + k%8)
+ *              p == O+65              -> (O, O+8, O+8)
+ *              p == O+66              -> (O, O, O)
+ *              p >= start == O+67     -> (p-58, p-58, p-58)
+ * start, amount  [n_seqs] int32 out (nullable): start = O+67, amount = 58 for an image sequence;
+ *            2^30 and 0 for a text-only one.
+ * origin     [n_seqs] int32 out (nullable): O, or -1 when the sequence has no marker.
+ * seq_flags  [n_seqs] int32 out (nullable): MROPE_SEQ_* bits.
+ * workspace  see mrope_workspace_bytes(n_tokens).
+ *
+ * One launch: each 64-token tile finds its markers with a wavefront ballot and takes the first
+ * marker of a sequence that began in an earlier tile from its predecessors by decoupled look-back.
+ * ------------------------------------------------------------------------------------------- */
+mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                          int32_t marker_id, int32_t *planes, int64_t plane_stride, int32_t *start,
+                          int32_t *amount, int32_t *origin, int32_t *seq_flags, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mrope_apply -- rotate Q and K heads with given planes ([card] "What it is": interleaved sections).
+ *
+ * q          Q heads, dtype `dtype`, element (t, h, d) at t*q_tok_stride + h*q_head_stride + d.
+ * k          K heads likewise (may be NULL when n_k_heads == 0).
+ * n_tokens   tokens to rotate (0 = nothing to do).
+ * head_dim   dims per head, multiple of 8, 64..1024 (256 for the model).
+ * rot_dim    rotated dims per head; must be 64.  For j < 32, with a_j = fl32(fl32(pos_j) *
+ *            inv_freq[j]), inv_freq[j] = fl32(1 / fl32(theta^(2j/64))):
+ *              y[j]    = x[j]    * cos(a_j) - x[j+32] * sin(a_j)
+ *              y[j+32] = x[j+32] * cos(a_j) + x[j]    * sin(a_j)
+ *            pos_j is the T, H or W plane of the token by the rule in the file header.
+ * planes     [3][plane_stride] int32 (as written by mrope_planes); |plane| < 2^24.
+ * theta      rotary base (1e7 for the model), > 0 and finite.
+ * q_out, k_out  NULL: rotate in place (dims >= rot_dim are never read or written).  Otherwise the
+ *            full heads are written there, with the same strides as q / k (no aliasing with the
+ *            inputs).  Both NULL or both non-NULL (k_out may be NULL when n_k_heads == 0).
+ * Alignment: q, k, q_out, k_out 16-byte aligned; strides multiples of 8 (bf16) or 4 (fp32).
+ * ------------------------------------------------------------------------------------------- */
+mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,
+                         int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
+                         int32_t head_dim, int32_t rot_dim, int32_t dtype, const int32_t *planes,
+                         int64_t plane_stride, double theta, void *q_out, void *k_out, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mrope_apply_ids -- planes derivation and rotation fused in ONE launch: ids -> first marker per
+ * sequence -> planes (in registers) -> rotate Q and K.  Arguments as in mrope_planes and
+ * mrope_apply; planes_out (nullable) additionally receives the planes ([3][plane_stride]).
+ * n_tokens must equal cu_seqlens[n_seqs].
+ * ------------------------------------------------------------------------------------------- */
+mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,
+                             int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
+                             int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *q_out,
+                             void *k_out, const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs,
+                             int32_t marker_id, int32_t *planes_out, int64_t plane_stride, int32_t *start,
+                             int32_t *amount, int32_t *origin, int32_t *seq_flags, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mrope_decode -- one generated token per sequence ([card] canvas table, last row: every position
+ * from start on, generated tokens included, takes p - amount on all three planes).
+ *
+ * q          [n_seqs] tokens of Q heads (strides as in mrope_apply), rotated in place.
+ * k          [n_seqs] tokens of new K heads (read only).
+ * pos, amount  [n_seqs] int32: the token's position p and its sequence's amount; plane = p - amount.
+ * k_cache    paged cache: element (block, row, head, d) at block*cache_block_stride +
+ *            row*cache_tok_stride + head*cache_head_stride + d.  The full head_dim dims of every K
+ *            head, first rot_dim rotated, are written at slot_mapping[s] (block = slot / block_size,
+ *            row = slot % block_size).  slot < 0 or slot >= num_blocks*block_size: nothing written.
+ *            Two sequences with the same slot: undefined which one lands.
+ * slot_mapping [n_seqs] int64.
+ * ------------------------------------------------------------------------------------------- */
+mrope_status mrope_decode(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads,
+                          const void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads,
+                          int32_t n_seqs, const int32_t *pos, const int32_t *amount, void *k_cache,
+                          const int64_t *slot_mapping, int32_t block_size, int64_t num_blocks,
+                          int64_t cache_block_stride, int64_t cache_tok_stride, int64_t cache_head_stride,
+                          int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MROPE_H */

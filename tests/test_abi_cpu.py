@@ -1,0 +1,126 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol include/mrope.h declares, and
+rejects bad arguments on the host with the documented status, before anything reaches the GPU.
+No call here passes validation, so nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from canvas_rope_rotary_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mrope.h")
+OK, ARG, ALIGN, UNSUP, WS, HIP = range(6)
+BF16, F32 = _lib.MROPE_BF16, _lib.MROPE_F32
+A = 1 << 20            # a 16-byte (and 256-byte) aligned fake device address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = set(re.findall(r"^\w[\w \*]*?\b(mrope_\w+)\s*\(", open(HEADER).read(), re.M))
+    assert decl == set(_lib.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.mrope_abi_version() == 1
+    for code, text in ((OK, "ok"), (ARG, "invalid argument"), (HIP, "HIP runtime error")):
+        assert lib.mrope_status_string(code).decode() == text
+    assert lib.mrope_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    for n, tiles in ((0, 0), (1, 1), (64, 1), (65, 2), (1 << 20, 1 << 14)):
+        assert lib.mrope_workspace_bytes(n) == 256 + 8 * tiles
+
+
+def _apply(lib, **kw):
+    a = dict(q=A, qt=2048, qh=256, nq=8, k=A, kt=512, kh=256, nk=2, n=100, hd=256, rot=64, dt=BF16, planes=A,
+             ps=100, theta=1e7, qo=None, ko=None)
+    a.update(kw)
+    return lib.mrope_apply(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["n"], a["hd"],
+                           a["rot"], a["dt"], a["planes"], a["ps"], a["theta"], a["qo"], a["ko"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rot=32), UNSUP), (dict(hd=60), UNSUP), (dict(hd=260), UNSUP), (dict(hd=2048), UNSUP),
+    (dict(dt=7), UNSUP), (dict(nq=65), UNSUP), (dict(nk=-1), UNSUP),
+    (dict(n=-1), ARG), (dict(q=None), ARG), (dict(k=None), ARG), (dict(planes=None), ARG), (dict(ps=99), ARG),
+    (dict(theta=0.0), ARG), (dict(theta=float("nan")), ARG), (dict(theta=float("inf")), ARG),
+    (dict(qo=A), ARG), (dict(qt=-8), ARG),
+    (dict(q=A + 8), ALIGN), (dict(k=A + 4), ALIGN), (dict(qt=2044), ALIGN), (dict(kh=252), ALIGN),
+    (dict(dt=F32, qt=2050), ALIGN),
+])
+def test_apply_validation(lib, kw, code):
+    assert _apply(lib, **kw) == code
+    assert lib.mrope_last_error().decode() != ""
+
+
+def test_apply_nothing_to_do(lib):
+    assert _apply(lib, n=0) == OK
+    assert _apply(lib, nq=0, nk=0) == OK
+
+
+def _planes(lib, **kw):
+    a = dict(ids=A, cu=A, ns=4, n=1000, marker=248078, planes=A, ps=1000, ws=A, wsb=10 ** 6)
+    a.update(kw)
+    return lib.mrope_planes(a["ids"], a["cu"], a["ns"], a["n"], a["marker"], a["planes"], a["ps"], None, None, None,
+                            None, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ns=-1), ARG), (dict(n=-1), ARG), (dict(ns=0), ARG), (dict(cu=None), ARG), (dict(ids=None), ARG),
+    (dict(planes=None), ARG), (dict(ps=999), ARG), (dict(n=1 << 31), ARG),
+    (dict(ws=None), WS), (dict(ws=A + 64), WS), (dict(wsb=256 + 8 * 15), WS),
+])
+def test_planes_validation(lib, kw, code):
+    assert _planes(lib, **kw) == code
+
+
+def test_planes_empty_is_ok(lib):
+    assert _planes(lib, ns=0, n=0, ws=None) == OK
+
+
+def test_workspace_init_validation(lib):
+    assert lib.mrope_workspace_init(None, 1024, None) == WS
+    assert lib.mrope_workspace_init(A + 128, 1024, None) == WS
+    assert lib.mrope_workspace_init(A, 100, None) == WS
+
+
+def _decode(lib, **kw):
+    a = dict(q=A, qt=2048, qh=256, nq=8, k=A, kt=512, kh=256, nk=2, ns=16, pos=A, am=A, cache=A, slots=A, bs=16,
+             nb=64, cb=8192, ct=512, ch=256, hd=256, rot=64, dt=BF16, theta=1e7)
+    a.update(kw)
+    return lib.mrope_decode(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["ns"], a["pos"],
+                            a["am"], a["cache"], a["slots"], a["bs"], a["nb"], a["cb"], a["ct"], a["ch"], a["hd"],
+                            a["rot"], a["dt"], a["theta"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pos=None), ARG), (dict(am=None), ARG), (dict(cache=None), ARG), (dict(slots=None), ARG),
+    (dict(bs=0), ARG), (dict(nb=-1), ARG), (dict(ct=-512), ARG), (dict(cache=A + 2), ALIGN), (dict(ch=250), ALIGN),
+    (dict(rot=128), UNSUP), (dict(theta=-1.0), ARG),
+])
+def test_decode_validation(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_nothing_to_do(lib):
+    assert _decode(lib, ns=0) == OK
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package (binding, kernels, build) neither imports nor calls the oracle, nor links it."""
+    pkg = os.path.join(ROOT, "canvas_rope_rotary_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b|\boracle\.\w+\(|liboracle|mrope_oracle",
+                                     src, re.M), f

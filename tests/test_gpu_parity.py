@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Planes, start, amount, origin and flags: bit-exact.  Rotated Q/K: fp32 within 2e-6 of the oracle
+(pair-norm relative), bf16 within 1 ulp of the fp32 oracle rounded to bf16; the dims past the
+rotary part bit-identical.  Small inputs are compared element by element; the full-size workloads
+in full for planes and on sampled tokens for the rotation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import canvas_rope_rotary_amd as mr
+import oracle
+from canvas_rope_rotary_amd import synth
+from gpu_util import MARKER, as_f32, compare_heads, dev_heads, expected_flags, host_heads, i32, say
+from parity import check_bf16, check_fp32
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_planes(b):
+    return oracle.planes(b.ids, b.cu_seqlens, MARKER)
+
+
+def _check_scan(b, pl, st, am, og, fl, what):
+    epl, est, eam, eog = _oracle_planes(b)
+    np.testing.assert_array_equal(pl.cpu().numpy()[:, :b.n_tokens], epl, err_msg=f"{what} planes")
+    np.testing.assert_array_equal(st.cpu().numpy(), est, err_msg=f"{what} start")
+    np.testing.assert_array_equal(am.cpu().numpy(), eam, err_msg=f"{what} amount")
+    np.testing.assert_array_equal(og.cpu().numpy(), eog, err_msg=f"{what} origin")
+    if fl is not None:
+        np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg=f"{what} flags")
+    return epl, est, eam, eog
+
+
+def _sample_tokens(b, og, n_random=4096, seed=0):
+    idx = set()
+    g = np.random.default_rng(seed)
+    for s in range(b.n_seqs):
+        lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
+        if hi == lo:
+            continue
+        idx.update((lo, hi - 1))
+        if og[s] >= 0:
+            o = lo + int(og[s])
+            idx.update(range(o, min(o + 70, hi)))
+    idx.update(g.integers(0, b.n_tokens, size=min(n_random, b.n_tokens)).tolist())
+    return np.array(sorted(idx), np.int64)
+
+
+# ------------------------------------------------------------------ small, element by element ---
+
+def test_config1_fp32_single_image():
+    b = synth.config1()
+    say("case: single image prompt, fp32, L=110")
+    qn, kn = b.qk()
+    ids, cu = i32(b.ids), i32(b.cu_seqlens)
+    pl, st, am, og, fl = mr.planes(ids, cu, MARKER)
+    epl, est, eam, eog = _check_scan(b, pl, st, am, og, fl, "config1")
+    assert (int(st[0]), int(am[0]), int(og[0])) == (73, 58, 6)
+    # in place
+    q, k = dev_heads(qn, "f32"), dev_heads(kn, "f32")
+    mr.apply(q, k, pl)
+    compare_heads(host_heads(q), qn, epl, "f32", what="q in place")
+    compare_heads(host_heads(k), kn, epl, "f32", what="k in place")
+    # out of place == in place, inputs untouched
+    q2, k2 = dev_heads(qn, "f32"), dev_heads(kn, "f32")
+    qo, ko = torch.empty_like(q2), torch.empty_like(k2)
+    mr.apply(q2, k2, pl, q_out=qo, k_out=ko)
+    assert torch.equal(qo, q) and torch.equal(ko, k)
+    np.testing.assert_array_equal(host_heads(q2), qn)
+    # fused
+    q3, k3 = dev_heads(qn, "f32"), dev_heads(kn, "f32")
+    pl3 = torch.full((3, b.n_tokens), -7, dtype=torch.int32, device="cuda")
+    st3, am3, og3, fl3, _ = mr.apply_ids(q3, k3, ids, cu, MARKER, planes_out=pl3)
+    _check_scan(b, pl3, st3, am3, og3, fl3, "config1 fused")
+    assert torch.equal(q3, q) and torch.equal(k3, k)
+
+
+def test_config1_prefix_103():
+    """Reading of the workload text: 6 + 67 + 30 = 103 tokens; L = 110 is kept, and the 103-token
+    prefix must give the same planes."""
+    b = synth.config1()
+    ids = i32(b.ids[:103])
+    pl, st, am, og, fl = mr.planes(ids, i32([0, 103]), MARKER)
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    np.testing.assert_array_equal(pl.cpu().numpy(), epl[:, :103])
+    assert (int(st[0]), int(am[0])) == (73, 58)
+
+
+@pytest.mark.parametrize("seed,dtype,n_seqs,max_len,empty", [
+    (101, "bf16", 40, 300, 0.0), (102, "f32", 40, 300, 0.1), (103, "bf16", 300, 90, 0.2),
+    (104, "bf16", 12, 3000, 0.0), (105, "f32", 5, 700, 0.0), (106, "bf16", 1, 1, 0.0),
+])
+def test_fuzz_small_batches(seed, dtype, n_seqs, max_len, empty):
+    b = synth.random_batch(seed, n_seqs, max_len=max_len, dtype=dtype, empty_frac=empty)
+    say(f"case: fuzz seed={seed} dtype={dtype} seqs={n_seqs} tokens={b.n_tokens}")
+    qn, kn = b.qk()
+    ids, cu = i32(b.ids), i32(b.cu_seqlens)
+    pl, st, am, og, fl = mr.planes(ids, cu, MARKER)
+    epl, *_ = _check_scan(b, pl, st, am, og, fl, f"fuzz {seed}")
+    q, k = dev_heads(qn, dtype), dev_heads(kn, dtype)
+    mr.apply(q, k, pl)
+    compare_heads(host_heads(q), qn, epl, dtype, what="q")
+    compare_heads(host_heads(k), kn, epl, dtype, what="k")
+    # fused kernel: same bits as planes + apply
+    q2, k2 = dev_heads(qn, dtype), dev_heads(kn, dtype)
+    pl2 = torch.full_like(pl, -7)
+    st2, am2, og2, fl2, _ = mr.apply_ids(q2, k2, ids, cu, MARKER, planes_out=pl2)
+    _check_scan(b, pl2, st2, am2, og2, fl2, f"fuzz {seed} fused")
+    assert torch.equal(q2, q) and torch.equal(k2, k)
+
+
+def test_many_tiny_sequences_and_empties():
+    """5000 sequences of 0..3 tokens: many sequences per 64-token tile, empty ones in runs."""
+    g = np.random.default_rng(7)
+    lens = g.integers(0, 4, size=5000)
+    lens[:3] = 0
+    lens[-4:] = 0
+    ids = synth.text_ids(synth.rng(7, 4), int(lens.sum()))
+    ids[g.integers(0, ids.size, size=200)] = MARKER
+    cu = np.zeros(lens.size + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    b = synth.Prefill("tiny", ids, cu, [None] * lens.size, "bf16", seed=7)
+    pl, st, am, og, fl = mr.planes(i32(ids), i32(cu), MARKER)
+    _check_scan(b, pl, st, am, og, fl, "tiny")
+
+
+def test_zero_tokens_text_scalars():
+    cu = i32([0, 0, 0])
+    ids = torch.zeros(0, dtype=torch.int32, device="cuda")
+    pl, st, am, og, fl = mr.planes(ids, cu, MARKER)
+    assert st.tolist() == [1 << 30] * 2 and am.tolist() == [0, 0] and og.tolist() == [-1, -1]
+
+
+def test_origin_zero_negative_planes():
+    ids = synth.prompt_ids(synth.rng(3, 9), 200, 0)
+    b = synth.Prefill("o0", ids, np.array([0, 200], np.int32), [0], "bf16", seed=3)
+    pl, st, am, og, fl = mr.planes(i32(ids), i32(b.cu_seqlens), MARKER)
+    epl, *_ = _check_scan(b, pl, st, am, og, fl, "O=0")
+    assert pl[1, 0].item() == -1 and pl[2, 0].item() == -1
+    qn, kn = b.qk()
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    mr.apply(q, k, pl)
+    compare_heads(host_heads(q), qn, epl, "bf16", what="q O=0")
+
+
+def test_long_sequence_lookback_chain():
+    """One 200,000-token sequence with its marker near the end and one with none: look-back over
+    thousands of tiles."""
+    lens = [200000, 150000, 70]
+    placed = [199000, None, 0]
+    g = synth.rng(9, 4)
+    ids = np.concatenate([synth.prompt_ids(g, n, o) for n, o in zip(lens, placed)])
+    cu = np.zeros(4, np.int32)
+    cu[1:] = np.cumsum(lens)
+    b = synth.Prefill("long", ids, cu, placed, "bf16", seed=9)
+    for rep in range(3):
+        pl, st, am, og, fl = mr.planes(i32(ids), i32(cu), MARKER)
+        _check_scan(b, pl, st, am, og, fl, f"long rep {rep}")
+
+
+def test_strided_views_equal_contiguous():
+    """Q and K as views of one fused QKV projection buffer give the same bits as contiguous copies."""
+    b = synth.random_batch(21, 30, max_len=200)
+    qn, kn = b.qk()
+    T = b.n_tokens
+    pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    qkv = torch.zeros((T, 8 + 2 + 2, 256), dtype=torch.bfloat16, device="cuda")
+    qkv[:, :8] = dev_heads(qn, "bf16")
+    qkv[:, 8:10] = dev_heads(kn, "bf16")
+    qv, kv = qkv[:, :8], qkv[:, 8:10]
+    assert not qv.is_contiguous() and qv.stride(0) == 12 * 256
+    qc, kc = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    mr.apply(qv, kv, pl)
+    mr.apply(qc, kc, pl)
+    assert torch.equal(qv, qc) and torch.equal(kv, kc)
+    assert torch.equal(qkv[:, 10:], torch.zeros_like(qkv[:, 10:]))
+
+
+def test_generic_head_counts():
+    """Head counts other than 8 + 2 take the generic kernel; same results as the oracle."""
+    b = synth.random_batch(31, 10, max_len=300)
+    T = b.n_tokens
+    xq = synth.to_bf16_bits(synth.normal(31, 60, T * 4 * 128)).reshape(T, 4, 128)
+    xk = synth.to_bf16_bits(synth.normal(31, 61, T * 1 * 128)).reshape(T, 1, 128)
+    pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    q, k = dev_heads(xq, "bf16"), dev_heads(xk, "bf16")
+    mr.apply(q, k, pl)
+    compare_heads(host_heads(q), xq, epl, "bf16", what="q 4x128")
+    compare_heads(host_heads(k), xk, epl, "bf16", what="k 1x128")
+    q2 = dev_heads(xq, "bf16")
+    mr.apply(q2, None, pl)
+    assert torch.equal(q2, q)
+
+
+def test_red_arms_fail_on_gpu_output():
+    """amount + 1 and 1-D planes must fail the rotation gate against the GPU output on every image
+    prompt with text after the frame (zoo page: gate the planes themselves)."""
+    b = synth.random_batch(41, 20, max_len=500, min_len=150, text_frac=0.0, dtype="f32")
+    qn, _ = b.qk()
+    pl, st, am, og, fl = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    q = dev_heads(qn, "f32")
+    mr.apply(q, None, pl)
+    got = host_heads(q)
+    epl, est, eam, eog = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    n_red = 0
+    for s in range(b.n_seqs):
+        lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
+        if eog[s] < 0 or est[s] >= hi - lo:
+            continue
+        p = np.arange(hi - lo, dtype=np.int32)
+        arm = epl[:, lo:hi].copy()
+        arm[:, p >= est[s]] -= 1
+        for planes_arm in (arm, np.stack([p, p, p])):
+            ok, _ = check_fp32(got[lo:hi], oracle.rotate(qn[lo:hi], planes_arm))
+            assert not ok
+            n_red += 1
+        ok, _ = check_fp32(got[lo:hi], oracle.rotate(qn[lo:hi], epl[:, lo:hi]))
+        assert ok
+    assert n_red >= 10
+
+
+# ------------------------------------------------------------------ full-size workloads --------
+
+def _full_prefill(b, fused: bool):
+    say(f"case: {b.name} tokens={b.n_tokens} seqs={b.n_seqs} fused={fused}")
+    qn, kn = b.qk()
+    ids, cu = i32(b.ids), i32(b.cu_seqlens)
+    q, k = dev_heads(qn, b.dtype), dev_heads(kn, b.dtype)
+    q_tail, k_tail = q[..., 64:].clone(), k[..., 64:].clone()
+    if fused:
+        pl = torch.empty((3, b.n_tokens), dtype=torch.int32, device="cuda")
+        st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER, planes_out=pl)
+    else:
+        pl, st, am, og, fl = mr.planes(ids, cu, MARKER)
+        mr.apply(q, k, pl)
+    torch.cuda.synchronize()
+    epl, est, eam, eog = _check_scan(b, pl, st, am, og, fl, b.name)
+    assert torch.equal(q[..., 64:], q_tail) and torch.equal(k[..., 64:], k_tail)
+    idx = _sample_tokens(b, eog)
+    ti = torch.from_numpy(idx).cuda()
+    say(f"  sampled {idx.size} tokens")
+    compare_heads(host_heads(q[ti]), qn[idx], epl[:, idx], b.dtype, what=f"{b.name} q")
+    compare_heads(host_heads(k[ti]), kn[idx], epl[:, idx], b.dtype, what=f"{b.name} k")
+    del q, k, q_tail, k_tail
+    torch.cuda.empty_cache()
+    return eog
+
+
+def test_config2_full_64x4096():
+    _full_prefill(synth.config2(), fused=False)
+
+
+def test_config2_full_fused():
+    _full_prefill(synth.config2(), fused=True)
+
+
+def test_config3_full_fused_8x32768():
+    _full_prefill(synth.config3(), fused=True)
+
+
+def test_config5_full_ragged():
+    b = synth.config5()
+    eog = _full_prefill(b, fused=False)
+    assert (eog[1::2] == -1).all() and (eog[0::2] >= 0).all()
+
+
+def test_config5_full_ragged_fused():
+    _full_prefill(synth.config5(), fused=True)
+
+
+def test_config4_decode_paged():
+    d = synth.config4()
+    say(f"case: {d.name}")
+    qn, kn = d.qk()
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    cache = torch.full((d.num_blocks, d.block_size, d.n_k_heads, d.head_dim), 0, dtype=torch.int16,
+                       device="cuda").fill_(d.sentinel_bits - (1 << 16)).view(torch.bfloat16)
+    pos, amount, slots = i32(d.pos), i32(d.amount), torch.from_numpy(d.slot_mapping).cuda()
+    mr.decode(q, k, pos, amount, cache, slots)
+    torch.cuda.synchronize()
+    # Q: every element against the oracle at plane pos - amount
+    ref_q = oracle.rotate(as_f32(qn, "bf16"), np.stack([d.pos - d.amount] * 3))
+    ok, info = check_bf16(host_heads(q), oracle.round_bf16(ref_q))
+    assert ok, info
+    # K: the rotated heads at their slots ...
+    ref_k = oracle.rotate(as_f32(kn, "bf16"), np.stack([d.pos - d.amount] * 3))
+    blk = torch.from_numpy(d.slot_mapping // d.block_size).cuda()
+    row = torch.from_numpy(d.slot_mapping % d.block_size).cuda()
+    got_k = host_heads(cache[blk, row])
+    ok, info = check_bf16(got_k, oracle.round_bf16(ref_k))
+    assert ok, info
+    # ... and every other slot still holds the sentinel
+    untouched = (cache.view(torch.int16) != (d.sentinel_bits - (1 << 16))).sum().item()
+    assert untouched == d.n_seqs * d.n_k_heads * d.head_dim
+    # decode == prefill rotation of the same token at plane p - amount (oracle cross-check)
+    qo = oracle.decode(as_f32(qn[:64], "bf16"), as_f32(kn[:64], "bf16"), d.pos[:64], d.amount[:64],
+                       np.zeros((64, d.block_size, 2, 256), np.float32), np.arange(64) * d.block_size, d.block_size)
+    np.testing.assert_array_equal(qo, ref_q[:64])
+
+
+def test_decode_skips_negative_and_out_of_range_slots():
+    d = synth.config4(n_seqs=64, num_blocks=64)
+    qn, kn = d.qk()
+    slots = np.arange(64, dtype=np.int64)
+    slots[::3] = -1
+    slots[1::7] = 8 * 16 + 5      # past the cache
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    cache = torch.zeros((8, 16, 2, 256), dtype=torch.bfloat16, device="cuda")
+    mr.decode(q, k, i32(d.pos), i32(d.amount), cache, torch.from_numpy(slots).cuda())
+    ref_k = oracle.round_bf16(oracle.rotate(as_f32(kn, "bf16"), np.stack([d.pos - d.amount] * 3)))
+    c = host_heads(cache)
+    for s in range(64):
+        sl = slots[s]
+        if 0 <= sl < 128:
+            ok, info = check_bf16(c[sl // 16, sl % 16], ref_k[s])
+            assert ok, info
+    written = {int(s) for s in slots if 0 <= s < 128}
+    for sl in range(128):
+        if sl not in written:
+            assert (c[sl // 16, sl % 16] == 0).all()
+
+
+def test_workspace_reuse_across_sizes():
+    """Back-to-back calls of different sizes on one workspace: the epoch and counters carry over."""
+    ws = mr.Workspace(1 << 16)
+    for i, seed in enumerate((51, 52, 53, 54, 55, 56)):
+        b = synth.random_batch(seed, 20 + 30 * i, max_len=400 + 200 * i, empty_frac=0.05)
+        pl, st, am, og, fl = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER, workspace=ws)
+        _check_scan(b, pl, st, am, og, fl, f"reuse {i}")
