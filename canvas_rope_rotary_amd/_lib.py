@@ -24,7 +24,6 @@ EXPORTS = ("mrope_abi_version", "mrope_status_string", "mrope_last_error", "mrop
 class MarkerFlags(enum.IntFlag):
     MULTI_MARKER = 1
     FRAME_OVERRUN = 2
-    LOOKBACK_TIMEOUT = 4
 
 
 class MropeError(RuntimeError):
@@ -57,12 +56,13 @@ def load():
     lib.mrope_workspace_bytes.restype = U64
     lib.mrope_workspace_init.argtypes = [P, U64, P]
     lib.mrope_workspace_init.restype = ctypes.c_int
-    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, P, I64, P, P, P, P, P, U64, P]
+    U32 = ctypes.c_uint32
+    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_planes.restype = ctypes.c_int
     lib.mrope_apply.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, P, I64, F64, P, P, P]
     lib.mrope_apply.restype = ctypes.c_int
     lib.mrope_apply_ids.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
-                                    P, P, I32, I32, P, I64, P, P, P, P, P, U64, P]
+                                    P, P, I32, I32, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_apply_ids.restype = ctypes.c_int
     lib.mrope_decode.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I32, P, P, P, P, I32, I64, I64, I64, I64,
                                  I32, I32, I32, F64, P]
@@ -132,13 +132,21 @@ def cu_seqlens_from_lens(lens: torch.Tensor) -> torch.Tensor:
 
 class Workspace:
     """Device workspace of the plane-deriving calls, zero-filled once, reusable across calls on one
-    stream (the library keeps it consistent between calls)."""
+    stream.  It also keeps the call counter that tags each call's status words (the epoch); under
+    HIP-graph capture the library's device-side counter is used instead (epoch 0)."""
 
     def __init__(self, n_tokens: int, device=None):
         self.device = torch.device(device if device is not None else "cuda")
         self.capacity = 0
         self.buf = None
+        self.calls = 0
         self.ensure(n_tokens)
+
+    def next_epoch(self) -> int:
+        if torch.cuda.is_current_stream_capturing():
+            return 0
+        self.calls = self.calls % ((1 << 29) - 1) + 1
+        return self.calls
 
     def ensure(self, n_tokens: int):
         need = int(load().mrope_workspace_bytes(int(n_tokens)))
@@ -187,7 +195,7 @@ def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078,
     with torch.cuda.device(dev):
         _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), _ptr(out), out.stride(0),
                                    _ptr(start), _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr,
-                                   ws.capacity, _stream(dev)))
+                                   ws.capacity, ws.next_epoch(), _stream(dev)))
     return out, start, amount, origin, seq_flags
 
 
@@ -251,7 +259,7 @@ def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seq
         _check(load().mrope_apply_ids(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, float(theta),
                                       _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
                                       _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
-                                      _ptr(seq_flags), ws.ptr, ws.capacity, _stream(dev)))
+                                      _ptr(seq_flags), ws.ptr, ws.capacity, ws.next_epoch(), _stream(dev)))
     return start, amount, origin, seq_flags, planes_out
 
 

@@ -121,7 +121,8 @@ mrope_status check_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, i
 }
 
 Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_tokens, int32_t marker, int32_t *planes,
-               int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin, int32_t *flags, void *ws)
+               int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin, int32_t *flags, void *ws,
+               uint32_t epoch)
 {
     Scan s;
     s.ids = ids;
@@ -136,6 +137,7 @@ Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_
     s.origin = origin;
     s.flags = flags;
     s.workspace = ws;
+    s.epoch = epoch;
     return s;
 }
 
@@ -179,12 +181,13 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream)
 
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
                           int32_t marker_id, int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount,
-                          int32_t *origin, int32_t *seq_flags, void *workspace, size_t workspace_bytes, void *stream)
+                          int32_t *origin, int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
+                          void *stream)
 {
     mrope_status st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes, plane_stride, workspace, workspace_bytes, true);
     if (st != MROPE_OK) return st;
     const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, planes, plane_stride, start, amount, origin,
-                              seq_flags, workspace);
+                              seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (n_tokens == 0) {
@@ -219,7 +222,8 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *q_out, void *k_out,
                              const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
                              int32_t *planes_out, int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
-                             int32_t *seq_flags, void *workspace, size_t workspace_bytes, void *stream)
+                             int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
+                             void *stream)
 {
     mrope_status st = check_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
                                   n_tokens, head_dim, rot_dim, dtype, q_out, k_out);
@@ -228,7 +232,7 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
     st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes_out, plane_stride, workspace, workspace_bytes, false);
     if (st != MROPE_OK) return st;
     const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, planes_out, plane_stride, start, amount,
-                              origin, seq_flags, workspace);
+                              origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (n_tokens == 0) {

@@ -8,7 +8,7 @@ namespace mrope {
 
 constexpr int kMaxHeads = 64;
 constexpr int kTile = 64;               // tokens per scan tile: one wavefront, one lane per token
-constexpr size_t kWsHeaderBytes = 256;  // ticket, finish counter, epoch (+ padding)
+constexpr size_t kWsHeaderBytes = 256;  // device epoch counter (+ padding)
 
 // Rotary constants: 32 fp32 inverse frequencies and the plane each frequency reads, 2 bits per
 // frequency (0 = T, 1 = H, 2 = W).
@@ -43,6 +43,7 @@ struct Scan {
     int32_t *origin;     // nullable
     int32_t *flags;      // nullable
     void *workspace;
+    uint32_t epoch;      // tags this launch's status words; 0 = use (and advance) the device counter
 };
 
 struct DecodeArgs {

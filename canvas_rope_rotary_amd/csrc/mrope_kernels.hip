@@ -8,7 +8,8 @@
 //   Core AI", section "The canvas rule and why the gate is on the planes".
 //
 // Kernels
-//   planes_kernel     ids -> first marker per sequence (ballot + decoupled look-back) -> planes, scalars
+//   planes_kernel     ids -> first marker per sequence (ballot + wait-free decoupled look-back) -> planes,
+//                     start, amount
 //   apply_kernel      planes -> cos/sin on the fly -> rotate-half of Q and K (the HBM stream)
 //   apply_ids_kernel  the two above in one launch; planes stay in LDS
 //   decode_kernel     one token per sequence: Q in place, K rotated and scattered to a paged cache
@@ -18,6 +19,10 @@
 // its 8 (cos, sin) pairs once and applies them to all heads of its token, so each sincos is done once
 // per token, with no LDS traffic and no cross-lane exchange.  Each head is one 128-byte line (bf16):
 // the four lanes of a token read it as two 64-byte runs.
+//
+// Precision: the angle is one fp32 multiply (as the model's rotary forms it); cos/sin and the two
+// products of each output are double (the same per-lane rate as fp32 on this chip with packed fp32
+// off); each output is rounded once to fp32 and, for bf16, once more to bf16 (nearest even).
 #include "mrope_internal.h"
 #include "mrope_math.h"
 
@@ -59,22 +64,21 @@ __device__ __forceinline__ void canvas_planes(int32_t p, int32_t o, int32_t &t, 
 }
 
 // ------------------------------------------------------------------ workspace ------------------
+// Header (256 bytes): the device epoch counter, used when the caller passes epoch 0; then one status
+// word per 64-token tile.
 struct WsHeader {
-    uint32_t ticket;  // next tile index to hand out
-    uint32_t done;    // participants finished in this launch
-    uint32_t epoch;   // launch counter; tags the status words of this launch
-    uint32_t error;   // sticky: bit 0 = a look-back gave up
+    uint32_t epoch;
 };
 
 // status word of a tile: [63:34] epoch | [33:32] flag | [31] multi | [30:0] first marker (global idx)
 constexpr uint64_t kAgg = 1;   // value covers only this tile's part of its last sequence
 constexpr uint64_t kIncl = 2;  // value covers the whole sequence up to the end of this tile
-constexpr uint32_t kEpochMask = 0x3fffffffu;
-constexpr uint32_t kSpinLimit = 1u << 21;
+constexpr uint32_t kEpochMask = 0x1fffffffu;  // caller epochs use 29 bits ...
+constexpr uint32_t kDeviceEpochBit = 0x20000000u;  // ... device-counter epochs carry bit 29 as well
 
 __device__ __forceinline__ uint64_t status_word(uint32_t epoch, uint64_t flag, bool multi, int32_t first)
 {
-    return ((uint64_t)(epoch & kEpochMask) << 34) | (flag << 32) | ((uint64_t)(multi ? 1u : 0u) << 31) |
+    return ((uint64_t)epoch << 34) | (flag << 32) | ((uint64_t)(multi ? 1u : 0u) << 31) |
            (uint64_t)((uint32_t)first & 0x7fffffffu);
 }
 
@@ -84,9 +88,9 @@ __device__ __forceinline__ uint64_t *status_array(void *ws)
 }
 
 template <typename T>
-__device__ __forceinline__ T aload(T *p)
+__device__ __forceinline__ T aload(const T *p)
 {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 template <typename T>
 __device__ __forceinline__ void astore(T *p, T v)
@@ -94,16 +98,12 @@ __device__ __forceinline__ void astore(T *p, T v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One participant (a wave or a workgroup) of a scan launch is done with the workspace.  The last
-// one resets the ticket and finish counters and advances the epoch for the next launch.
-__device__ __forceinline__ void finish_participant(WsHeader *hdr, uint32_t participants, uint32_t epoch)
+// The epoch that tags this launch's status words: the caller's (29 bits), or the device counter's
+// with bit 29 set (caller passed 0; a one-thread kernel advances the counter after the launch).
+__device__ __forceinline__ uint32_t launch_epoch(const Scan &sc)
 {
-    const uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == participants - 1) {
-        astore(&hdr->ticket, 0u);
-        astore(&hdr->done, 0u);
-        astore(&hdr->epoch, (epoch + 1u) & kEpochMask);
-    }
+    if (sc.epoch) return sc.epoch & kEpochMask;
+    return (aload(&static_cast<const WsHeader *>(sc.workspace)->epoch) & kEpochMask) | kDeviceEpochBit;
 }
 
 // ------------------------------------------------------------------ wave helpers ---------------
@@ -129,45 +129,62 @@ __device__ __forceinline__ int32_t seq_of(const int32_t *cu, int32_t n_seqs, int
 }
 
 // Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan with Decoupled
-// Look-back", 2016) with a (first marker, more-than-one) operator.  The whole wave reads the status
-// words of the 64 preceding tiles at once; it combines everything up to the nearest tile that holds
-// an inclusive value, or slides 64 tiles further back when none does.  The tile where the sequence
-// begins always publishes an inclusive value, so the walk ends there.  Every wait is bounded.
-__device__ void lookback(const uint64_t *status, int64_t tile, uint32_t epoch, int lane, int32_t &first,
-                         bool &multi, bool &timed_out)
+// Look-back", 2016) with a (first marker, more-than-one) operator, made wait-free: a tile never
+// waits for a predecessor.  The wave reads the status words of the 64 preceding tiles at once and
+// combines everything up to the nearest inclusive value -- a predecessor's published inclusive word,
+// or the tile where the sequence begins.  A predecessor that has not published yet (any status word
+// without this launch's epoch) is evaluated on the spot from its 64 ids (one coalesced load and a
+// ballot), so the result never depends on which workgroups the hardware has scheduled.
+// Returns the first marker (global index) of the sequence over [s0_begin, tile*64) and whether that
+// range holds more than one marker.
+__device__ void lookback(const Scan &sc, const uint64_t *status, int64_t tile, uint32_t ep, int lane,
+                         int64_t s0_begin, int32_t &first, bool &multi)
 {
     first = kNone;
     multi = false;
-    timed_out = false;
+    const int64_t stop = s0_begin / kTile;
     int64_t base = tile - 1;
-    uint32_t spins = 0;
-    const uint32_t ep = epoch & kEpochMask;
     while (true) {
         const int64_t idx = base - lane;
-        const uint64_t w = idx >= 0 ? aload(const_cast<uint64_t *>(status) + idx) : status_word(ep, kIncl, false, kNone);
+        const bool valid = idx >= stop;
+        const uint64_t w = valid ? aload(status + idx) : 0ull;
         const uint64_t flag = (w >> 32) & 3u;
-        const bool ready = (uint32_t)(w >> 34) == ep && flag != 0;
-        const uint64_t incl_mask = __ballot(ready && flag == kIncl);
-        const uint64_t ready_mask = __ballot(ready);
-        const int lim = incl_mask ? __builtin_ctzll(incl_mask) : 63;
-        const uint64_t need = lim >= 63 ? ~0ull : ((2ull << lim) - 1);
-        if ((ready_mask & need) == need) {
-            const bool use = lane <= lim;
-            const int32_t v = use ? (int32_t)(w & 0x7fffffffu) : kNone;
-            const uint64_t has = __ballot(use && v != kNone);
-            const bool mm = __ballot(use && ((w >> 31) & 1u)) != 0;
-            const int cnt = __builtin_popcountll(has) + (first != kNone ? 1 : 0);
-            multi = multi || mm || cnt >= 2;
-            first = min(first, wave_min(v));
-            if (incl_mask) return;
-            base -= 64;
-        } else {
-            if (++spins > kSpinLimit) {
-                timed_out = true;
-                return;
+        const bool ready = valid && (uint32_t)(w >> 34) == ep && flag != 0;
+        const uint64_t end_mask = __ballot(valid && ((ready && flag == kIncl) || idx == stop));
+        const int lim = end_mask ? __builtin_ctzll(end_mask) : 63;
+        const bool use = valid && lane <= lim;
+        int32_t v = (use && ready) ? (int32_t)(w & 0x7fffffffu) : kNone;
+        bool m = use && ready && ((w >> 31) & 1u);
+        uint64_t todo = __ballot(use && !ready);
+        while (todo) {  // up to four unpublished tiles per round trip
+            int bsel[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                bsel[k] = todo ? __builtin_ctzll(todo) : -1;
+                todo &= todo - 1;
             }
-            __builtin_amdgcn_s_sleep(1);
+            bool hit[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t gg = (base - bsel[k]) * kTile + lane;
+                hit[k] = bsel[k] >= 0 && gg >= s0_begin && gg < sc.n_tokens && sc.ids[gg] == sc.marker;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint64_t hm = __ballot(hit[k]);
+                if (bsel[k] >= 0 && lane == bsel[k]) {
+                    v = hm ? (int32_t)((base - bsel[k]) * kTile + __builtin_ctzll(hm)) : kNone;
+                    m = __builtin_popcountll(hm) >= 2;
+                }
+            }
         }
+        const uint64_t has = __ballot(use && v != kNone);
+        const bool mm = __ballot(use && m) != 0;
+        const int cnt = __builtin_popcountll(has) + (first != kNone ? 1 : 0);
+        multi = multi || mm || cnt >= 2;
+        first = min(first, wave_min(v));
+        if (end_mask) return;
+        base -= 64;
     }
 }
 
@@ -177,21 +194,19 @@ struct TokenPos {
     bool valid;     // the token belongs to a sequence
 };
 
-__device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t origin, bool multi, int64_t len,
-                                              bool timed_out)
+__device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t origin, bool multi, int64_t len)
 {
     const bool img = origin >= 0;
     if (sc.start) sc.start[s] = img ? origin + kFrameLen : kTextStart;
     if (sc.amount) sc.amount[s] = img ? kAmount : 0;
     if (sc.origin) sc.origin[s] = img ? origin : -1;
-    if (sc.flags)
-        sc.flags[s] = (multi ? 1 : 0) | ((img && (int64_t)origin + kFrameLen > len) ? 2 : 0) | (timed_out ? 4 : 0);
+    if (sc.flags) sc.flags[s] = (multi ? 1 : 0) | ((img && (int64_t)origin + kFrameLen > len) ? 2 : 0);
 }
 
 // Scan of one 64-token tile by one full wave, lane i <-> token tile*64 + i.  Publishes the tile's
 // status word, looks back when the tile's first sequence began earlier, writes the scalars of every
 // sequence that ends in the tile, and returns each lane's position and canvas origin.
-__device__ TokenPos scan_tile(const Scan &sc, uint64_t *status, WsHeader *hdr, int64_t tile, uint32_t epoch, int lane)
+__device__ TokenPos scan_tile(const Scan &sc, uint64_t *status, int64_t tile, uint32_t ep, int lane)
 {
     const int64_t t0 = tile * kTile;
     const int64_t g = t0 + lane;
@@ -222,26 +237,24 @@ __device__ TokenPos scan_tile(const Scan &sc, uint64_t *status, WsHeader *hdr, i
     const bool multi_last = __shfl((int)multi, last) != 0;
     const int32_t s_last = __shfl(s, last);
     const int32_t s0 = __shfl(s, 0);
+    const int64_t s0_begin = __shfl(sb, 0);
     const bool need_carry = __shfl((int)(in_seq && sb < t0), 0) != 0;
     const bool last_open = need_carry && s_last == s0;  // the tile's last sequence began before it
 
-    if (lane == 0)
-        astore(status + tile, status_word(epoch, last_open ? kAgg : kIncl, multi_last, first_last));
+    if (lane == 0) astore(status + tile, status_word(ep, last_open ? kAgg : kIncl, multi_last, first_last));
 
-    bool timed_out = false;
     if (need_carry) {
         int32_t cf;
         bool cm;
-        lookback(status, tile, epoch, lane, cf, cm, timed_out);
+        lookback(sc, status, tile, ep, lane, s0_begin, cf, cm);
         if (last_open && lane == 0) {
             const bool mm = cm || multi_last || (cf != kNone && first_last != kNone);
-            astore(status + tile, status_word(epoch, kIncl, mm, min(cf, first_last)));
+            astore(status + tile, status_word(ep, kIncl, mm, min(cf, first_last)));
         }
         if (in_seq && s == s0) {
             multi = multi || cm || (cf != kNone && first != kNone);
             first = min(first, cf);
         }
-        if (timed_out && lane == 0) atomicOr(&hdr->error, 1u);
     }
 
     TokenPos r;
@@ -250,12 +263,11 @@ __device__ TokenPos scan_tile(const Scan &sc, uint64_t *status, WsHeader *hdr, i
     r.o = (in_seq && first != kNone && first <= g) ? (int32_t)(first - sb) : kNone;
 
     if (in_seq && g == se - 1) {
-        write_scalars(sc, s, first == kNone ? -1 : (int32_t)(first - sb), multi, se - sb, timed_out && s == s0);
-        for (int32_t s2 = s + 1; s2 < sc.n_seqs && sc.cu[s2 + 1] == sc.cu[s2]; ++s2)
-            write_scalars(sc, s2, -1, false, 0, false);
+        write_scalars(sc, s, first == kNone ? -1 : (int32_t)(first - sb), multi, se - sb);
+        for (int32_t s2 = s + 1; s2 < sc.n_seqs && sc.cu[s2 + 1] == sc.cu[s2]; ++s2) write_scalars(sc, s2, -1, false, 0);
     }
     if (in_seq && g == 0)
-        for (int32_t s2 = 0; s2 < s; ++s2) write_scalars(sc, s2, -1, false, 0, false);
+        for (int32_t s2 = 0; s2 < s; ++s2) write_scalars(sc, s2, -1, false, 0);
     return r;
 }
 
@@ -335,7 +347,7 @@ __device__ __forceinline__ Raw8<BF16> pack8(const float (&y)[8])
 // ------------------------------------------------------------------ rotary ---------------------
 // (cos, sin) of the 8 frequencies of quarter q4 for planes (pt, ph, pw).
 __device__ __forceinline__ void quarter_sincos(const Rotary &rot, int q4, int32_t pt, int32_t ph, int32_t pw,
-                                               float (&c)[8], float (&s)[8])
+                                               double (&c)[8], double (&s)[8])
 {
     const uint32_t sel = (uint32_t)(rot.plane_sel >> (16 * q4));
 #pragma unroll
@@ -353,16 +365,16 @@ __device__ __forceinline__ void quarter_sincos(const Rotary &rot, int q4, int32_
 
 // Rotate-half on 8 pairs: lo holds dims j, hi holds dims j + 32.
 template <bool BF16>
-__device__ __forceinline__ void rotate8(Raw8<BF16> &lo, Raw8<BF16> &hi, const float (&c)[8], const float (&s)[8])
+__device__ __forceinline__ void rotate8(Raw8<BF16> &lo, Raw8<BF16> &hi, const double (&c)[8], const double (&s)[8])
 {
     float a[8], b[8];
     unpack8<BF16>(lo, a);
     unpack8<BF16>(hi, b);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float x1 = a[i], x2 = b[i];
-        a[i] = __builtin_fmaf(x1, c[i], -(x2 * s[i]));
-        b[i] = __builtin_fmaf(x2, c[i], x1 * s[i]);
+        const double x1 = a[i], x2 = b[i];
+        a[i] = (float)__builtin_fma(x1, c[i], -(x2 * s[i]));
+        b[i] = (float)__builtin_fma(x2, c[i], x1 * s[i]);
     }
     lo = pack8<BF16>(a);
     hi = pack8<BF16>(b);
@@ -377,8 +389,8 @@ __device__ __forceinline__ void copy_tail(const void *src, void *dst, int64_t of
 
 // All heads of one token-quarter: loads first (all in flight), then sincos, then rotate + store.
 template <bool BF16, int NQ, int NK>
-__device__ __forceinline__ void rotate_token_fixed(const Heads &hd, int64_t g, int q4, const float (&c)[8],
-                                                   const float (&s)[8], Raw8<BF16> (&ql)[NQ], Raw8<BF16> (&qh)[NQ],
+__device__ __forceinline__ void rotate_token_fixed(const Heads &hd, int64_t g, int q4, const double (&c)[8],
+                                                   const double (&s)[8], Raw8<BF16> (&ql)[NQ], Raw8<BF16> (&qh)[NQ],
                                                    Raw8<BF16> (&kl)[NK], Raw8<BF16> (&kh)[NK])
 {
     void *qo = hd.q_out ? hd.q_out : hd.q;
@@ -425,8 +437,8 @@ __device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int
 
 // Any head counts: one head at a time.
 template <bool BF16>
-__device__ __forceinline__ void rotate_token_any(const Heads &hd, int64_t g, int q4, const float (&c)[8],
-                                                 const float (&s)[8])
+__device__ __forceinline__ void rotate_token_any(const Heads &hd, int64_t g, int q4, const double (&c)[8],
+                                                 const double (&s)[8])
 {
     for (int hh = 0; hh < hd.nq + hd.nk; ++hh) {
         const bool isq = hh < hd.nq;
@@ -456,7 +468,7 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
     const int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 2);
     if (g >= hd.n_tokens) return;
     const int32_t pt = planes[g], ph = planes[ps + g], pw = planes[2 * ps + g];
-    float c[8], s[8];
+    double c[8], s[8];
     if constexpr (NQ > 0 && NK > 0) {
         Raw8<BF16> ql[NQ], qh[NQ], kl[NK], kh[NK];
         load_token_fixed<BF16, NQ, NK>(hd, g, q4, ql, qh, kl, kh);
@@ -468,51 +480,34 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
     }
 }
 
-__global__ __launch_bounds__(kTile) void planes_kernel(Scan sc, uint32_t n_tiles)
+// One wave per 64-token tile, four tiles per workgroup.
+__global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_tiles)
 {
-    const int lane = threadIdx.x;
-    WsHeader *hdr = static_cast<WsHeader *>(sc.workspace);
-    uint64_t *status = status_array(sc.workspace);
-    uint32_t tk = 0, ep = 0;
-    if (lane == 0) {
-        tk = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ep = aload(&hdr->epoch);
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;
+    const TokenPos r = scan_tile(sc, status_array(sc.workspace), tile, launch_epoch(sc), lane);
+    if (r.valid) {
+        int32_t t, h, w;
+        canvas_planes(r.p, r.o, t, h, w);
+        const int64_t g = tile * kTile + lane;
+        sc.planes[g] = t;
+        sc.planes[sc.plane_stride + g] = h;
+        sc.planes[2 * sc.plane_stride + g] = w;
     }
-    tk = __shfl(tk, 0);
-    ep = __shfl(ep, 0);
-    if (tk < n_tiles) {
-        const TokenPos r = scan_tile(sc, status, hdr, tk, ep, lane);
-        if (r.valid) {
-            int32_t t, h, w;
-            canvas_planes(r.p, r.o, t, h, w);
-            const int64_t g = (int64_t)tk * kTile + lane;
-            sc.planes[g] = t;
-            sc.planes[sc.plane_stride + g] = h;
-            sc.planes[2 * sc.plane_stride + g] = w;
-        }
-    }
-    if (lane == 0) finish_participant(hdr, n_tiles, ep);
 }
 
 template <bool BF16, int NQ, int NK>
-__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, uint32_t n_tiles)
+__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc)
 {
-    __shared__ uint32_t s_tile, s_epoch;
     __shared__ int32_t s_pl[3][kTile];
     __shared__ int32_t s_ok[kTile];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int q4 = tid & 3;
-    WsHeader *hdr = static_cast<WsHeader *>(sc.workspace);
-    if (tid == 0) {
-        s_tile = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_epoch = aload(&hdr->epoch);
-    }
-    __syncthreads();
-    const uint32_t tile = s_tile, ep = s_epoch;
-    const bool live = tile < n_tiles;
-    const int64_t g = (int64_t)tile * kTile + (tid >> 2);
-    const bool tok_ok = live && g < hd.n_tokens;
+    const int64_t tile = blockIdx.x;
+    const int64_t g = tile * kTile + (tid >> 2);
+    const bool tok_ok = g < hd.n_tokens;
 
     // Q/K loads go out before the scan so the look-back hides behind them.
     constexpr bool kFixed = NQ > 0 && NK > 0;
@@ -524,18 +519,15 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
 
     if (tid < 64) {
         int32_t t = 0, h = 0, w = 0;
-        bool ok = false;
-        if (live) {
-            const TokenPos r = scan_tile(sc, status_array(sc.workspace), hdr, tile, ep, lane);
-            ok = r.valid;
-            if (ok) {
-                canvas_planes(r.p, r.o, t, h, w);
-                if (sc.planes) {
-                    const int64_t gg = (int64_t)tile * kTile + lane;
-                    sc.planes[gg] = t;
-                    sc.planes[sc.plane_stride + gg] = h;
-                    sc.planes[2 * sc.plane_stride + gg] = w;
-                }
+        const TokenPos r = scan_tile(sc, status_array(sc.workspace), tile, launch_epoch(sc), lane);
+        const bool ok = r.valid;
+        if (ok) {
+            canvas_planes(r.p, r.o, t, h, w);
+            if (sc.planes) {
+                const int64_t gg = tile * kTile + lane;
+                sc.planes[gg] = t;
+                sc.planes[sc.plane_stride + gg] = h;
+                sc.planes[2 * sc.plane_stride + gg] = w;
             }
         }
         s_pl[0][lane] = t;
@@ -544,11 +536,10 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         s_ok[lane] = ok;
     }
     __syncthreads();
-    if (tid == 0) finish_participant(hdr, n_tiles, ep);
 
     const int tl = tid >> 2;
     if (!tok_ok || !s_ok[tl]) return;
-    float c[8], s[8];
+    double c[8], s[8];
     quarter_sincos(rot, q4, s_pl[0][tl], s_pl[1][tl], s_pl[2][tl], c, s);
     if constexpr (kFixed) {
         rotate_token_fixed<BF16, AQ, AK>(hd, g, q4, c, s, ql, qh, kl, kh);
@@ -580,7 +571,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot
             const int64_t off = isq ? s * d.q_tok + h * d.q_head + 8 * q4 : s * d.k_tok + h * d.k_head + 8 * q4;
             const void *src = isq ? d.q : d.k;
             Raw8<BF16> lo = load8<BF16>(src, off), hi = load8<BF16>(src, off + 32);
-            float c[8], sn[8];
+            double c[8], sn[8];
             quarter_sincos(rot, q4, plane, plane, plane, c, sn);
             rotate8<BF16>(lo, hi, c, sn);
             if (isq) {
@@ -609,7 +600,13 @@ __global__ void zero_kernel(uint32_t *p, size_t words)
 __global__ void text_scalars_kernel(Scan sc)
 {
     const int32_t s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s < sc.n_seqs) write_scalars(sc, s, -1, false, 0, false);
+    if (s < sc.n_seqs) write_scalars(sc, s, -1, false, 0);
+}
+
+// Device-counter epochs: advance the counter once the scan launch before it has finished.
+__global__ void epoch_bump_kernel(WsHeader *hdr)
+{
+    if (threadIdx.x == 0) hdr->epoch = (hdr->epoch + 1u) & kEpochMask;
 }
 
 }  // namespace
@@ -630,11 +627,19 @@ hipError_t launch_text_scalars(const Scan &s, hipStream_t stream)
     return hipGetLastError();
 }
 
+static hipError_t bump_if_device_epoch(const Scan &s, hipStream_t stream)
+{
+    if (s.epoch == 0) epoch_bump_kernel<<<1, 64, 0, stream>>>(static_cast<WsHeader *>(s.workspace));
+    return hipGetLastError();
+}
+
 hipError_t launch_planes(const Scan &s, hipStream_t stream)
 {
-    const uint32_t n_tiles = (uint32_t)((s.n_tokens + kTile - 1) / kTile);
-    planes_kernel<<<n_tiles, kTile, 0, stream>>>(s, n_tiles);
-    return hipGetLastError();
+    const int64_t n_tiles = (s.n_tokens + kTile - 1) / kTile;
+    const unsigned blocks = (unsigned)((n_tiles + kBlock / 64 - 1) / (kBlock / 64));
+    planes_kernel<<<blocks, kBlock, 0, stream>>>(s, n_tiles);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : bump_if_device_epoch(s, stream);
 }
 
 template <bool BF16>
@@ -657,12 +662,13 @@ hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, 
 template <bool BF16>
 static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, hipStream_t st)
 {
-    const uint32_t n_tiles = (uint32_t)((h.n_tokens + kTile - 1) / kTile);
+    const unsigned n_tiles = (unsigned)((h.n_tokens + kTile - 1) / kTile);
     if (h.nq == 8 && h.nk == 2)
-        apply_ids_kernel<BF16, 8, 2><<<n_tiles, kBlock, 0, st>>>(h, r, s, n_tiles);
+        apply_ids_kernel<BF16, 8, 2><<<n_tiles, kBlock, 0, st>>>(h, r, s);
     else
-        apply_ids_kernel<BF16, 0, 0><<<n_tiles, kBlock, 0, st>>>(h, r, s, n_tiles);
-    return hipGetLastError();
+        apply_ids_kernel<BF16, 0, 0><<<n_tiles, kBlock, 0, st>>>(h, r, s);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : bump_if_device_epoch(s, st);
 }
 
 hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, bool bf16, hipStream_t stream)

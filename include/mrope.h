@@ -53,14 +53,12 @@ typedef enum {
 
 typedef enum {
     MROPE_F32 = 0,   /* float32 Q/K/cache */
-    MROPE_BF16 = 1   /* bfloat16 Q/K/cache; math in fp32, one round-to-nearest-even per output */
+    MROPE_BF16 = 1   /* bfloat16 Q/K/cache */
 } mrope_dtype;
 
 /* seq_flags bits (optional per-sequence output of the plane-deriving calls). */
 #define MROPE_SEQ_MULTI_MARKER 1u /* more than one <image> marker; planes follow the first frame */
 #define MROPE_SEQ_FRAME_OVERRUN 2u /* the frame (67 tokens from the marker) runs past the end     */
-#define MROPE_SEQ_LOOKBACK_TIMEOUT 4u /* a scan tile gave up waiting for its predecessor (workspace
-                                         not initialised or shared by concurrent calls)            */
 
 /* Text-only sequences get start = 2^30 and amount = 0 (card, start/amount paragraph). */
 #define MROPE_TEXT_ONLY_START (1 << 30)
@@ -77,9 +75,18 @@ const char *mrope_last_error(void);
  * Workspace for the calls that derive planes from ids (mrope_planes, mrope_apply_ids).
  *
  * Returns the bytes needed for n_tokens packed tokens.  The workspace must be 256-byte aligned
- * device memory, and must be zero-filled (or passed once through mrope_workspace_init) before its
- * first use.  Each call leaves it ready for the next one; do not clear it between calls.  It holds
- * a tile ticket counter, a finish counter, an epoch and one 64-bit status word per 64-token tile.
+ * device memory, zero-filled (or passed once through mrope_workspace_init) before its first use;
+ * it needs no clearing between calls.  It holds a device epoch counter and one 64-bit status word
+ * per 64-token tile, through which a tile hands the first marker of a sequence to the next tiles.
+ *
+ * Epochs.  The plane-deriving calls take an `epoch` that tags the status words they write, so a
+ * call never mistakes words left by an earlier call for its own:
+ *   epoch != 0  the caller's tag (low 29 bits used); it must differ from the epoch of the previous
+ *               call on the same workspace (a call counter does).  No extra work.
+ *   epoch == 0  the library reads a counter held in the workspace and advances it with a
+ *               one-thread kernel after the scan -- use this when the call is captured in a HIP
+ *               graph, whose replays would otherwise repeat one tag.
+ * Device-counter tags carry bit 29, caller tags never do, so the two kinds can share a workspace.
  * ------------------------------------------------------------------------------------------- */
 size_t mrope_workspace_bytes(int64_t n_tokens);
 
@@ -108,13 +115,17 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  * seq_flags  [n_seqs] int32 out (nullable): MROPE_SEQ_* bits.
  * workspace  see mrope_workspace_bytes(n_tokens).
  *
- * One launch: each 64-token tile finds its markers with a wavefront ballot and takes the first
- * marker of a sequence that began in an earlier tile from its predecessors by decoupled look-back.
+ * epoch      see mrope_workspace_bytes.
+ *
+ * One launch (plus a one-thread kernel when epoch == 0): each 64-token tile finds its markers with a
+ * wavefront ballot and takes the first marker of a sequence that began in an earlier tile from its
+ * predecessors by a wait-free decoupled look-back (a predecessor that has not published yet is
+ * evaluated from its ids), so no tile ever waits on another.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
                           int32_t marker_id, int32_t *planes, int64_t plane_stride, int32_t *start,
                           int32_t *amount, int32_t *origin, int32_t *seq_flags, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          size_t workspace_bytes, uint32_t epoch, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mrope_apply -- rotate Q and K heads with given planes ([card] "What it is": interleaved sections).
@@ -130,6 +141,9 @@ mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t
  *            pos_j is the T, H or W plane of the token by the rule in the file header.
  * planes     [3][plane_stride] int32 (as written by mrope_planes); |plane| < 2^24.
  * theta      rotary base (1e7 for the model), > 0 and finite.
+ * Precision: the angle is the fp32 product above; cos, sin and the two products of each output are
+ *            double; each output is rounded to nearest-even once to fp32 and, for bf16, once more to
+ *            bf16.
  * q_out, k_out  NULL: rotate in place (dims >= rot_dim are never read or written).  Otherwise the
  *            full heads are written there, with the same strides as q / k (no aliasing with the
  *            inputs).  Both NULL or both non-NULL (k_out may be NULL when n_k_heads == 0).
@@ -141,10 +155,11 @@ mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, i
                          int64_t plane_stride, double theta, void *q_out, void *k_out, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
- * mrope_apply_ids -- planes derivation and rotation fused in ONE launch: ids -> first marker per
- * sequence -> planes (in registers) -> rotate Q and K.  Arguments as in mrope_planes and
- * mrope_apply; planes_out (nullable) additionally receives the planes ([3][plane_stride]).
- * n_tokens must equal cu_seqlens[n_seqs].
+ * mrope_apply_ids -- planes derivation and rotation fused in ONE launch (plus a one-thread kernel
+ * when epoch == 0): ids -> first marker per sequence -> planes (kept in LDS) -> rotate Q and K.
+ * Arguments as in mrope_planes and mrope_apply; planes_out (nullable) additionally receives the
+ * planes ([3][plane_stride]).  n_tokens must equal cu_seqlens[n_seqs].  The Q/K loads of a tile are
+ * issued before its look-back, which hides behind them.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
@@ -152,7 +167,7 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              void *k_out, const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs,
                              int32_t marker_id, int32_t *planes_out, int64_t plane_stride, int32_t *start,
                              int32_t *amount, int32_t *origin, int32_t *seq_flags, void *workspace,
-                             size_t workspace_bytes, void *stream);
+                             size_t workspace_bytes, uint32_t epoch, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mrope_decode -- one generated token per sequence ([card] canvas table, last row: every position

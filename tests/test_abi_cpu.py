@@ -71,7 +71,7 @@ def _planes(lib, **kw):
     a = dict(ids=A, cu=A, ns=4, n=1000, marker=248078, planes=A, ps=1000, ws=A, wsb=10 ** 6)
     a.update(kw)
     return lib.mrope_planes(a["ids"], a["cu"], a["ns"], a["n"], a["marker"], a["planes"], a["ps"], None, None, None,
-                            None, a["ws"], a["wsb"], None)
+                            None, a["ws"], a["wsb"], 1, None)
 
 
 @pytest.mark.parametrize("kw,code", [

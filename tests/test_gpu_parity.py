@@ -330,3 +330,84 @@ def test_workspace_reuse_across_sizes():
         b = synth.random_batch(seed, 20 + 30 * i, max_len=400 + 200 * i, empty_frac=0.05)
         pl, st, am, og, fl = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER, workspace=ws)
         _check_scan(b, pl, st, am, og, fl, f"reuse {i}")
+
+
+def test_device_epoch_mode_through_c_abi():
+    """epoch = 0: the library tags status words from its device counter and advances it after each
+    call (one extra one-thread kernel); back-to-back calls with new inputs stay exact."""
+    import ctypes
+
+    lib = mr._lib.load()
+    ws = mr.Workspace(1 << 15)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i, seed in enumerate((61, 62, 63, 64)):
+        b = synth.random_batch(seed, 40, max_len=700)
+        ids, cu = i32(b.ids), i32(b.cu_seqlens)
+        L, n = b.n_tokens, b.n_seqs
+        pl = torch.empty((3, L), dtype=torch.int32, device="cuda")
+        st, am, og, fl = (torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(4))
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        ws.ensure(L)
+        rc = lib.mrope_planes(p(ids), p(cu), n, L, MARKER, p(pl), L, p(st), p(am), p(og), p(fl), ws.ptr, ws.capacity,
+                              0, stream)
+        assert rc == 0
+        _check_scan(b, pl, st, am, og, fl, f"device epoch call {i}")
+    hdr = ws.view[:4].view(torch.int32).item()
+    assert hdr == 4
+
+
+def test_graph_replays_with_new_inputs():
+    """planes + apply captured in a HIP graph; between replays new ids and Q/K are copied into the
+    captured buffers (eager work in between); every replay matches the oracle."""
+    L, n = 6000, 24
+    batches = []
+    for seed in (71, 72, 73):
+        g = np.random.default_rng(seed)
+        cuts = np.sort(g.choice(np.arange(1, L), size=n - 1, replace=False))
+        lens = np.diff(np.concatenate([[0], cuts, [L]]))
+        placed = [int(g.integers(0, max(1, m - 67))) if g.uniform() < 0.7 else None for m in lens]
+        gi = synth.rng(seed, 4)
+        ids = np.concatenate([synth.prompt_ids(gi, int(m), o) for m, o in zip(lens, placed)])
+        cu = np.zeros(n + 1, np.int32)
+        cu[1:] = np.cumsum(lens)
+        b = synth.Prefill(f"graph{seed}", ids, cu, placed, "bf16", seed=seed)
+        batches.append((b,) + b.qk())
+    ids_d = torch.zeros(L, dtype=torch.int32, device="cuda")
+    cu_d = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    q_d = torch.zeros((L, 8, 256), dtype=torch.bfloat16, device="cuda")
+    k_d = torch.zeros((L, 2, 256), dtype=torch.bfloat16, device="cuda")
+    pl_d = torch.zeros((3, L), dtype=torch.int32, device="cuda")
+    st_d, am_d, og_d, fl_d = (torch.zeros(n, dtype=torch.int32, device="cuda") for _ in range(4))
+    ws = mr.Workspace(L)
+
+    def load(bt):
+        b, qn, kn = bt
+        ids_d.copy_(i32(b.ids))
+        cu_d.copy_(i32(b.cu_seqlens))
+        q_d.copy_(dev_heads(qn, "bf16"))
+        k_d.copy_(dev_heads(kn, "bf16"))
+
+    def body():
+        mr.planes(ids_d, cu_d, MARKER, out=pl_d, start=st_d, amount=am_d, origin=og_d, seq_flags=fl_d, workspace=ws)
+        mr.apply(q_d, k_d, pl_d)
+
+    load(batches[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()                     # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    for rep in range(6):
+        bt = batches[rep % 3]
+        load(bt)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        b, qn, kn = bt
+        epl, *_ = _check_scan(b, pl_d, st_d, am_d, og_d, fl_d, f"replay {rep}")
+        compare_heads(host_heads(q_d), qn, epl, "bf16", what=f"replay {rep} q")
+        compare_heads(host_heads(k_d), kn, epl, "bf16", what=f"replay {rep} k")
+        _ = torch.randn(1000, device="cuda").sum().item()   # unrelated eager work between replays
