@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--mode", choices=("bench", "copy"), default="bench",
+                    help="copy: only a plain 1 GiB device copy, repeated (calibrates rocprofv3 HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the method shards by "
@@ -112,6 +114,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "copy":
+        # plain copy of known size: every dispatch reads 1 GiB and writes 1 GiB
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_dispatch": 1 << 30, "bytes_written_per_dispatch": 1 << 30,
+                          "dispatches": args.steps}), flush=True)
+        return
     mr._lib.load()
 
     b = synth.config2()

@@ -14,11 +14,12 @@
 //   apply_ids_kernel  the two above in one launch; planes stay in LDS
 //   decode_kernel     one token per sequence: Q in place, K rotated and scattered to a paged cache
 //
-// Thread layout of the rotary kernels: four lanes per token, lane quarter q4 owns frequencies
-// 8*q4 .. 8*q4+7, i.e. dims [8*q4, 8*q4+8) and [32+8*q4, 32+8*q4+8) of every head.  A lane computes
-// its 8 (cos, sin) pairs once and applies them to all heads of its token, so each sincos is done once
-// per token, with no LDS traffic and no cross-lane exchange.  Each head is one 128-byte line (bf16):
-// the four lanes of a token read it as two 64-byte runs.
+// Thread layout of the rotary kernels: eight lanes per token; lane pair m holds frequencies
+// 8m .. 8m+7, one lane the x_j dims and its neighbour the x_{j+32} dims of every head, so the eight
+// lanes of a token read or write one whole 128-byte line (bf16) per instruction.  Partners swap data
+// by DPP; each sincos is evaluated once per token, and a lane applies its (cos, sin) to all heads of
+// its token.  (Four lanes per token, each reading the two 64-byte halves of a line with two
+// instructions, measured 25% slower on this access pattern.)
 //
 // Precision: the angle is one fp32 multiply (as the model's rotary forms it); cos/sin and the two
 // products of each output are double (the same per-lane rate as fp32 on this chip with packed fp32
@@ -345,139 +346,185 @@ __device__ __forceinline__ Raw8<BF16> pack8(const float (&y)[8])
 }
 
 // ------------------------------------------------------------------ rotary ---------------------
-// (cos, sin) of the 8 frequencies of quarter q4 for planes (pt, ph, pw).
-__device__ __forceinline__ void quarter_sincos(const Rotary &rot, int q4, int32_t pt, int32_t ph, int32_t pw,
-                                               double (&c)[8], double (&s)[8])
+// Lane layout: eight lanes per token.  Lane l = 2m + half holds the 8 consecutive dims
+// [32*half + 8m, 32*half + 8m + 8) of a head: frequencies j = 8m .. 8m+7, the x_j side (half 0) or
+// the x_{j+32} side (half 1).  The eight lanes of a token cover one whole 128-byte line per head
+// (bf16) with one load instruction, and rotate-half partners are neighbour lanes (l, l^1), which
+// swap their data with one DPP move per dword.
+
+// Value of the neighbour lane (l ^ 1) by DPP quad_perm [1,0,3,2].
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v)
 {
-    const uint32_t sel = (uint32_t)(rot.plane_sel >> (16 * q4));
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ double swap_pair(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = swap_pair((uint32_t)u), hi = swap_pair((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> swap_pair(const Raw8<BF16> &r)
+{
+    Raw8<BF16> o;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int k = 0; k < (BF16 ? 1 : 2); ++k)
+        o.w[k] = make_uint4(swap_pair(r.w[k].x), swap_pair(r.w[k].y), swap_pair(r.w[k].z), swap_pair(r.w[k].w));
+    return o;
+}
+
+// (cos, sign*sin) of frequencies 8m .. 8m+7 for lane pair m.  Each lane evaluates four of them
+// (half 0: 8m..8m+3, half 1: 8m+4..8m+7) and the pair swaps results.  ss = -sin on the x_j side
+// and +sin on the x_{j+32} side, so every output is y = own*c + partner*ss.
+__device__ __forceinline__ void pair_sincos(const Rotary &rot, int m, int half, int32_t pt, int32_t ph, int32_t pw,
+                                            double (&c)[8], double (&ss)[8])
+{
+    const int j0 = 8 * m + 4 * half;
+    const uint32_t sel = (uint32_t)(rot.plane_sel >> (2 * j0));
+    double oc[4], os[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
         const uint32_t pl = (sel >> (2 * i)) & 3u;
         const int32_t pos = pl == 1u ? ph : (pl == 2u ? pw : pt);
-        const float f = q4 == 0 ? rot.inv_freq[i]
-                      : q4 == 1 ? rot.inv_freq[8 + i]
-                      : q4 == 2 ? rot.inv_freq[16 + i]
-                                : rot.inv_freq[24 + i];
-        const float a = (float)pos * f;
-        sincos_angle(a, &s[i], &c[i]);
+        const float a = (float)pos * rot.inv_freq[j0 + i];
+        sincos_angle(a, &os[i], &oc[i]);
     }
-}
-
-// Rotate-half on 8 pairs: lo holds dims j, hi holds dims j + 32.
-template <bool BF16>
-__device__ __forceinline__ void rotate8(Raw8<BF16> &lo, Raw8<BF16> &hi, const double (&c)[8], const double (&s)[8])
-{
-    float a[8], b[8];
-    unpack8<BF16>(lo, a);
-    unpack8<BF16>(hi, b);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const double x1 = a[i], x2 = b[i];
-        a[i] = (float)__builtin_fma(x1, c[i], -(x2 * s[i]));
-        b[i] = (float)__builtin_fma(x2, c[i], x1 * s[i]);
+    for (int i = 0; i < 4; ++i) {
+        const double pc = swap_pair(oc[i]), ps = swap_pair(os[i]);
+        c[i] = half ? pc : oc[i];
+        c[4 + i] = half ? oc[i] : pc;
+        const double s_lo = half ? ps : os[i], s_hi = half ? os[i] : ps;
+        ss[i] = half ? s_lo : -s_lo;
+        ss[4 + i] = half ? s_hi : -s_hi;
     }
-    lo = pack8<BF16>(a);
-    hi = pack8<BF16>(b);
 }
 
-// Copy this quarter's share of the dims past the rotary part (out-of-place calls only).
+// One head chunk: own holds this lane's 8 dims, the partner's come by DPP.
 template <bool BF16>
-__device__ __forceinline__ void copy_tail(const void *src, void *dst, int64_t off, int head_dim, int q4)
+__device__ __forceinline__ Raw8<BF16> rotate_chunk(const Raw8<BF16> &own, const double (&c)[8], const double (&ss)[8])
 {
-    for (int d = 64 + 8 * q4; d < head_dim; d += 32) store8<BF16>(dst, off + d, load8<BF16>(src, off + d));
+    float x[8], p[8], y[8];
+    unpack8<BF16>(own, x);
+    unpack8<BF16>(swap_pair<BF16>(own), p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (float)__builtin_fma((double)x[e], c[e], (double)p[e] * ss[e]);
+    return pack8<BF16>(y);
 }
 
-// All heads of one token-quarter: loads first (all in flight), then sincos, then rotate + store.
+// Copy this lane's share of the dims past the rotary part (out-of-place calls only).
+template <bool BF16>
+__device__ __forceinline__ void copy_tail(const void *src, void *dst, int64_t off, int head_dim, int l)
+{
+    for (int d = 64 + 8 * l; d < head_dim; d += 64) store8<BF16>(dst, off + d, load8<BF16>(src, off + d));
+}
+
+__device__ __forceinline__ int64_t q_off(const Heads &hd, int64_t g, int h) { return g * hd.q_tok + h * hd.q_head; }
+__device__ __forceinline__ int64_t k_off(const Heads &hd, int64_t g, int h) { return g * hd.k_tok + h * hd.k_head; }
+
 template <bool BF16, int NQ, int NK>
-__device__ __forceinline__ void rotate_token_fixed(const Heads &hd, int64_t g, int q4, const double (&c)[8],
-                                                   const double (&s)[8], Raw8<BF16> (&ql)[NQ], Raw8<BF16> (&qh)[NQ],
-                                                   Raw8<BF16> (&kl)[NK], Raw8<BF16> (&kh)[NK])
+__device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int e0, Raw8<BF16> (&qv)[NQ],
+                                                 Raw8<BF16> (&kv)[NK])
+{
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) qv[h] = load8<BF16>(hd.q, q_off(hd, g, h) + e0);
+#pragma unroll
+    for (int h = 0; h < NK; ++h) kv[h] = load8<BF16>(hd.k, k_off(hd, g, h) + e0);
+}
+
+template <bool BF16, int NQ, int NK>
+__device__ __forceinline__ void rotate_token_fixed(const Heads &hd, int64_t g, int e0, int l, const double (&c)[8],
+                                                   const double (&ss)[8], const Raw8<BF16> (&qv)[NQ],
+                                                   const Raw8<BF16> (&kv)[NK])
 {
     void *qo = hd.q_out ? hd.q_out : hd.q;
     void *ko = hd.k_out ? hd.k_out : hd.k;
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) {
-        const int64_t off = g * hd.q_tok + h * hd.q_head + 8 * q4;
-        rotate8<BF16>(ql[h], qh[h], c, s);
-        store8<BF16>(qo, off, ql[h]);
-        store8<BF16>(qo, off + 32, qh[h]);
-    }
+    for (int h = 0; h < NQ; ++h) store8<BF16>(qo, q_off(hd, g, h) + e0, rotate_chunk<BF16>(qv[h], c, ss));
 #pragma unroll
-    for (int h = 0; h < NK; ++h) {
-        const int64_t off = g * hd.k_tok + h * hd.k_head + 8 * q4;
-        rotate8<BF16>(kl[h], kh[h], c, s);
-        store8<BF16>(ko, off, kl[h]);
-        store8<BF16>(ko, off + 32, kh[h]);
-    }
+    for (int h = 0; h < NK; ++h) store8<BF16>(ko, k_off(hd, g, h) + e0, rotate_chunk<BF16>(kv[h], c, ss));
     if (hd.q_out) {
-#pragma unroll
-        for (int h = 0; h < NQ; ++h) copy_tail<BF16>(hd.q, hd.q_out, g * hd.q_tok + h * hd.q_head, hd.head_dim, q4);
-#pragma unroll
-        for (int h = 0; h < NK; ++h) copy_tail<BF16>(hd.k, hd.k_out, g * hd.k_tok + h * hd.k_head, hd.head_dim, q4);
-    }
-}
-
-template <bool BF16, int NQ, int NK>
-__device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int q4, Raw8<BF16> (&ql)[NQ],
-                                                 Raw8<BF16> (&qh)[NQ], Raw8<BF16> (&kl)[NK], Raw8<BF16> (&kh)[NK])
-{
-#pragma unroll
-    for (int h = 0; h < NQ; ++h) {
-        const int64_t off = g * hd.q_tok + h * hd.q_head + 8 * q4;
-        ql[h] = load8<BF16>(hd.q, off);
-        qh[h] = load8<BF16>(hd.q, off + 32);
-    }
-#pragma unroll
-    for (int h = 0; h < NK; ++h) {
-        const int64_t off = g * hd.k_tok + h * hd.k_head + 8 * q4;
-        kl[h] = load8<BF16>(hd.k, off);
-        kh[h] = load8<BF16>(hd.k, off + 32);
+        for (int h = 0; h < NQ; ++h) copy_tail<BF16>(hd.q, hd.q_out, q_off(hd, g, h), hd.head_dim, l);
+        for (int h = 0; h < NK; ++h) copy_tail<BF16>(hd.k, hd.k_out, k_off(hd, g, h), hd.head_dim, l);
     }
 }
 
 // Any head counts: one head at a time.
 template <bool BF16>
-__device__ __forceinline__ void rotate_token_any(const Heads &hd, int64_t g, int q4, const double (&c)[8],
-                                                 const double (&s)[8])
+__device__ __forceinline__ void rotate_token_any(const Heads &hd, int64_t g, int e0, int l, const double (&c)[8],
+                                                 const double (&ss)[8])
 {
     for (int hh = 0; hh < hd.nq + hd.nk; ++hh) {
         const bool isq = hh < hd.nq;
         const int h = isq ? hh : hh - hd.nq;
         void *src = isq ? hd.q : hd.k;
         void *dst = isq ? (hd.q_out ? hd.q_out : hd.q) : (hd.k_out ? hd.k_out : hd.k);
-        const int64_t base = isq ? g * hd.q_tok + h * hd.q_head : g * hd.k_tok + h * hd.k_head;
-        const int64_t off = base + 8 * q4;
-        Raw8<BF16> lo = load8<BF16>(src, off), hi = load8<BF16>(src, off + 32);
-        rotate8<BF16>(lo, hi, c, s);
-        store8<BF16>(dst, off, lo);
-        store8<BF16>(dst, off + 32, hi);
-        if (hd.q_out) copy_tail<BF16>(src, dst, base, hd.head_dim, q4);
+        const int64_t base = isq ? q_off(hd, g, h) : k_off(hd, g, h);
+        store8<BF16>(dst, base + e0, rotate_chunk<BF16>(load8<BF16>(src, base + e0), c, ss));
+        if (hd.q_out) copy_tail<BF16>(src, dst, base, hd.head_dim, l);
     }
 }
 
 // ------------------------------------------------------------------ kernels --------------------
-constexpr int kBlock = 256;           // 4 waves
-constexpr int kTokPerBlock = kBlock / 4;
+constexpr int kBlock = 256;                 // 4 waves
+constexpr int kLanesPerTok = 8;
+constexpr int kTokPerBlock = kBlock / kLanesPerTok;
 
+// Fixed head counts: a grid-stride loop over tokens (the grid is sized to the chip by the host).
+// Each 8-lane group prefetches the next token's planes and head chunks before it rotates and
+// stores the current one, so loads stay in flight while the sincos and rotation math runs.
 template <bool BF16, int NQ, int NK>
 __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
                                                        int64_t ps)
 {
     const int tid = threadIdx.x;
-    const int q4 = tid & 3;
-    const int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 2);
-    if (g >= hd.n_tokens) return;
-    const int32_t pt = planes[g], ph = planes[ps + g], pw = planes[2 * ps + g];
-    double c[8], s[8];
-    if constexpr (NQ > 0 && NK > 0) {
-        Raw8<BF16> ql[NQ], qh[NQ], kl[NK], kh[NK];
-        load_token_fixed<BF16, NQ, NK>(hd, g, q4, ql, qh, kl, kh);
-        quarter_sincos(rot, q4, pt, ph, pw, c, s);
-        rotate_token_fixed<BF16, NQ, NK>(hd, g, q4, c, s, ql, qh, kl, kh);
-    } else {
-        quarter_sincos(rot, q4, pt, ph, pw, c, s);
-        rotate_token_any<BF16>(hd, g, q4, c, s);
+    const int l = tid & 7, m = l >> 1, half = l & 1;
+    const int e0 = 32 * half + 8 * m;
+    const int64_t stride = (int64_t)gridDim.x * kTokPerBlock;
+    int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 3);
+    if (g >= hd.n_tokens) return;   // the eight lanes of a token leave together
+    int32_t pt = planes[g], ph = planes[ps + g], pw = planes[2 * ps + g];
+    Raw8<BF16> qv[NQ], kv[NK];
+    load_token_fixed<BF16, NQ, NK>(hd, g, e0, qv, kv);
+    while (true) {
+        const int64_t gn = g + stride;
+        const bool more = gn < hd.n_tokens;
+        int32_t nt = 0, nh = 0, nw = 0;
+        Raw8<BF16> qn[NQ], kn[NK];
+        if (more) {
+            nt = planes[gn];
+            nh = planes[ps + gn];
+            nw = planes[2 * ps + gn];
+            load_token_fixed<BF16, NQ, NK>(hd, gn, e0, qn, kn);
+        }
+        double c[8], ss[8];
+        pair_sincos(rot, m, half, pt, ph, pw, c, ss);
+        rotate_token_fixed<BF16, NQ, NK>(hd, g, e0, l, c, ss, qv, kv);
+        if (!more) break;
+        g = gn;
+        pt = nt;
+        ph = nh;
+        pw = nw;
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) qv[h] = qn[h];
+#pragma unroll
+        for (int h = 0; h < NK; ++h) kv[h] = kn[h];
     }
+}
+
+// Any head counts: one token per 8-lane group, one head at a time.
+template <bool BF16>
+__global__ __launch_bounds__(kBlock) void apply_any_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
+                                                           int64_t ps)
+{
+    const int tid = threadIdx.x;
+    const int l = tid & 7, m = l >> 1, half = l & 1;
+    const int e0 = 32 * half + 8 * m;
+    const int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 3);
+    if (g >= hd.n_tokens) return;
+    double c[8], ss[8];
+    pair_sincos(rot, m, half, planes[g], planes[ps + g], planes[2 * ps + g], c, ss);
+    rotate_token_any<BF16>(hd, g, e0, l, c, ss);
 }
 
 // One wave per 64-token tile, four tiles per workgroup.
@@ -497,24 +544,29 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_tiles
     }
 }
 
+// One 64-token tile per workgroup of 512 threads (eight lanes per token); wave 0 scans the tile.
+constexpr int kIdsBlock = kTile * kLanesPerTok;
+
 template <bool BF16, int NQ, int NK>
-__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc)
+__global__ __launch_bounds__(kIdsBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc)
 {
     __shared__ int32_t s_pl[3][kTile];
     __shared__ int32_t s_ok[kTile];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int q4 = tid & 3;
+    const int l = tid & 7, m = l >> 1, half = l & 1;
+    const int e0 = 32 * half + 8 * m;
     const int64_t tile = blockIdx.x;
-    const int64_t g = tile * kTile + (tid >> 2);
+    const int tl = tid >> 3;
+    const int64_t g = tile * kTile + tl;
     const bool tok_ok = g < hd.n_tokens;
 
     // Q/K loads go out before the scan so the look-back hides behind them.
     constexpr bool kFixed = NQ > 0 && NK > 0;
     constexpr int AQ = kFixed ? NQ : 1, AK = kFixed ? NK : 1;
-    Raw8<BF16> ql[AQ], qh[AQ], kl[AK], kh[AK];
+    Raw8<BF16> qv[AQ], kv[AK];
     if constexpr (kFixed) {
-        if (tok_ok) load_token_fixed<BF16, AQ, AK>(hd, g, q4, ql, qh, kl, kh);
+        if (tok_ok) load_token_fixed<BF16, AQ, AK>(hd, g, e0, qv, kv);
     }
 
     if (tid < 64) {
@@ -537,19 +589,18 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     }
     __syncthreads();
 
-    const int tl = tid >> 2;
-    if (!tok_ok || !s_ok[tl]) return;
-    double c[8], s[8];
-    quarter_sincos(rot, q4, s_pl[0][tl], s_pl[1][tl], s_pl[2][tl], c, s);
+    if (!tok_ok || !s_ok[tl]) return;   // the eight lanes of a token leave together
+    double c[8], ss[8];
+    pair_sincos(rot, m, half, s_pl[0][tl], s_pl[1][tl], s_pl[2][tl], c, ss);
     if constexpr (kFixed) {
-        rotate_token_fixed<BF16, AQ, AK>(hd, g, q4, c, s, ql, qh, kl, kh);
+        rotate_token_fixed<BF16, AQ, AK>(hd, g, e0, l, c, ss, qv, kv);
     } else {
-        rotate_token_any<BF16>(hd, g, q4, c, s);
+        rotate_token_any<BF16>(hd, g, e0, l, c, ss);
     }
 }
 
-// One wave per sequence.  Work items of a wave: Q rotation (nq*4 quarters, in place), K rotation
-// (nk*4 quarters, to the cache) and K pass-through copies (16-byte chunks past the rotary dims).
+// One wave per sequence.  Work items of a wave, eight lanes each: the Q heads (rotated in place),
+// the K heads (rotated into the cache), then 16-byte K pass-through chunks past the rotary dims.
 template <bool BF16>
 __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot)
 {
@@ -560,37 +611,32 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot
     const int64_t slot = d.slots[s];
     const bool wr = slot >= 0 && slot < d.num_slots;
     const int64_t cbase = wr ? (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok : 0;
-    const int nrq = d.nq * 4, nrk = d.nk * 4;
+    const int nrq = d.nq * 8, nrk = d.nk * 8;
     const int chunks = (d.head_dim - 64) / 8;
     const int total = nrq + nrk + d.nk * chunks;
     for (int it = lane; it < total; it += 64) {
-        if (it < nrq + nrk) {
+        if (it < nrq + nrk) {   // a whole 8-lane group takes this branch together
             const bool isq = it < nrq;
-            const int h = (isq ? it : it - nrq) >> 2;
-            const int q4 = it & 3;
-            const int64_t off = isq ? s * d.q_tok + h * d.q_head + 8 * q4 : s * d.k_tok + h * d.k_head + 8 * q4;
-            const void *src = isq ? d.q : d.k;
-            Raw8<BF16> lo = load8<BF16>(src, off), hi = load8<BF16>(src, off + 32);
-            double c[8], sn[8];
-            quarter_sincos(rot, q4, plane, plane, plane, c, sn);
-            rotate8<BF16>(lo, hi, c, sn);
-            if (isq) {
-                store8<BF16>(d.q, off, lo);
-                store8<BF16>(d.q, off + 32, hi);
-            } else if (wr) {
-                const int64_t co = cbase + h * d.c_head + 8 * q4;
-                store8<BF16>(d.cache, co, lo);
-                store8<BF16>(d.cache, co + 32, hi);
-            }
+            const int h = (isq ? it : it - nrq) >> 3;
+            const int l = it & 7, m = l >> 1, half = l & 1;
+            const int e0 = 32 * half + 8 * m;
+            const int64_t off = (isq ? s * d.q_tok + h * d.q_head : s * d.k_tok + h * d.k_head) + e0;
+            const Raw8<BF16> own = load8<BF16>(isq ? d.q : d.k, off);
+            double c[8], ss[8];
+            pair_sincos(rot, m, half, plane, plane, plane, c, ss);
+            const Raw8<BF16> y = rotate_chunk<BF16>(own, c, ss);
+            if (isq)
+                store8<BF16>(d.q, off, y);
+            else if (wr)
+                store8<BF16>(d.cache, cbase + h * d.c_head + e0, y);
         } else if (wr) {
-            const int c = it - nrq - nrk;
-            const int h = c / chunks;
-            const int e = 64 + (c % chunks) * 8;
+            const int cc = it - nrq - nrk;
+            const int h = cc / chunks;
+            const int e = 64 + (cc % chunks) * 8;
             store8<BF16>(d.cache, cbase + h * d.c_head + e, load8<BF16>(d.k, s * d.k_tok + h * d.k_head + e));
         }
     }
 }
-
 __global__ void zero_kernel(uint32_t *p, size_t words)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
@@ -642,14 +688,31 @@ hipError_t launch_planes(const Scan &s, hipStream_t stream)
     return e != hipSuccess ? e : bump_if_device_epoch(s, stream);
 }
 
+// Workgroups per compute unit of the grid-stride rotary kernel (its VGPR use allows two resident).
+#ifndef MROPE_APPLY_BLOCKS_PER_CU
+#define MROPE_APPLY_BLOCKS_PER_CU 2
+#endif
+constexpr int kApplyBlocksPerCU = MROPE_APPLY_BLOCKS_PER_CU;
+
+static int compute_units()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 256;
+    return cus > 0 ? cus : 256;
+}
+
 template <bool BF16>
 static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, hipStream_t st)
 {
-    const unsigned blocks = (unsigned)((h.n_tokens + kTokPerBlock - 1) / kTokPerBlock);
-    if (h.nq == 8 && h.nk == 2)
+    const int64_t groups = (h.n_tokens + kTokPerBlock - 1) / kTokPerBlock;
+    if (h.nq == 8 && h.nk == 2) {
+        const int64_t cap = (int64_t)compute_units() * kApplyBlocksPerCU;
+        const unsigned blocks = (unsigned)(groups < cap ? groups : cap);
         apply_kernel<BF16, 8, 2><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
-    else
-        apply_kernel<BF16, 0, 0><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
+    } else {
+        apply_any_kernel<BF16><<<(unsigned)groups, kBlock, 0, st>>>(h, r, planes, ps);
+    }
     return hipGetLastError();
 }
 
@@ -664,9 +727,9 @@ static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan
 {
     const unsigned n_tiles = (unsigned)((h.n_tokens + kTile - 1) / kTile);
     if (h.nq == 8 && h.nk == 2)
-        apply_ids_kernel<BF16, 8, 2><<<n_tiles, kBlock, 0, st>>>(h, r, s);
+        apply_ids_kernel<BF16, 8, 2><<<n_tiles, kIdsBlock, 0, st>>>(h, r, s);
     else
-        apply_ids_kernel<BF16, 0, 0><<<n_tiles, kBlock, 0, st>>>(h, r, s);
+        apply_ids_kernel<BF16, 0, 0><<<n_tiles, kIdsBlock, 0, st>>>(h, r, s);
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : bump_if_device_epoch(s, st);
 }
