@@ -8,7 +8,8 @@ tokens (262,144 tokens), <image> at O ~ U{0..512}, Q/K ~ N(0, 1) from a fixed se
 in HBM before the timed region.
 
 Prints one JSON line: tokens/s over the timed steps, the roofline of the dominant kernel
-(mrope_apply: algorithmic bytes / mean launch time from HIP events on its stream, against 8 TB/s),
+(mrope_apply: algorithmic bytes / mean time of back-to-back launches from HIP events on its stream,
+against 8 TB/s),
 and the CPU oracle timed on this host over the same workload.
 """
 from __future__ import annotations
@@ -97,6 +98,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cold", action="store_true", help="also time mrope_apply after a cache-clearing read sweep")
     ap.add_argument("--mode", choices=("bench", "copy"), default="bench",
                     help="copy: only a plain 1 GiB device copy, repeated (calibrates rocprofv3 HBM counters)")
     args = ap.parse_args()
@@ -142,14 +144,19 @@ def main():
     ws = mr.Workspace(L, dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
+    def step():
         mr.planes(ids, cu, synth.IMAGE_ID, out=planes, start=start, amount=amount, origin=origin,
                   seq_flags=flags, workspace=ws)
-        if ev is not None:
-            ev[0].record(stream)
         mr.apply(q, k, planes)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -157,52 +164,44 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronised on both sides
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    step_s = timed(step, args.steps)
     wall = time.perf_counter() - w0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    apply_ms = [a.elapsed_time(bb) for a, bb in evs]
-    apply_mean_s = sum(apply_ms) / len(apply_ms) / 1e3
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us/step), "
-        f"mrope_apply {apply_mean_s * 1e6:.1f} us/launch")
+    ms_step = step_s * 1e3
 
-    # planes kernel alone (context, not the roofline)
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    p0.record(stream)
-    for _ in range(args.steps):
-        mr.planes(ids, cu, synth.IMAGE_ID, out=planes, start=start, amount=amount, origin=origin,
-                  seq_flags=flags, workspace=ws)
-    p1.record(stream)
-    torch.cuda.synchronize()
-    planes_us = p0.elapsed_time(p1) / args.steps * 1e3
+    # the dominant kernel alone, `steps` back-to-back launches on the same stream (HIP events)
+    apply_mean_s = timed(lambda: mr.apply(q, k, planes), args.steps)
+    planes_us = timed(lambda: mr.planes(ids, cu, synth.IMAGE_ID, out=planes, start=start, amount=amount,
+                                        origin=origin, seq_flags=flags, workspace=ws), args.steps) * 1e6
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us/step); "
+        f"mrope_apply {apply_mean_s * 1e6:.1f} us, mrope_planes {planes_us:.1f} us per launch")
+
+    cold = None
+    if args.cold:
+        # one launch after streaming 1 GiB through the caches (read only, so no dirty lines are left
+        # to write back): the HBM-only figure, without hits in the 256 MB memory-side cache
+        sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        ts = []
+        for _ in range(10):
+            sweep.sum()
+            torch.cuda.synchronize()
+            ts.append(timed(lambda: mr.apply(q, k, planes), 1))
+        cold = sorted(ts)[len(ts) // 2]
+        del sweep
 
     # plain device-to-device copy of 1 GiB: the practical streaming ceiling on this machine (context)
     src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 2 * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    copy_gbs = 2 * src.numel() * 2 / timed(lambda: dst.copy_(src), 10) / 1e9
     del src, dst
 
     ab = algorithmic_bytes_apply(L)
     achieved = ab / apply_mean_s / 1e9
     out = {
         "metric": METRIC,
-        "value": L * args.steps / (total_ms / 1e3),
+        "value": L / step_s,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -226,6 +225,9 @@ def main():
         "planes_gbs": algorithmic_bytes_planes(L) / (planes_us / 1e6) / 1e9,
         "copy_ceiling_gbs": copy_gbs,
     }
+    if cold is not None:
+        out["apply_cold"] = {"us": cold * 1e6, "gbs": ab / cold / 1e9,
+                             "note": "median single launch after a 1 GiB read sweep (no memory-side cache hits)"}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(b, qn, kn, min_seconds=args.cpu_seconds)

@@ -8,10 +8,10 @@
 //   Core AI", section "The canvas rule and why the gate is on the planes".
 //
 // Kernels
-//   planes_kernel     ids -> first marker per sequence (ballot + wait-free decoupled look-back) -> planes,
-//                     start, amount
+//   planes_kernel     ids -> first marker per sequence (ballot + decoupled look-back over 512-token
+//                     chunks) -> planes, start, amount
 //   apply_kernel      planes -> cos/sin on the fly -> rotate-half of Q and K (the HBM stream)
-//   apply_ids_kernel  the two above in one launch; planes stay in LDS
+//   apply_ids_kernel  the two above in one launch; a chunk's planes stay in LDS
 //   decode_kernel     one token per sequence: Q in place, K rotated and scattered to a paged cache
 //
 // Thread layout of the rotary kernels: eight lanes per token; lane pair m holds frequencies
@@ -115,68 +115,124 @@ __device__ __forceinline__ int32_t wave_min(int32_t v)
     return v;
 }
 
-// Largest s in [0, n_seqs] with cu[s] <= g (n_seqs when g is past the last sequence), -1 if none.
-__device__ __forceinline__ int32_t seq_of(const int32_t *cu, int32_t n_seqs, int64_t g)
+// Number of entries of the non-decreasing array cu[0..n] that are <= key, by a 64-ary search of the
+// whole wave: one coalesced load and a ballot per level (two levels up to 4,096 sequences).
+__device__ int32_t wave_count_le(const int32_t *cu, int32_t n, int64_t key, int lane)
 {
-    int32_t lo = 0, hi = n_seqs + 1;
-    while (lo < hi) {
-        const int32_t mid = (lo + hi) >> 1;
-        if ((int64_t)cu[mid] <= g)
-            lo = mid + 1;
-        else
-            hi = mid;
+    int32_t lo = 0, hi = n + 1;  // the count lies in [lo, hi]
+    while (true) {
+        const int32_t stride = (hi - lo + 63) / 64;
+        const int32_t pos = lo + lane * stride;
+        const int c = __builtin_popcountll(__ballot(pos < hi && (int64_t)cu[pos] <= key));
+        if (stride <= 1 || c == 0) return lo + c;
+        const int32_t nhi = lo + c * stride;
+        lo = lo + (c - 1) * stride + 1;
+        hi = min(hi, nhi);
+        if (lo >= hi) return lo;
     }
-    return lo - 1;
+}
+
+// Bits [lo, hi) of a 64-bit word, for any lo, hi (clamped to [0, 64]).
+__device__ __forceinline__ uint64_t bit_range(int lo, int hi)
+{
+    lo = max(0, min(lo, 64));
+    hi = max(0, min(hi, 64));
+    if (hi <= lo) return 0;
+    const uint64_t upto_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1);
+    const uint64_t below_lo = (1ull << lo) - 1;  // lo < 64 here
+    return upto_hi & ~below_lo;
+}
+
+// ------------------------------------------------------------------ the plane scan -------------
+// A chunk of kChunk tokens is scanned by one wave: kSub coalesced loads of 64 ids, one ballot each,
+// give the marker bitmask of the chunk.  Sequences come from a window of up to 64 cu_seqlens entries
+// (one coalesced load; more windows when more than 64 sequences touch the chunk), and a token finds
+// its sequence by a 6-step shuffle search of the window.  The first marker of a sequence that began
+// in an earlier chunk comes from the decoupled look-back below.
+constexpr int kChunk = 512;
+constexpr int kSub = kChunk / 64;
+
+struct ChunkMasks {
+    uint64_t m[kSub];  // bit i of m[k]: token c0 + 64k + i is a marker
+};
+
+// First marker (global index, kNone if none) among chunk positions [a, b), and whether there are two.
+__device__ __forceinline__ void first_in(const ChunkMasks &cm, int64_t c0, int a, int b, int32_t &first, bool &multi)
+{
+    first = kNone;
+    int cnt = 0;
+#pragma unroll
+    for (int k = kSub - 1; k >= 0; --k) {
+        const uint64_t m = cm.m[k] & bit_range(a - 64 * k, b - 64 * k);
+        if (m) first = (int32_t)(c0 + 64 * k + __builtin_ctzll(m));
+        cnt += __builtin_popcountll(m);
+    }
+    multi = cnt >= 2;
+}
+
+__device__ __forceinline__ void load_masks(const Scan &sc, int64_t c0, int64_t c_end, int64_t from, int lane, ChunkMasks &cm)
+{
+    int32_t v[kSub];
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+        const int64_t g = c0 + 64 * k + lane;
+        v[k] = (g < c_end && g >= from) ? sc.ids[g] : ~sc.marker;
+    }
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) cm.m[k] = __ballot(v[k] == sc.marker);
 }
 
 // Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan with Decoupled
-// Look-back", 2016) with a (first marker, more-than-one) operator, made wait-free: a tile never
-// waits for a predecessor.  The wave reads the status words of the 64 preceding tiles at once and
-// combines everything up to the nearest inclusive value -- a predecessor's published inclusive word,
-// or the tile where the sequence begins.  A predecessor that has not published yet (any status word
-// without this launch's epoch) is evaluated on the spot from its 64 ids (one coalesced load and a
-// ballot), so the result never depends on which workgroups the hardware has scheduled.
-// Returns the first marker (global index) of the sequence over [s0_begin, tile*64) and whether that
-// range holds more than one marker.
-__device__ void lookback(const Scan &sc, const uint64_t *status, int64_t tile, uint32_t ep, int lane,
+// Look-back", 2016) over chunk status words with a (first marker, more-than-one) operator.  The wave
+// reads the words of the 64 preceding chunks at once and combines everything up to the nearest
+// inclusive value -- a predecessor's published inclusive word, or the chunk where the sequence
+// begins.  A predecessor that has not published yet is polled a bounded number of times and then
+// evaluated on the spot from its ids, so no wait is unbounded and the result never depends on which
+// workgroups the hardware has scheduled.  Returns the first marker (global index) of the sequence over
+// [s0_begin, chunk*kChunk) and whether that range holds more than one marker.
+constexpr int kPolls = 32;
+
+__device__ void lookback(const Scan &sc, const uint64_t *status, int64_t chunk, uint32_t ep, int lane,
                          int64_t s0_begin, int32_t &first, bool &multi)
 {
     first = kNone;
     multi = false;
-    const int64_t stop = s0_begin / kTile;
-    int64_t base = tile - 1;
+    const int64_t stop = max<int64_t>(s0_begin, 0) / kChunk;  // the walk always ends at or above chunk 0
+    int64_t base = chunk - 1;
     while (true) {
         const int64_t idx = base - lane;
         const bool valid = idx >= stop;
-        const uint64_t w = valid ? aload(status + idx) : 0ull;
-        const uint64_t flag = (w >> 32) & 3u;
-        const bool ready = valid && (uint32_t)(w >> 34) == ep && flag != 0;
-        const uint64_t end_mask = __ballot(valid && ((ready && flag == kIncl) || idx == stop));
-        const int lim = end_mask ? __builtin_ctzll(end_mask) : 63;
+        uint64_t w = 0;
+        bool ready = false;
+        uint64_t end_mask = 0;
+        int lim = 63;
+        for (int poll = 0;; ++poll) {
+            if (valid && !ready) {
+                w = aload(status + idx);
+                ready = (uint32_t)(w >> 34) == ep && ((w >> 32) & 3u) != 0;
+            }
+            end_mask = __ballot(valid && ((ready && ((w >> 32) & 3u) == kIncl) || idx == stop));
+            lim = end_mask ? __builtin_ctzll(end_mask) : 63;
+            const bool missing = __ballot(valid && lane <= lim && !ready) != 0;
+            if (!missing || poll == kPolls) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
         const bool use = valid && lane <= lim;
         int32_t v = (use && ready) ? (int32_t)(w & 0x7fffffffu) : kNone;
         bool m = use && ready && ((w >> 31) & 1u);
         uint64_t todo = __ballot(use && !ready);
-        while (todo) {  // up to four unpublished tiles per round trip
-            int bsel[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                bsel[k] = todo ? __builtin_ctzll(todo) : -1;
-                todo &= todo - 1;
-            }
-            bool hit[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int64_t gg = (base - bsel[k]) * kTile + lane;
-                hit[k] = bsel[k] >= 0 && gg >= s0_begin && gg < sc.n_tokens && sc.ids[gg] == sc.marker;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t hm = __ballot(hit[k]);
-                if (bsel[k] >= 0 && lane == bsel[k]) {
-                    v = hm ? (int32_t)((base - bsel[k]) * kTile + __builtin_ctzll(hm)) : kNone;
-                    m = __builtin_popcountll(hm) >= 2;
-                }
+        while (todo) {  // chunks still unpublished after the polls: read their ids
+            const int bsel = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int64_t cb = (base - bsel) * kChunk;
+            ChunkMasks cm;
+            load_masks(sc, cb, min<int64_t>(cb + kChunk, sc.n_tokens), s0_begin, lane, cm);
+            int32_t f;
+            bool mm;
+            first_in(cm, cb, 0, kChunk, f, mm);
+            if (lane == bsel) {
+                v = f;
+                m = mm;
             }
         }
         const uint64_t has = __ballot(use && v != kNone);
@@ -189,12 +245,6 @@ __device__ void lookback(const Scan &sc, const uint64_t *status, int64_t tile, u
     }
 }
 
-struct TokenPos {
-    int32_t p;      // position in its sequence
-    int32_t o;      // in-sequence index of the first marker at or before p, kNone if none
-    bool valid;     // the token belongs to a sequence
-};
-
 __device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t origin, bool multi, int64_t len)
 {
     const bool img = origin >= 0;
@@ -204,72 +254,79 @@ __device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t
     if (sc.flags) sc.flags[s] = (multi ? 1 : 0) | ((img && (int64_t)origin + kFrameLen > len) ? 2 : 0);
 }
 
-// Scan of one 64-token tile by one full wave, lane i <-> token tile*64 + i.  Publishes the tile's
-// status word, looks back when the tile's first sequence began earlier, writes the scalars of every
-// sequence that ends in the tile, and returns each lane's position and canvas origin.
-__device__ TokenPos scan_tile(const Scan &sc, uint64_t *status, int64_t tile, uint32_t ep, int lane)
+// Scan of one chunk by one full wave.  Publishes the chunk's status word, looks back when the
+// chunk's first sequence began earlier, writes the scalars of every sequence whose last token (for
+// an empty sequence: the token before it) lies in the chunk, and hands each token's planes to
+// sink(k, ok, t, h, w) for token chunk*kChunk + 64k + lane.
+template <class Sink>
+__device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint32_t ep, int lane, Sink sink)
 {
-    const int64_t t0 = tile * kTile;
-    const int64_t g = t0 + lane;
-    const bool in_range = g < sc.n_tokens;
-    const int32_t s = in_range ? seq_of(sc.cu, sc.n_seqs, g) : -1;
-    const bool in_seq = in_range && s >= 0 && s < sc.n_seqs;
-    int64_t sb = 0, se = 0;
-    if (in_seq) {
-        sb = sc.cu[s];
-        se = sc.cu[s + 1];
-    }
-    const bool is_marker = in_seq && sc.ids[g] == sc.marker;
-    const uint64_t mk = __ballot(is_marker);
+    const int64_t c0 = chunk * kChunk;
+    const int64_t c_end = min<int64_t>(c0 + kChunk, sc.n_tokens);
+    const int32_t n = sc.n_seqs;
 
-    // lanes of this token's sequence inside the tile: [lo, hi), always containing the lane itself
-    int lo = lane, hi = lane + 1;
-    if (in_seq) {
-        lo = (int)max<int64_t>(0, min<int64_t>(sb - t0, lane));
-        hi = (int)min<int64_t>(kTile, max<int64_t>(se - t0, lane + 1));
-    }
-    const uint64_t seg = (hi >= 64 ? ~0ull : ((1ull << hi) - 1)) & ~((1ull << lo) - 1);
-    const uint64_t m = mk & seg;
-    int32_t first = m ? (int32_t)(t0 + __builtin_ctzll(m)) : kNone;
-    bool multi = __builtin_popcountll(m) >= 2;
+    ChunkMasks cm;
+    load_masks(sc, c0, c_end, c0, lane, cm);
+    const int32_t s_first = wave_count_le(sc.cu, n, c0, lane) - 1;
+    const int32_t s_last = wave_count_le(sc.cu, n, c_end - 1, lane) - 1;
+    const bool first_ok = s_first >= 0 && s_first < n;
+    const int64_t s0_begin = first_ok ? sc.cu[s_first] : c0;
+    const bool need_carry = first_ok && s0_begin < c0;
+    const bool last_ok = s_last >= 0 && s_last < n;
+    const int64_t sl_begin = last_ok ? sc.cu[s_last] : c_end;
+    const bool last_open = need_carry && s_last == s_first;
 
-    const int last = (int)min<int64_t>(kTile - 1, sc.n_tokens - 1 - t0);
-    const int32_t first_last = __shfl(first, last);
-    const bool multi_last = __shfl((int)multi, last) != 0;
-    const int32_t s_last = __shfl(s, last);
-    const int32_t s0 = __shfl(s, 0);
-    const int64_t s0_begin = __shfl(sb, 0);
-    const bool need_carry = __shfl((int)(in_seq && sb < t0), 0) != 0;
-    const bool last_open = need_carry && s_last == s0;  // the tile's last sequence began before it
+    // the chunk's last sequence: its part in this chunk, published before the look-back
+    int32_t f_last;
+    bool m_last;
+    first_in(cm, c0, (int)(max(sl_begin, c0) - c0), (int)(c_end - c0), f_last, m_last);
+    if (lane == 0) astore(status + chunk, status_word(ep, last_open ? kAgg : kIncl, m_last, last_ok ? f_last : kNone));
 
-    if (lane == 0) astore(status + tile, status_word(ep, last_open ? kAgg : kIncl, multi_last, first_last));
-
+    int32_t carry = kNone;
+    bool carry_multi = false;
     if (need_carry) {
-        int32_t cf;
-        bool cm;
-        lookback(sc, status, tile, ep, lane, s0_begin, cf, cm);
+        lookback(sc, status, chunk, ep, lane, s0_begin, carry, carry_multi);
         if (last_open && lane == 0) {
-            const bool mm = cm || multi_last || (cf != kNone && first_last != kNone);
-            astore(status + tile, status_word(ep, kIncl, mm, min(cf, first_last)));
-        }
-        if (in_seq && s == s0) {
-            multi = multi || cm || (cf != kNone && first != kNone);
-            first = min(first, cf);
+            const bool mm = carry_multi || m_last || (carry != kNone && f_last != kNone);
+            astore(status + chunk, status_word(ep, kIncl, mm, min(carry, f_last)));
         }
     }
 
-    TokenPos r;
-    r.valid = in_seq;
-    r.p = (int32_t)(g - sb);
-    r.o = (in_seq && first != kNone && first <= g) ? (int32_t)(first - sb) : kNone;
-
-    if (in_seq && g == se - 1) {
-        write_scalars(sc, s, first == kNone ? -1 : (int32_t)(first - sb), multi, se - sb);
-        for (int32_t s2 = s + 1; s2 < sc.n_seqs && sc.cu[s2 + 1] == sc.cu[s2]; ++s2) write_scalars(sc, s2, -1, false, 0);
+    // windows of 64 sequences; chunk 0 starts at sequence 0 so leading empty sequences get scalars
+    int32_t win = c0 == 0 ? 0 : max(s_first, 0);
+    while (true) {
+        const int32_t j = win + lane;
+        const int64_t W = j <= n ? (int64_t)sc.cu[min(j, n)] : INT64_MAX;
+        const int64_t Wn = j < n ? (int64_t)sc.cu[j + 1] : INT64_MAX;
+        int32_t f;
+        bool mm;
+        first_in(cm, c0, (int)(max(min(W, c_end), c0) - c0), (int)(max(min(Wn, c_end), c0) - c0), f, mm);
+        if (need_carry && j == s_first) {
+            mm = mm || carry_multi || (carry != kNone && f != kNone);
+            f = min(f, carry);
+        }
+        if (j < n) {
+            const int64_t fin = max<int64_t>(Wn - 1, 0);
+            if (fin >= c0 && fin < c_end) write_scalars(sc, j, f == kNone ? -1 : (int32_t)(f - W), mm, Wn - W);
+        }
+        const int64_t w_lo = __shfl(W, 0), w_hi = __shfl(Wn, 63);
+#pragma unroll
+        for (int k = 0; k < kSub; ++k) {
+            const int64_t g = c0 + 64 * k + lane;
+            int r = 0;
+#pragma unroll
+            for (int step = 32; step > 0; step >>= 1)
+                if (__shfl(Wn, r + step - 1) <= g) r += step;
+            const int32_t fr = __shfl(f, r);
+            const int64_t sb = __shfl(W, r);
+            const bool ok = g < c_end && g >= w_lo && g < w_hi;
+            int32_t t = 0, h = 0, w = 0;
+            if (ok) canvas_planes((int32_t)(g - sb), (fr != kNone && fr <= g) ? (int32_t)(fr - sb) : kNone, t, h, w);
+            sink(k, ok, t, h, w);
+        }
+        if (win + 64 >= n || (int64_t)sc.cu[win + 64] > c_end) break;
+        win += 64;
     }
-    if (in_seq && g == 0)
-        for (int32_t s2 = 0; s2 < s; ++s2) write_scalars(sc, s2, -1, false, 0);
-    return r;
 }
 
 // ------------------------------------------------------------------ element I/O ----------------
@@ -527,75 +584,92 @@ __global__ __launch_bounds__(kBlock) void apply_any_kernel(Heads hd, Rotary rot,
     rotate_token_any<BF16>(hd, g, e0, l, c, ss);
 }
 
-// One wave per 64-token tile, four tiles per workgroup.
-__global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_tiles)
+// One wave per chunk, four chunks per workgroup.
+__global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunks)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t tile = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-    if (tile >= n_tiles) return;
-    const TokenPos r = scan_tile(sc, status_array(sc.workspace), tile, launch_epoch(sc), lane);
-    if (r.valid) {
-        int32_t t, h, w;
-        canvas_planes(r.p, r.o, t, h, w);
-        const int64_t g = tile * kTile + lane;
-        sc.planes[g] = t;
-        sc.planes[sc.plane_stride + g] = h;
-        sc.planes[2 * sc.plane_stride + g] = w;
-    }
+    const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    if (chunk >= n_chunks) return;
+    const int64_t c0 = chunk * kChunk;
+    scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane,
+               [&](int k, bool ok, int32_t t, int32_t h, int32_t w) {
+                   if (!ok) return;
+                   const int64_t g = c0 + 64 * k + lane;
+                   sc.planes[g] = t;
+                   sc.planes[sc.plane_stride + g] = h;
+                   sc.planes[2 * sc.plane_stride + g] = w;
+               });
 }
 
-// One 64-token tile per workgroup of 512 threads (eight lanes per token); wave 0 scans the tile.
-constexpr int kIdsBlock = kTile * kLanesPerTok;
-
+// Fused: one chunk per workgroup.  Every lane issues the Q/K loads of its first token, wave 0 scans
+// the chunk into LDS meanwhile, then the workgroup rotates the chunk 32 tokens at a time, each
+// 8-lane group prefetching its next token before rotating the current one.
 template <bool BF16, int NQ, int NK>
-__global__ __launch_bounds__(kIdsBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc)
+__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc)
 {
-    __shared__ int32_t s_pl[3][kTile];
-    __shared__ int32_t s_ok[kTile];
+    __shared__ int32_t s_pl[3][kChunk];
+    __shared__ uint64_t s_ok[kSub];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int l = tid & 7, m = l >> 1, half = l & 1;
     const int e0 = 32 * half + 8 * m;
-    const int64_t tile = blockIdx.x;
-    const int tl = tid >> 3;
-    const int64_t g = tile * kTile + tl;
-    const bool tok_ok = g < hd.n_tokens;
-
-    // Q/K loads go out before the scan so the look-back hides behind them.
+    const int64_t chunk = blockIdx.x;
+    const int64_t c0 = chunk * kChunk;
+    const int64_t c_end = min<int64_t>(c0 + kChunk, hd.n_tokens);
     constexpr bool kFixed = NQ > 0 && NK > 0;
     constexpr int AQ = kFixed ? NQ : 1, AK = kFixed ? NK : 1;
+
+    int64_t g = c0 + (tid >> 3);
     Raw8<BF16> qv[AQ], kv[AK];
     if constexpr (kFixed) {
-        if (tok_ok) load_token_fixed<BF16, AQ, AK>(hd, g, e0, qv, kv);
+        if (g < c_end) load_token_fixed<BF16, AQ, AK>(hd, g, e0, qv, kv);
     }
 
     if (tid < 64) {
-        int32_t t = 0, h = 0, w = 0;
-        const TokenPos r = scan_tile(sc, status_array(sc.workspace), tile, launch_epoch(sc), lane);
-        const bool ok = r.valid;
-        if (ok) {
-            canvas_planes(r.p, r.o, t, h, w);
-            if (sc.planes) {
-                const int64_t gg = tile * kTile + lane;
-                sc.planes[gg] = t;
-                sc.planes[sc.plane_stride + gg] = h;
-                sc.planes[2 * sc.plane_stride + gg] = w;
-            }
-        }
-        s_pl[0][lane] = t;
-        s_pl[1][lane] = h;
-        s_pl[2][lane] = w;
-        s_ok[lane] = ok;
+        if (lane < kSub) s_ok[lane] = 0;
+        // a token is handed over once, in the sequence window that holds it
+        scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane,
+                   [&](int k, bool ok, int32_t t, int32_t h, int32_t w) {
+                       const int p = 64 * k + lane;
+                       const uint64_t okm = __ballot(ok);
+                       if (lane == 0) s_ok[k] |= okm;
+                       if (!ok) return;
+                       s_pl[0][p] = t;
+                       s_pl[1][p] = h;
+                       s_pl[2][p] = w;
+                       if (sc.planes) {
+                           const int64_t gg = c0 + p;
+                           sc.planes[gg] = t;
+                           sc.planes[sc.plane_stride + gg] = h;
+                           sc.planes[2 * sc.plane_stride + gg] = w;
+                       }
+                   });
     }
     __syncthreads();
 
-    if (!tok_ok || !s_ok[tl]) return;   // the eight lanes of a token leave together
-    double c[8], ss[8];
-    pair_sincos(rot, m, half, s_pl[0][tl], s_pl[1][tl], s_pl[2][tl], c, ss);
-    if constexpr (kFixed) {
-        rotate_token_fixed<BF16, AQ, AK>(hd, g, e0, l, c, ss, qv, kv);
-    } else {
-        rotate_token_any<BF16>(hd, g, e0, l, c, ss);
+    while (g < c_end) {  // the eight lanes of a token stay together
+        const int p = (int)(g - c0);
+        const bool ok = (s_ok[p >> 6] >> (p & 63)) & 1u;
+        const int64_t gn = g + kTokPerBlock;
+        double c[8], ss[8];
+        if constexpr (kFixed) {
+            Raw8<BF16> qn[AQ], kn[AK];
+            if (gn < c_end) load_token_fixed<BF16, AQ, AK>(hd, gn, e0, qn, kn);
+            if (ok) {
+                pair_sincos(rot, m, half, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
+                rotate_token_fixed<BF16, AQ, AK>(hd, g, e0, l, c, ss, qv, kv);
+            }
+#pragma unroll
+            for (int h = 0; h < AQ; ++h) qv[h] = qn[h];
+#pragma unroll
+            for (int h = 0; h < AK; ++h) kv[h] = kn[h];
+        } else {
+            if (ok) {
+                pair_sincos(rot, m, half, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
+                rotate_token_any<BF16>(hd, g, e0, l, c, ss);
+            }
+        }
+        g = gn;
     }
 }
 
@@ -681,9 +755,9 @@ static hipError_t bump_if_device_epoch(const Scan &s, hipStream_t stream)
 
 hipError_t launch_planes(const Scan &s, hipStream_t stream)
 {
-    const int64_t n_tiles = (s.n_tokens + kTile - 1) / kTile;
-    const unsigned blocks = (unsigned)((n_tiles + kBlock / 64 - 1) / (kBlock / 64));
-    planes_kernel<<<blocks, kBlock, 0, stream>>>(s, n_tiles);
+    const int64_t n_chunks = (s.n_tokens + kChunk - 1) / kChunk;
+    const unsigned blocks = (unsigned)((n_chunks + kBlock / 64 - 1) / (kBlock / 64));
+    planes_kernel<<<blocks, kBlock, 0, stream>>>(s, n_chunks);
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : bump_if_device_epoch(s, stream);
 }
@@ -725,11 +799,11 @@ hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, 
 template <bool BF16>
 static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, hipStream_t st)
 {
-    const unsigned n_tiles = (unsigned)((h.n_tokens + kTile - 1) / kTile);
+    const unsigned n_chunks = (unsigned)((h.n_tokens + kChunk - 1) / kChunk);
     if (h.nq == 8 && h.nk == 2)
-        apply_ids_kernel<BF16, 8, 2><<<n_tiles, kIdsBlock, 0, st>>>(h, r, s);
+        apply_ids_kernel<BF16, 8, 2><<<n_chunks, kBlock, 0, st>>>(h, r, s);
     else
-        apply_ids_kernel<BF16, 0, 0><<<n_tiles, kIdsBlock, 0, st>>>(h, r, s);
+        apply_ids_kernel<BF16, 0, 0><<<n_chunks, kBlock, 0, st>>>(h, r, s);
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : bump_if_device_epoch(s, st);
 }

@@ -123,7 +123,39 @@ def test_many_tiny_sequences_and_empties():
     cu[1:] = np.cumsum(lens)
     b = synth.Prefill("tiny", ids, cu, [None] * lens.size, "bf16", seed=7)
     pl, st, am, og, fl = mr.planes(i32(ids), i32(cu), MARKER)
-    _check_scan(b, pl, st, am, og, fl, "tiny")
+    epl, *_ = _check_scan(b, pl, st, am, og, fl, "tiny")
+    # fused: hundreds of sequences per 512-token chunk (several sequence windows per chunk)
+    qn, kn = b.qk()
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    pl2 = torch.full_like(pl, -7)
+    st2, am2, og2, fl2, _ = mr.apply_ids(q, k, i32(ids), i32(cu), MARKER, planes_out=pl2)
+    _check_scan(b, pl2, st2, am2, og2, fl2, "tiny fused")
+    compare_heads(host_heads(q), qn, epl, "bf16", what="tiny fused q")
+    compare_heads(host_heads(k), kn, epl, "bf16", what="tiny fused k")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_chunk_boundaries(fused):
+    """Sequences and frames on and across the 512-token chunk edges: markers at the first and last
+    token of a chunk, frames straddling two and three chunks, lengths 511/512/513, empties."""
+    lens = [512, 512, 1, 511, 513, 1024, 0, 0, 512, 600, 1700, 3]
+    placed = [0, 511, 0, 444, 0, 500, None, None, None, 510, 1023, None]
+    g = synth.rng(13, 4)
+    ids = np.concatenate([synth.prompt_ids(g, n, o) for n, o in zip(lens, placed) if n > 0])
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    b = synth.Prefill("edges", ids, cu, placed, "bf16", seed=13)
+    qn, kn = b.qk()
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    if fused:
+        pl = torch.full((3, b.n_tokens), -7, dtype=torch.int32, device="cuda")
+        st, am, og, fl, _ = mr.apply_ids(q, k, i32(ids), i32(cu), MARKER, planes_out=pl)
+    else:
+        pl, st, am, og, fl = mr.planes(i32(ids), i32(cu), MARKER)
+        mr.apply(q, k, pl)
+    epl, *_ = _check_scan(b, pl, st, am, og, fl, f"edges fused={fused}")
+    compare_heads(host_heads(q), qn, epl, "bf16", what="edges q")
+    compare_heads(host_heads(k), kn, epl, "bf16", what="edges k")
 
 
 def test_zero_tokens_text_scalars():
