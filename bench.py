@@ -54,6 +54,93 @@ def algorithmic_bytes_planes(tokens: int) -> int:
     return tokens * 16
 
 
+def algorithmic_bytes_fused(tokens: int, heads: int = 10, rot_dim: int = 64, elem: int = 2) -> int:
+    """mrope_apply_ids in place: ids read (4 B) and the rotated dims read and written, per token."""
+    return tokens * (heads * rot_dim * elem * 2 + 4)
+
+
+def graph_timed(fn, reps, warm=2):
+    """Mean GPU time per call of `reps` calls captured in one HIP graph and replayed (no host launch
+    overhead: for kernels shorter than the binding's per-call host time)."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(warm):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps / 1e3
+
+
+def extras(args, dev, timed):
+    """Other workloads of the method, one timing each (context; not the headline).  Kernels shorter
+    than the host's per-call launch time are also timed from a replayed HIP graph."""
+    import numpy as np
+    import torch
+
+    import canvas_rope_rotary_amd as mr
+    from canvas_rope_rotary_amd import synth
+
+    out = {}
+
+    def heads(x, dt):
+        if dt == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    for cfg in (synth.config3(), synth.config5(), synth.config1()):
+        log(f"extras: {cfg.name}")
+        qn, kn = cfg.qk()
+        q, k = heads(qn, cfg.dtype), heads(kn, cfg.dtype)
+        ids = torch.from_numpy(cfg.ids).to(dev)
+        cu = torch.from_numpy(cfg.cu_seqlens).to(dev)
+        ws = mr.Workspace(cfg.n_tokens, dev)
+        pl = torch.empty((3, cfg.n_tokens), dtype=torch.int32, device=dev)
+        elem = 2 if cfg.dtype == "bf16" else 4
+        f_us = timed(lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, workspace=ws), args.steps) * 1e6
+        p_us = timed(lambda: mr.planes(ids, cu, synth.IMAGE_ID, out=pl, workspace=ws), args.steps) * 1e6
+        a_us = timed(lambda: mr.apply(q, k, pl), args.steps) * 1e6
+        small = cfg.n_tokens < 65536
+        if small:  # launch-bound: GPU time from a graph (scans then use the device epoch counter)
+            f_us = graph_timed(lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, workspace=ws), args.steps) * 1e6
+            p_us = graph_timed(lambda: mr.planes(ids, cu, synth.IMAGE_ID, out=pl, workspace=ws), args.steps) * 1e6
+            a_us = graph_timed(lambda: mr.apply(q, k, pl), args.steps) * 1e6
+        out[cfg.name] = {"tokens": cfg.n_tokens, "fused_us": f_us, "planes_us": p_us, "apply_us": a_us,
+                         "timing": "hip graph replay" if small else "hip events, back-to-back launches",
+                         "fused_gbs": algorithmic_bytes_fused(cfg.n_tokens, elem=elem) / f_us / 1e3,
+                         "apply_gbs": algorithmic_bytes_apply(cfg.n_tokens, elem=elem) / a_us / 1e3,
+                         "tokens_per_s_fused": cfg.n_tokens / (f_us / 1e6)}
+        del q, k, pl
+        torch.cuda.empty_cache()
+    d = synth.config4()
+    log(f"extras: {d.name}")
+    qn, kn = d.qk()
+    q, k = heads(qn, "bf16"), heads(kn, "bf16")
+    cache = torch.zeros((d.num_blocks, d.block_size, d.n_k_heads, d.head_dim), dtype=torch.bfloat16, device=dev)
+    pos, amount = torch.from_numpy(d.pos).to(dev), torch.from_numpy(d.amount).to(dev)
+    slots = torch.from_numpy(d.slot_mapping).to(dev)
+    d_us = graph_timed(lambda: mr.decode(q, k, pos, amount, cache, slots), args.steps) * 1e6
+    dbytes = d.n_seqs * (8 * 64 * 2 * 2 + 2 * 256 * 2 * 2 + 4 + 4 + 8)
+    out[d.name] = {"seqs": d.n_seqs, "decode_us": d_us, "tokens_per_s": d.n_seqs / (d_us / 1e6),
+                   "gbs": dbytes / d_us / 1e3, "timing": "hip graph replay"}
+    del q, k, cache
+    torch.cuda.empty_cache()
+    return out
+
+
 def traffic_from_counters(launch_tokens: int):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, scaled by the
     copy-kernel calibration -- only if it was taken on the current kernel sources."""
@@ -99,6 +186,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cold", action="store_true", help="also time mrope_apply after a cache-clearing read sweep")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time the other workloads: 8 x 32768 fused, 1M-token ragged, decode, L=110 fp32")
     ap.add_argument("--mode", choices=("bench", "copy"), default="bench",
                     help="copy: only a plain 1 GiB device copy, repeated (calibrates rocprofv3 HBM counters)")
     args = ap.parse_args()
@@ -190,6 +279,10 @@ def main():
         cold = sorted(ts)[len(ts) // 2]
         del sweep
 
+    # the fused one-launch variant on the same batch (context)
+    fused_us = timed(lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, planes_out=None, start=start, amount=amount,
+                                          origin=origin, seq_flags=flags, workspace=ws), args.steps) * 1e6
+
     # plain device-to-device copy of 1 GiB: the practical streaming ceiling on this machine (context)
     src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
     dst = torch.empty_like(src)
@@ -221,13 +314,16 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(L),
                      "kernel": "mrope_apply", "algorithmic_bytes_per_launch": ab,
                      "mean_launch_us": apply_mean_s * 1e6},
-        "kernels_us": {"mrope_planes": planes_us, "mrope_apply": apply_mean_s * 1e6},
+        "kernels_us": {"mrope_planes": planes_us, "mrope_apply": apply_mean_s * 1e6, "mrope_apply_ids": fused_us},
+        "fused_gbs": algorithmic_bytes_fused(L) / (fused_us / 1e6) / 1e9,
         "planes_gbs": algorithmic_bytes_planes(L) / (planes_us / 1e6) / 1e9,
         "copy_ceiling_gbs": copy_gbs,
     }
     if cold is not None:
         out["apply_cold"] = {"us": cold * 1e6, "gbs": ab / cold / 1e9,
                              "note": "median single launch after a 1 GiB read sweep (no memory-side cache hits)"}
+    if args.extras:
+        out["extras"] = extras(args, dev, timed)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(b, qn, kn, min_seconds=args.cpu_seconds)

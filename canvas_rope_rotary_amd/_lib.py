@@ -85,6 +85,26 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+class _on_device:
+    """Make `device` current for the call, skipping the switch when it already is."""
+
+    __slots__ = ("dev", "prev")
+
+    def __init__(self, dev):
+        self.dev = dev
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if self.dev.index is not None and self.dev.index != cur:
+            self.prev = cur
+            torch.cuda.set_device(self.dev)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return MROPE_BF16
@@ -192,7 +212,7 @@ def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078,
     start, amount, origin, seq_flags = (mk(start, "start"), mk(amount, "amount"), mk(origin, "origin"),
                                         mk(seq_flags, "seq_flags"))
     ws = _workspace(workspace, L, dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), _ptr(out), out.stride(0),
                                    _ptr(start), _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr,
                                    ws.capacity, ws.next_epoch(), _stream(dev)))
@@ -227,7 +247,7 @@ def apply(q: torch.Tensor, k: torch.Tensor | None, planes_: torch.Tensor, theta:
     if planes_.dtype != torch.int32 or planes_.dim() != 2 or planes_.shape[0] != 3 or planes_.shape[1] < T \
             or planes_.stride(1) != 1:
         raise ValueError("planes must be an int32 [3, >= tokens] tensor with unit column stride")
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         _check(load().mrope_apply(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, _ptr(planes_),
                                   planes_.stride(0), float(theta), _ptr(q_out), _ptr(k_out), _stream(dev)))
     return (q_out if q_out is not None else q), (k_out if k_out is not None else k)
@@ -255,7 +275,7 @@ def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seq
     start, amount, origin, seq_flags = (mk(start, "start"), mk(amount, "amount"), mk(origin, "origin"),
                                         mk(seq_flags, "seq_flags"))
     ws = _workspace(workspace, T, dev)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         _check(load().mrope_apply_ids(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, float(theta),
                                       _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
                                       _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
@@ -287,7 +307,7 @@ def decode(q: torch.Tensor, k: torch.Tensor | None, pos: torch.Tensor, amount: t
         cb, ct, ch = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
     else:
         nb, bs, cb, ct, ch = 0, 1, 0, 0, 0
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         _check(load().mrope_decode(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, S, _ptr(pos), _ptr(amount),
                                    _ptr(k_cache), _ptr(slot_mapping), bs, nb, cb, ct, ch, D, rot_dim, dt,
                                    float(theta), _stream(dev)))

@@ -115,21 +115,47 @@ __device__ __forceinline__ int32_t wave_min(int32_t v)
     return v;
 }
 
-// Number of entries of the non-decreasing array cu[0..n] that are <= key, by a 64-ary search of the
-// whole wave: one coalesced load and a ballot per level (two levels up to 4,096 sequences).
-__device__ int32_t wave_count_le(const int32_t *cu, int32_t n, int64_t key, int lane)
+// Numbers of entries of the non-decreasing array cu[0..n] that are <= ka and <= kb, by a 128-ary
+// search of the whole wave for both keys at once: per level each lane samples two positions per key
+// (four independent loads) and ballots count the samples at or below the key (one level up to 127
+// sequences, two up to 16,383).
+__device__ void wave_count_le2(const int32_t *cu, int32_t n, int64_t ka, int64_t kb, int lane, int32_t &ca, int32_t &cb)
 {
-    int32_t lo = 0, hi = n + 1;  // the count lies in [lo, hi]
-    while (true) {
-        const int32_t stride = (hi - lo + 63) / 64;
-        const int32_t pos = lo + lane * stride;
-        const int c = __builtin_popcountll(__ballot(pos < hi && (int64_t)cu[pos] <= key));
-        if (stride <= 1 || c == 0) return lo + c;
-        const int32_t nhi = lo + c * stride;
-        lo = lo + (c - 1) * stride + 1;
-        hi = min(hi, nhi);
-        if (lo >= hi) return lo;
+    int32_t lo[2] = {0, 0}, hi[2] = {n + 1, n + 1};
+    const int64_t key[2] = {ka, kb};
+    bool done[2] = {false, false};
+    int32_t res[2] = {0, 0};
+    while (!(done[0] && done[1])) {
+        int32_t stride[2], p0[2], p1[2];
+        bool le0[2], le1[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            stride[q] = (hi[q] - lo[q] + 127) / 128;
+            p0[q] = lo[q] + (2 * lane) * stride[q];
+            p1[q] = p0[q] + stride[q];
+            le0[q] = !done[q] && p0[q] < hi[q] && (int64_t)cu[p0[q]] <= key[q];
+            le1[q] = !done[q] && p1[q] < hi[q] && (int64_t)cu[p1[q]] <= key[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if (done[q]) continue;
+            const int c = __builtin_popcountll(__ballot(le0[q])) + __builtin_popcountll(__ballot(le1[q]));
+            if (stride[q] <= 1 || c == 0) {
+                res[q] = lo[q] + c;
+                done[q] = true;
+                continue;
+            }
+            const int32_t nhi = lo[q] + c * stride[q];
+            lo[q] = lo[q] + (c - 1) * stride[q] + 1;
+            hi[q] = min(hi[q], nhi);
+            if (lo[q] >= hi[q]) {
+                res[q] = lo[q];
+                done[q] = true;
+            }
+        }
     }
+    ca = res[0];
+    cb = res[1];
 }
 
 // Bits [lo, hi) of a 64-bit word, for any lo, hi (clamped to [0, 64]).
@@ -170,16 +196,29 @@ __device__ __forceinline__ void first_in(const ChunkMasks &cm, int64_t c0, int a
     multi = cnt >= 2;
 }
 
-__device__ __forceinline__ void load_masks(const Scan &sc, int64_t c0, int64_t c_end, int64_t from, int lane, ChunkMasks &cm)
+// Issue the chunk's id loads (tokens outside [from, c_end) read as a non-marker) ...
+__device__ __forceinline__ void issue_ids(const Scan &sc, int64_t c0, int64_t c_end, int64_t from, int lane,
+                                          int32_t (&v)[kSub])
 {
-    int32_t v[kSub];
 #pragma unroll
     for (int k = 0; k < kSub; ++k) {
         const int64_t g = c0 + 64 * k + lane;
         v[k] = (g < c_end && g >= from) ? sc.ids[g] : ~sc.marker;
     }
+}
+
+// ... and ballot them into the chunk's marker mask.
+__device__ __forceinline__ void ballot_ids(const Scan &sc, const int32_t (&v)[kSub], ChunkMasks &cm)
+{
 #pragma unroll
     for (int k = 0; k < kSub; ++k) cm.m[k] = __ballot(v[k] == sc.marker);
+}
+
+__device__ __forceinline__ void load_masks(const Scan &sc, int64_t c0, int64_t c_end, int64_t from, int lane, ChunkMasks &cm)
+{
+    int32_t v[kSub];
+    issue_ids(sc, c0, c_end, from, lane, v);
+    ballot_ids(sc, v, cm);
 }
 
 // Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan with Decoupled
@@ -265,15 +304,31 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
     const int64_t c_end = min<int64_t>(c0 + kChunk, sc.n_tokens);
     const int32_t n = sc.n_seqs;
 
+    // id loads and the sequence search go out together
+    int32_t idv[kSub];
+    issue_ids(sc, c0, c_end, c0, lane, idv);
+    int32_t cnt_first, cnt_last;
+    wave_count_le2(sc.cu, n, c0, c_end - 1, lane, cnt_first, cnt_last);
     ChunkMasks cm;
-    load_masks(sc, c0, c_end, c0, lane, cm);
-    const int32_t s_first = wave_count_le(sc.cu, n, c0, lane) - 1;
-    const int32_t s_last = wave_count_le(sc.cu, n, c_end - 1, lane) - 1;
+    ballot_ids(sc, idv, cm);
+    const int32_t s_first = cnt_first - 1, s_last = cnt_last - 1;
+
+    // first window of 64 sequences (chunk 0 starts at sequence 0 so leading empty sequences get
+    // their scalars); it also holds the starts of the chunk's first and, usually, last sequence
+    int32_t win = c0 == 0 ? 0 : max(s_first, 0);
+    int64_t W, Wn;
+    {
+        const int32_t j = win + lane;
+        W = j <= n ? (int64_t)sc.cu[min(j, n)] : INT64_MAX;
+        Wn = j < n ? (int64_t)sc.cu[j + 1] : INT64_MAX;
+    }
     const bool first_ok = s_first >= 0 && s_first < n;
-    const int64_t s0_begin = first_ok ? sc.cu[s_first] : c0;
+    int64_t s0_begin = c0;
+    if (first_ok) s0_begin = (s_first - win < 64) ? __shfl(W, s_first - win) : (int64_t)sc.cu[s_first];
     const bool need_carry = first_ok && s0_begin < c0;
     const bool last_ok = s_last >= 0 && s_last < n;
-    const int64_t sl_begin = last_ok ? sc.cu[s_last] : c_end;
+    int64_t sl_begin = c_end;
+    if (last_ok) sl_begin = (s_last - win < 64) ? __shfl(W, s_last - win) : (int64_t)sc.cu[s_last];
     const bool last_open = need_carry && s_last == s_first;
 
     // the chunk's last sequence: its part in this chunk, published before the look-back
@@ -292,12 +347,8 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
         }
     }
 
-    // windows of 64 sequences; chunk 0 starts at sequence 0 so leading empty sequences get scalars
-    int32_t win = c0 == 0 ? 0 : max(s_first, 0);
     while (true) {
         const int32_t j = win + lane;
-        const int64_t W = j <= n ? (int64_t)sc.cu[min(j, n)] : INT64_MAX;
-        const int64_t Wn = j < n ? (int64_t)sc.cu[j + 1] : INT64_MAX;
         int32_t f;
         bool mm;
         first_in(cm, c0, (int)(max(min(W, c_end), c0) - c0), (int)(max(min(Wn, c_end), c0) - c0), f, mm);
@@ -310,22 +361,40 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
             if (fin >= c0 && fin < c_end) write_scalars(sc, j, f == kNone ? -1 : (int32_t)(f - W), mm, Wn - W);
         }
         const int64_t w_lo = __shfl(W, 0), w_hi = __shfl(Wn, 63);
-#pragma unroll
-        for (int k = 0; k < kSub; ++k) {
-            const int64_t g = c0 + 64 * k + lane;
-            int r = 0;
-#pragma unroll
-            for (int step = 32; step > 0; step >>= 1)
-                if (__shfl(Wn, r + step - 1) <= g) r += step;
+        if (s_first == s_last && s_first >= win && s_first - win < 64) {
+            // the whole chunk lies in one sequence: no per-token search
+            const int r = s_first - win;
             const int32_t fr = __shfl(f, r);
             const int64_t sb = __shfl(W, r);
-            const bool ok = g < c_end && g >= w_lo && g < w_hi;
-            int32_t t = 0, h = 0, w = 0;
-            if (ok) canvas_planes((int32_t)(g - sb), (fr != kNone && fr <= g) ? (int32_t)(fr - sb) : kNone, t, h, w);
-            sink(k, ok, t, h, w);
+#pragma unroll
+            for (int k = 0; k < kSub; ++k) {
+                const int64_t g = c0 + 64 * k + lane;
+                const bool ok = g < c_end;
+                int32_t t = 0, h = 0, w = 0;
+                if (ok) canvas_planes((int32_t)(g - sb), (fr != kNone && fr <= g) ? (int32_t)(fr - sb) : kNone, t, h, w);
+                sink(k, ok, t, h, w);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kSub; ++k) {
+                const int64_t g = c0 + 64 * k + lane;
+                int r = 0;
+#pragma unroll
+                for (int step = 32; step > 0; step >>= 1)
+                    if (__shfl(Wn, r + step - 1) <= g) r += step;
+                const int32_t fr = __shfl(f, r);
+                const int64_t sb = __shfl(W, r);
+                const bool ok = g < c_end && g >= w_lo && g < w_hi;
+                int32_t t = 0, h = 0, w = 0;
+                if (ok) canvas_planes((int32_t)(g - sb), (fr != kNone && fr <= g) ? (int32_t)(fr - sb) : kNone, t, h, w);
+                sink(k, ok, t, h, w);
+            }
         }
         if (win + 64 >= n || (int64_t)sc.cu[win + 64] > c_end) break;
         win += 64;
+        const int32_t jn = win + lane;
+        W = jn <= n ? (int64_t)sc.cu[min(jn, n)] : INT64_MAX;
+        Wn = jn < n ? (int64_t)sc.cu[jn + 1] : INT64_MAX;
     }
 }
 
@@ -673,22 +742,20 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     }
 }
 
-// One wave per sequence.  Work items of a wave, eight lanes each: the Q heads (rotated in place),
-// the K heads (rotated into the cache), then 16-byte K pass-through chunks past the rotary dims.
+// Two waves per sequence.  Work items, one 8-element chunk each: the Q heads (eight lanes per head,
+// rotated in place), the K heads (rotated into the cache), then the K pass-through chunks past the
+// rotary dims.  With 8 Q heads, 2 K heads and 256 dims there are exactly 128 items, so every lane
+// issues its loads at once and the whole step is one round trip plus the math.
 template <bool BF16>
 __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t s = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int item0 = threadIdx.x & 127;
+    const int64_t s = (int64_t)blockIdx.x * (kBlock / 128) + (threadIdx.x >> 7);
     if (s >= d.n_seqs) return;
-    const int32_t plane = d.pos[s] - d.amount[s];
-    const int64_t slot = d.slots[s];
-    const bool wr = slot >= 0 && slot < d.num_slots;
-    const int64_t cbase = wr ? (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok : 0;
     const int nrq = d.nq * 8, nrk = d.nk * 8;
     const int chunks = (d.head_dim - 64) / 8;
     const int total = nrq + nrk + d.nk * chunks;
-    for (int it = lane; it < total; it += 64) {
+    for (int it = item0; it < total; it += 128) {
         if (it < nrq + nrk) {   // a whole 8-lane group takes this branch together
             const bool isq = it < nrq;
             const int h = (isq ? it : it - nrq) >> 3;
@@ -696,21 +763,31 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot
             const int e0 = 32 * half + 8 * m;
             const int64_t off = (isq ? s * d.q_tok + h * d.q_head : s * d.k_tok + h * d.k_head) + e0;
             const Raw8<BF16> own = load8<BF16>(isq ? d.q : d.k, off);
+            const int32_t plane = d.pos[s] - d.amount[s];
             double c[8], ss[8];
             pair_sincos(rot, m, half, plane, plane, plane, c, ss);
             const Raw8<BF16> y = rotate_chunk<BF16>(own, c, ss);
-            if (isq)
+            if (isq) {
                 store8<BF16>(d.q, off, y);
-            else if (wr)
-                store8<BF16>(d.cache, cbase + h * d.c_head + e0, y);
-        } else if (wr) {
+            } else {
+                const int64_t slot = d.slots[s];
+                if (slot >= 0 && slot < d.num_slots)
+                    store8<BF16>(d.cache, (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok +
+                                              h * d.c_head + e0, y);
+            }
+        } else {
             const int cc = it - nrq - nrk;
             const int h = cc / chunks;
             const int e = 64 + (cc % chunks) * 8;
-            store8<BF16>(d.cache, cbase + h * d.c_head + e, load8<BF16>(d.k, s * d.k_tok + h * d.k_head + e));
+            const Raw8<BF16> v = load8<BF16>(d.k, s * d.k_tok + h * d.k_head + e);
+            const int64_t slot = d.slots[s];
+            if (slot >= 0 && slot < d.num_slots)
+                store8<BF16>(d.cache, (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok +
+                                          h * d.c_head + e, v);
         }
     }
 }
+
 __global__ void zero_kernel(uint32_t *p, size_t words)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
@@ -815,7 +892,7 @@ hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, bool
 
 hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, bool bf16, hipStream_t stream)
 {
-    const unsigned blocks = (unsigned)((d.n_seqs + 3) / 4);
+    const unsigned blocks = (unsigned)((d.n_seqs + 1) / 2);
     if (bf16)
         decode_kernel<true><<<blocks, kBlock, 0, stream>>>(d, r);
     else
