@@ -303,8 +303,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f64",
         "io_dtype": "bf16",
+        "angle_dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "64 image prompts x 4096 tokens, bf16: planes from int32 ids + in-place "
                                "rotary of Q[262144,8,256] and K[262144,2,256]",

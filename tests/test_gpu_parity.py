@@ -443,3 +443,82 @@ def test_graph_replays_with_new_inputs():
         compare_heads(host_heads(q_d), qn, epl, "bf16", what=f"replay {rep} q")
         compare_heads(host_heads(k_d), kn, epl, "bf16", what=f"replay {rep} k")
         _ = torch.randn(1000, device="cuda").sum().item()   # unrelated eager work between replays
+
+
+def test_bf16_out_of_place_and_wide_plane_stride():
+    """bf16 out of place == in place (full heads written, inputs untouched); planes written into a
+    wider [3, L + 37] buffer leave the extra columns alone."""
+    b = synth.random_batch(81, 25, max_len=500)
+    qn, kn = b.qk()
+    L = b.n_tokens
+    wide = torch.full((3, L + 37), -5, dtype=torch.int32, device="cuda")
+    mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER, out=wide)
+    assert (wide[:, L:] == -5).all()
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    np.testing.assert_array_equal(wide[:, :L].cpu().numpy(), epl)
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    mr.apply(q, k, wide, q_out=qo, k_out=ko)
+    np.testing.assert_array_equal(host_heads(q), qn)
+    compare_heads(host_heads(qo), qn, epl, "bf16", what="q out of place")
+    compare_heads(host_heads(ko), kn, epl, "bf16", what="k out of place")
+    q2, k2 = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    mr.apply(q2, k2, wide)
+    assert torch.equal(q2, qo) and torch.equal(k2, ko)
+    # fused, out of place, Q only
+    q3 = dev_heads(qn, "bf16")
+    q3o = torch.empty_like(q3)
+    mr.apply_ids(q3, None, i32(b.ids), i32(b.cu_seqlens), MARKER, q_out=q3o)
+    assert torch.equal(q3o, qo)
+    np.testing.assert_array_equal(host_heads(q3), qn)
+
+
+def test_decode_fp32_and_generic_shapes():
+    d = synth.config4(n_seqs=300, num_blocks=512)
+    g = synth.rng(91, 5)
+    for dt, nq, nk, D in (("f32", 8, 2, 256), ("bf16", 4, 1, 128), ("f32", 3, 3, 64)):
+        qf = synth.normal(91, 70, d.n_seqs * nq * D).reshape(d.n_seqs, nq, D)
+        kf = synth.normal(91, 71, d.n_seqs * nk * D).reshape(d.n_seqs, nk, D)
+        qn = synth.to_bf16_bits(qf) if dt == "bf16" else qf
+        kn = synth.to_bf16_bits(kf) if dt == "bf16" else kf
+        q, k = dev_heads(qn, dt), dev_heads(kn, dt)
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        cache = torch.zeros((512, 16, nk, D), dtype=tdt, device="cuda")
+        pos = g.integers(0, 40000, size=d.n_seqs).astype(np.int32)
+        amount = np.where(g.uniform(size=d.n_seqs) < 0.5, 58, 0).astype(np.int32)
+        slots = g.permutation(512 * 16)[:d.n_seqs].astype(np.int64)
+        mr.decode(q, k, i32(pos), i32(amount), cache, torch.from_numpy(slots).cuda())
+        plane = np.stack([pos - amount] * 3)
+        compare_heads(host_heads(q), qn, plane, dt, what=f"decode q {dt} {nq}x{D}")
+        got_k = host_heads(cache[torch.from_numpy(slots // 16).cuda(), torch.from_numpy(slots % 16).cuda()])
+        compare_heads(got_k, kn, plane, dt, what=f"decode k {dt} {nk}x{D}")
+
+
+def test_binding_raises_library_status():
+    q = torch.zeros((4, 8, 256), dtype=torch.bfloat16, device="cuda")
+    pl = torch.zeros((3, 4), dtype=torch.int32, device="cuda")
+    with pytest.raises(mr.MropeError) as e:
+        mr.apply(q, None, pl, rot_dim=32)
+    assert e.value.status == 3 and "rot_dim" in str(e.value)
+    with pytest.raises(mr.MropeError) as e:
+        mr.apply(q, None, pl, theta=-1.0)
+    assert e.value.status == 1
+    with pytest.raises(mr.MropeError) as e:
+        mr.apply(q[:, :, 4:], None, pl)   # head_dim 252: not a multiple of 8
+    assert e.value.status == 3
+
+
+def test_workspace_init_recovers_garbage():
+    """A workspace full of garbage words (which can carry any epoch tag) is made safe by
+    mrope_workspace_init; results are then exact in both epoch modes."""
+    import ctypes
+
+    lib = mr._lib.load()
+    b = synth.random_batch(95, 30, max_len=2000)
+    ws = mr.Workspace(b.n_tokens)
+    ws.view.fill_(0xFF)
+    rc = lib.mrope_workspace_init(ws.ptr, ws.capacity, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    assert int(ws.view.sum().item()) == 0
+    pl, st, am, og, fl = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER, workspace=ws)
+    _check_scan(b, pl, st, am, og, fl, "after init")
