@@ -125,6 +125,21 @@ def extras(args, dev, timed):
                          "tokens_per_s_fused": cfg.n_tokens / (f_us / 1e6)}
         del q, k, pl
         torch.cuda.empty_cache()
+    # fp16 I/O on the default batch shape (same bytes as bf16)
+    cfg = synth.config2()
+    log("extras: 64x4096 fp16")
+    qn, kn = cfg.qk()
+    q = torch.from_numpy(synth.to_f16_bits(synth.bf16_bits_to_f32(qn)).view(np.int16)).view(torch.float16).to(dev)
+    k = torch.from_numpy(synth.to_f16_bits(synth.bf16_bits_to_f32(kn)).view(np.int16)).view(torch.float16).to(dev)
+    ids = torch.from_numpy(cfg.ids).to(dev)
+    cu = torch.from_numpy(cfg.cu_seqlens).to(dev)
+    pl, *_ = mr.planes(ids, cu, synth.IMAGE_ID)
+    a_us = timed(lambda: mr.apply(q, k, pl), args.steps) * 1e6
+    out["64x4096-image-f16"] = {"tokens": cfg.n_tokens, "apply_us": a_us,
+                                "apply_gbs": algorithmic_bytes_apply(cfg.n_tokens) / a_us / 1e3}
+    del q, k, pl
+    torch.cuda.empty_cache()
+
     d = synth.config4()
     log(f"extras: {d.name}")
     qn, kn = d.qk()

@@ -18,7 +18,7 @@ the Qwen3.5 hybrid, on Core AI", section "The canvas rule and why the gate is on
 from __future__ import annotations
 
 from . import _lib
-from ._lib import (MROPE_BF16, MROPE_F32, MarkerFlags, MropeError, TEXT_ONLY_START, Workspace, apply, apply_ids,
+from ._lib import (MROPE_BF16, MROPE_F16, MROPE_F32, MarkerFlags, MropeError, TEXT_ONLY_START, Workspace, apply, apply_ids,
                    cu_seqlens_from_lens, decode, library_path, planes)
 
 IMAGE_ID = 248078
@@ -26,4 +26,4 @@ DEFAULT_THETA = 1e7
 
 __all__ = ["planes", "apply", "apply_ids", "decode", "Workspace", "MropeError", "MarkerFlags",
            "cu_seqlens_from_lens", "library_path", "IMAGE_ID", "DEFAULT_THETA", "TEXT_ONLY_START",
-           "MROPE_F32", "MROPE_BF16"]
+           "MROPE_F32", "MROPE_BF16", "MROPE_F16"]

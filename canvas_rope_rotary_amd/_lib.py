@@ -13,6 +13,7 @@ _lib = None
 
 MROPE_F32 = 0
 MROPE_BF16 = 1
+MROPE_F16 = 2
 TEXT_ONLY_START = 1 << 30
 ROT_DIM = 64
 
@@ -105,12 +106,14 @@ class _on_device:
             torch.cuda.set_device(self.prev)
 
 
+_DTYPES = {torch.float32: MROPE_F32, torch.bfloat16: MROPE_BF16, torch.float16: MROPE_F16}
+
+
 def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
-        return MROPE_BF16
-    if t.dtype == torch.float32:
-        return MROPE_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)") from None
 
 
 def _require_cuda(*ts):

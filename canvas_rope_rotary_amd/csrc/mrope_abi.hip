@@ -57,7 +57,8 @@ mrope_status check_heads(void *q, int64_t q_tok, int64_t q_head, int32_t nq, voi
                          int32_t nk, int64_t n_tokens, int32_t head_dim, int32_t rot_dim, int32_t dtype, void *q_out,
                          void *k_out)
 {
-    if (dtype != MROPE_F32 && dtype != MROPE_BF16) return fail(MROPE_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    if (dtype != MROPE_F32 && dtype != MROPE_BF16 && dtype != MROPE_F16)
+        return fail(MROPE_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
     if (rot_dim != 64) return fail(MROPE_ERR_UNSUPPORTED, "rot_dim must be 64 (got %d)", rot_dim);
     if (head_dim < 64 || head_dim > 1024 || head_dim % 8)
         return fail(MROPE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in [64, 1024] (got %d)", head_dim);
@@ -71,7 +72,7 @@ mrope_status check_heads(void *q, int64_t q_tok, int64_t q_head, int32_t nq, voi
     if (q_out && nk > 0 && !k_out) return fail(MROPE_ERR_ARG, "k_out is NULL while q_out is set");
     if (k_out && nq > 0 && !q_out) return fail(MROPE_ERR_ARG, "q_out is NULL while k_out is set");
     if (q_tok < 0 || q_head < 0 || k_tok < 0 || k_head < 0) return fail(MROPE_ERR_ARG, "negative stride");
-    const int64_t vec = dtype == MROPE_BF16 ? 8 : 4;
+    const int64_t vec = dtype == MROPE_F32 ? 4 : 8;
     if ((nq > 0 && (q_tok % vec || q_head % vec)) || (nk > 0 && (k_tok % vec || k_head % vec)))
         return fail(MROPE_ERR_ALIGN, "strides must be multiples of %lld elements", (long long)vec);
     if ((nq > 0 && !aligned16(q)) || (nk > 0 && !aligned16(k)) || (q_out && !aligned16(q_out)) ||
@@ -212,7 +213,7 @@ mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, i
     const Heads h = make_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
                                n_tokens, head_dim, q_out, k_out);
     (void)hipGetLastError();
-    return hip_status(launch_apply(h, make_rotary(theta), planes, plane_stride, dtype == MROPE_BF16,
+    return hip_status(launch_apply(h, make_rotary(theta), planes, plane_stride, dtype,
                                    static_cast<hipStream_t>(stream)),
                       "mrope_apply");
 }
@@ -241,7 +242,7 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
     }
     const Heads h = make_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
                                n_tokens, head_dim, q_out, k_out);
-    return hip_status(launch_apply_ids(h, make_rotary(theta), sc, dtype == MROPE_BF16, s), "mrope_apply_ids");
+    return hip_status(launch_apply_ids(h, make_rotary(theta), sc, dtype, s), "mrope_apply_ids");
 }
 
 mrope_status mrope_decode(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, const void *k,
@@ -262,7 +263,7 @@ mrope_status mrope_decode(void *q, int64_t q_tok_stride, int64_t q_head_stride, 
         if (block_size <= 0 || num_blocks < 0) return fail(MROPE_ERR_ARG, "block_size must be > 0 and num_blocks >= 0");
         if (cache_block_stride < 0 || cache_tok_stride < 0 || cache_head_stride < 0)
             return fail(MROPE_ERR_ARG, "negative cache stride");
-        const int64_t vec = dtype == MROPE_BF16 ? 8 : 4;
+        const int64_t vec = dtype == MROPE_F32 ? 4 : 8;
         if (!aligned16(k_cache) || cache_block_stride % vec || cache_tok_stride % vec || cache_head_stride % vec)
             return fail(MROPE_ERR_ALIGN, "cache pointer / strides break 16-byte alignment");
     }
@@ -287,7 +288,7 @@ mrope_status mrope_decode(void *q, int64_t q_tok_stride, int64_t q_head_stride, 
     d.c_tok = cache_tok_stride;
     d.c_head = cache_head_stride;
     (void)hipGetLastError();
-    return hip_status(launch_decode(d, make_rotary(theta), dtype == MROPE_BF16, static_cast<hipStream_t>(stream)),
+    return hip_status(launch_decode(d, make_rotary(theta), dtype, static_cast<hipStream_t>(stream)),
                       "mrope_decode");
 }
 

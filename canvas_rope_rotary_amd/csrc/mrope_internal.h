@@ -64,9 +64,10 @@ struct DecodeArgs {
 hipError_t launch_workspace_init(void *ws, size_t bytes, hipStream_t stream);
 hipError_t launch_text_scalars(const Scan &s, hipStream_t stream);
 hipError_t launch_planes(const Scan &s, hipStream_t stream);
-hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t plane_stride, bool bf16,
+// io: the C ABI's dtype code (0 fp32, 1 bf16, 2 fp16)
+hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t plane_stride, int io,
                         hipStream_t stream);
-hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, bool bf16, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, bool bf16, hipStream_t stream);
+hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, int io, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, int io, hipStream_t stream);
 
 }  // namespace mrope

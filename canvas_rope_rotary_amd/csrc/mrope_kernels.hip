@@ -23,7 +23,8 @@
 //
 // Precision: the angle is one fp32 multiply (as the model's rotary forms it); cos/sin and the two
 // products of each output are double (the same per-lane rate as fp32 on this chip with packed fp32
-// off); each output is rounded once to fp32 and, for bf16, once more to bf16 (nearest even).
+// off); each output is rounded once to fp32 and, for bf16/fp16 I/O, once more to the 16-bit type
+// (nearest even).
 #include "mrope_internal.h"
 #include "mrope_math.h"
 
@@ -399,26 +400,49 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
 }
 
 // ------------------------------------------------------------------ element I/O ----------------
+// Element types of Q/K (the C ABI's dtype codes).
+constexpr int kIoF32 = 0, kIoBF16 = 1, kIoF16 = 2;
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+// Two fp32 values to a packed pair of the 16-bit type, each rounded to nearest even.
+template <int IO>
+__device__ __forceinline__ uint32_t pack16x2(float a, float b)
 {
     const f32x2_t f = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    if constexpr (IO == kIoBF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
 }
 
-// 8 consecutive elements as raw 16-byte words: one for bf16, two for fp32.
-template <bool BF16>
+// A packed pair of the 16-bit type to fp32 (exact).
+template <int IO>
+__device__ __forceinline__ void unpack16x2(uint32_t u, float &lo, float &hi)
+{
+    if constexpr (IO == kIoBF16) {
+        lo = __uint_as_float(u << 16);
+        hi = __uint_as_float(u & 0xffff0000u);
+    } else {
+        const f32x2_t f = __builtin_convertvector(__builtin_bit_cast(f16x2_t, u), f32x2_t);
+        lo = f[0];
+        hi = f[1];
+    }
+}
+
+// 8 consecutive elements as raw 16-byte words: one for the 16-bit types, two for fp32.
+template <int IO>
 struct Raw8 {
-    uint4 w[BF16 ? 1 : 2];
+    uint4 w[IO == kIoF32 ? 2 : 1];
 };
 
-template <bool BF16>
-__device__ __forceinline__ Raw8<BF16> load8(const void *base, int64_t elem)
+template <int IO>
+__device__ __forceinline__ Raw8<IO> load8(const void *base, int64_t elem)
 {
-    Raw8<BF16> r;
-    if constexpr (BF16) {
+    Raw8<IO> r;
+    if constexpr (IO != kIoF32) {
         r.w[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
     } else {
         const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
@@ -428,10 +452,10 @@ __device__ __forceinline__ Raw8<BF16> load8(const void *base, int64_t elem)
     return r;
 }
 
-template <bool BF16>
-__device__ __forceinline__ void store8(void *base, int64_t elem, const Raw8<BF16> &r)
+template <int IO>
+__device__ __forceinline__ void store8(void *base, int64_t elem, const Raw8<IO> &r)
 {
-    if constexpr (BF16) {
+    if constexpr (IO != kIoF32) {
         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + elem) = r.w[0];
     } else {
         uint4 *p = reinterpret_cast<uint4 *>(static_cast<float *>(base) + elem);
@@ -440,16 +464,13 @@ __device__ __forceinline__ void store8(void *base, int64_t elem, const Raw8<BF16
     }
 }
 
-template <bool BF16>
-__device__ __forceinline__ void unpack8(const Raw8<BF16> &r, float (&x)[8])
+template <int IO>
+__device__ __forceinline__ void unpack8(const Raw8<IO> &r, float (&x)[8])
 {
-    if constexpr (BF16) {
+    if constexpr (IO != kIoF32) {
         const uint32_t u[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(u[i] << 16);
-            x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-        }
+        for (int i = 0; i < 4; ++i) unpack16x2<IO>(u[i], x[2 * i], x[2 * i + 1]);
     } else {
         const uint32_t u[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
 #pragma unroll
@@ -457,13 +478,13 @@ __device__ __forceinline__ void unpack8(const Raw8<BF16> &r, float (&x)[8])
     }
 }
 
-template <bool BF16>
-__device__ __forceinline__ Raw8<BF16> pack8(const float (&y)[8])
+template <int IO>
+__device__ __forceinline__ Raw8<IO> pack8(const float (&y)[8])
 {
-    Raw8<BF16> r;
-    if constexpr (BF16) {
-        r.w[0] = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                            pack_bf16x2(y[6], y[7]));
+    Raw8<IO> r;
+    if constexpr (IO != kIoF32) {
+        r.w[0] = make_uint4(pack16x2<IO>(y[0], y[1]), pack16x2<IO>(y[2], y[3]), pack16x2<IO>(y[4], y[5]),
+                            pack16x2<IO>(y[6], y[7]));
     } else {
         r.w[0] = make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3]));
         r.w[1] = make_uint4(__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7]));
@@ -489,12 +510,12 @@ __device__ __forceinline__ double swap_pair(double v)
     const uint64_t lo = swap_pair((uint32_t)u), hi = swap_pair((uint32_t)(u >> 32));
     return __builtin_bit_cast(double, lo | (hi << 32));
 }
-template <bool BF16>
-__device__ __forceinline__ Raw8<BF16> swap_pair(const Raw8<BF16> &r)
+template <int IO>
+__device__ __forceinline__ Raw8<IO> swap_pair(const Raw8<IO> &r)
 {
-    Raw8<BF16> o;
+    Raw8<IO> o;
 #pragma unroll
-    for (int k = 0; k < (BF16 ? 1 : 2); ++k)
+    for (int k = 0; k < (IO == kIoF32 ? 2 : 1); ++k)
         o.w[k] = make_uint4(swap_pair(r.w[k].x), swap_pair(r.w[k].y), swap_pair(r.w[k].z), swap_pair(r.w[k].w));
     return o;
 }
@@ -527,56 +548,56 @@ __device__ __forceinline__ void pair_sincos(const Rotary &rot, int m, int half, 
 }
 
 // One head chunk: own holds this lane's 8 dims, the partner's come by DPP.
-template <bool BF16>
-__device__ __forceinline__ Raw8<BF16> rotate_chunk(const Raw8<BF16> &own, const double (&c)[8], const double (&ss)[8])
+template <int IO>
+__device__ __forceinline__ Raw8<IO> rotate_chunk(const Raw8<IO> &own, const double (&c)[8], const double (&ss)[8])
 {
     float x[8], p[8], y[8];
-    unpack8<BF16>(own, x);
-    unpack8<BF16>(swap_pair<BF16>(own), p);
+    unpack8<IO>(own, x);
+    unpack8<IO>(swap_pair<IO>(own), p);
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = (float)__builtin_fma((double)x[e], c[e], (double)p[e] * ss[e]);
-    return pack8<BF16>(y);
+    return pack8<IO>(y);
 }
 
 // Copy this lane's share of the dims past the rotary part (out-of-place calls only).
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ void copy_tail(const void *src, void *dst, int64_t off, int head_dim, int l)
 {
-    for (int d = 64 + 8 * l; d < head_dim; d += 64) store8<BF16>(dst, off + d, load8<BF16>(src, off + d));
+    for (int d = 64 + 8 * l; d < head_dim; d += 64) store8<IO>(dst, off + d, load8<IO>(src, off + d));
 }
 
 __device__ __forceinline__ int64_t q_off(const Heads &hd, int64_t g, int h) { return g * hd.q_tok + h * hd.q_head; }
 __device__ __forceinline__ int64_t k_off(const Heads &hd, int64_t g, int h) { return g * hd.k_tok + h * hd.k_head; }
 
-template <bool BF16, int NQ, int NK>
-__device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int e0, Raw8<BF16> (&qv)[NQ],
-                                                 Raw8<BF16> (&kv)[NK])
+template <int IO, int NQ, int NK>
+__device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int e0, Raw8<IO> (&qv)[NQ],
+                                                 Raw8<IO> (&kv)[NK])
 {
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) qv[h] = load8<BF16>(hd.q, q_off(hd, g, h) + e0);
+    for (int h = 0; h < NQ; ++h) qv[h] = load8<IO>(hd.q, q_off(hd, g, h) + e0);
 #pragma unroll
-    for (int h = 0; h < NK; ++h) kv[h] = load8<BF16>(hd.k, k_off(hd, g, h) + e0);
+    for (int h = 0; h < NK; ++h) kv[h] = load8<IO>(hd.k, k_off(hd, g, h) + e0);
 }
 
-template <bool BF16, int NQ, int NK>
+template <int IO, int NQ, int NK>
 __device__ __forceinline__ void rotate_token_fixed(const Heads &hd, int64_t g, int e0, int l, const double (&c)[8],
-                                                   const double (&ss)[8], const Raw8<BF16> (&qv)[NQ],
-                                                   const Raw8<BF16> (&kv)[NK])
+                                                   const double (&ss)[8], const Raw8<IO> (&qv)[NQ],
+                                                   const Raw8<IO> (&kv)[NK])
 {
     void *qo = hd.q_out ? hd.q_out : hd.q;
     void *ko = hd.k_out ? hd.k_out : hd.k;
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) store8<BF16>(qo, q_off(hd, g, h) + e0, rotate_chunk<BF16>(qv[h], c, ss));
+    for (int h = 0; h < NQ; ++h) store8<IO>(qo, q_off(hd, g, h) + e0, rotate_chunk<IO>(qv[h], c, ss));
 #pragma unroll
-    for (int h = 0; h < NK; ++h) store8<BF16>(ko, k_off(hd, g, h) + e0, rotate_chunk<BF16>(kv[h], c, ss));
+    for (int h = 0; h < NK; ++h) store8<IO>(ko, k_off(hd, g, h) + e0, rotate_chunk<IO>(kv[h], c, ss));
     if (hd.q_out) {
-        for (int h = 0; h < NQ; ++h) copy_tail<BF16>(hd.q, hd.q_out, q_off(hd, g, h), hd.head_dim, l);
-        for (int h = 0; h < NK; ++h) copy_tail<BF16>(hd.k, hd.k_out, k_off(hd, g, h), hd.head_dim, l);
+        for (int h = 0; h < NQ; ++h) copy_tail<IO>(hd.q, hd.q_out, q_off(hd, g, h), hd.head_dim, l);
+        for (int h = 0; h < NK; ++h) copy_tail<IO>(hd.k, hd.k_out, k_off(hd, g, h), hd.head_dim, l);
     }
 }
 
 // Any head counts: one head at a time.
-template <bool BF16>
+template <int IO>
 __device__ __forceinline__ void rotate_token_any(const Heads &hd, int64_t g, int e0, int l, const double (&c)[8],
                                                  const double (&ss)[8])
 {
@@ -586,8 +607,8 @@ __device__ __forceinline__ void rotate_token_any(const Heads &hd, int64_t g, int
         void *src = isq ? hd.q : hd.k;
         void *dst = isq ? (hd.q_out ? hd.q_out : hd.q) : (hd.k_out ? hd.k_out : hd.k);
         const int64_t base = isq ? q_off(hd, g, h) : k_off(hd, g, h);
-        store8<BF16>(dst, base + e0, rotate_chunk<BF16>(load8<BF16>(src, base + e0), c, ss));
-        if (hd.q_out) copy_tail<BF16>(src, dst, base, hd.head_dim, l);
+        store8<IO>(dst, base + e0, rotate_chunk<IO>(load8<IO>(src, base + e0), c, ss));
+        if (hd.q_out) copy_tail<IO>(src, dst, base, hd.head_dim, l);
     }
 }
 
@@ -599,7 +620,7 @@ constexpr int kTokPerBlock = kBlock / kLanesPerTok;
 // Fixed head counts: a grid-stride loop over tokens (the grid is sized to the chip by the host).
 // Each 8-lane group prefetches the next token's planes and head chunks before it rotates and
 // stores the current one, so loads stay in flight while the sincos and rotation math runs.
-template <bool BF16, int NQ, int NK>
+template <int IO, int NQ, int NK>
 __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
                                                        int64_t ps)
 {
@@ -610,22 +631,22 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
     int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 3);
     if (g >= hd.n_tokens) return;   // the eight lanes of a token leave together
     int32_t pt = planes[g], ph = planes[ps + g], pw = planes[2 * ps + g];
-    Raw8<BF16> qv[NQ], kv[NK];
-    load_token_fixed<BF16, NQ, NK>(hd, g, e0, qv, kv);
+    Raw8<IO> qv[NQ], kv[NK];
+    load_token_fixed<IO, NQ, NK>(hd, g, e0, qv, kv);
     while (true) {
         const int64_t gn = g + stride;
         const bool more = gn < hd.n_tokens;
         int32_t nt = 0, nh = 0, nw = 0;
-        Raw8<BF16> qn[NQ], kn[NK];
+        Raw8<IO> qn[NQ], kn[NK];
         if (more) {
             nt = planes[gn];
             nh = planes[ps + gn];
             nw = planes[2 * ps + gn];
-            load_token_fixed<BF16, NQ, NK>(hd, gn, e0, qn, kn);
+            load_token_fixed<IO, NQ, NK>(hd, gn, e0, qn, kn);
         }
         double c[8], ss[8];
         pair_sincos(rot, m, half, pt, ph, pw, c, ss);
-        rotate_token_fixed<BF16, NQ, NK>(hd, g, e0, l, c, ss, qv, kv);
+        rotate_token_fixed<IO, NQ, NK>(hd, g, e0, l, c, ss, qv, kv);
         if (!more) break;
         g = gn;
         pt = nt;
@@ -639,7 +660,7 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
 }
 
 // Any head counts: one token per 8-lane group, one head at a time.
-template <bool BF16>
+template <int IO>
 __global__ __launch_bounds__(kBlock) void apply_any_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
                                                            int64_t ps)
 {
@@ -650,7 +671,7 @@ __global__ __launch_bounds__(kBlock) void apply_any_kernel(Heads hd, Rotary rot,
     if (g >= hd.n_tokens) return;
     double c[8], ss[8];
     pair_sincos(rot, m, half, planes[g], planes[ps + g], planes[2 * ps + g], c, ss);
-    rotate_token_any<BF16>(hd, g, e0, l, c, ss);
+    rotate_token_any<IO>(hd, g, e0, l, c, ss);
 }
 
 // One wave per chunk, four chunks per workgroup.
@@ -673,7 +694,7 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
 // Fused: one chunk per workgroup.  Every lane issues the Q/K loads of its first token, wave 0 scans
 // the chunk into LDS meanwhile, then the workgroup rotates the chunk 32 tokens at a time, each
 // 8-lane group prefetching its next token before rotating the current one.
-template <bool BF16, int NQ, int NK>
+template <int IO, int NQ, int NK>
 __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc)
 {
     __shared__ int32_t s_pl[3][kChunk];
@@ -689,9 +710,9 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     constexpr int AQ = kFixed ? NQ : 1, AK = kFixed ? NK : 1;
 
     int64_t g = c0 + (tid >> 3);
-    Raw8<BF16> qv[AQ], kv[AK];
+    Raw8<IO> qv[AQ], kv[AK];
     if constexpr (kFixed) {
-        if (g < c_end) load_token_fixed<BF16, AQ, AK>(hd, g, e0, qv, kv);
+        if (g < c_end) load_token_fixed<IO, AQ, AK>(hd, g, e0, qv, kv);
     }
 
     if (tid < 64) {
@@ -722,11 +743,11 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         const int64_t gn = g + kTokPerBlock;
         double c[8], ss[8];
         if constexpr (kFixed) {
-            Raw8<BF16> qn[AQ], kn[AK];
-            if (gn < c_end) load_token_fixed<BF16, AQ, AK>(hd, gn, e0, qn, kn);
+            Raw8<IO> qn[AQ], kn[AK];
+            if (gn < c_end) load_token_fixed<IO, AQ, AK>(hd, gn, e0, qn, kn);
             if (ok) {
                 pair_sincos(rot, m, half, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
-                rotate_token_fixed<BF16, AQ, AK>(hd, g, e0, l, c, ss, qv, kv);
+                rotate_token_fixed<IO, AQ, AK>(hd, g, e0, l, c, ss, qv, kv);
             }
 #pragma unroll
             for (int h = 0; h < AQ; ++h) qv[h] = qn[h];
@@ -735,7 +756,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         } else {
             if (ok) {
                 pair_sincos(rot, m, half, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
-                rotate_token_any<BF16>(hd, g, e0, l, c, ss);
+                rotate_token_any<IO>(hd, g, e0, l, c, ss);
             }
         }
         g = gn;
@@ -746,7 +767,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
 // rotated in place), the K heads (rotated into the cache), then the K pass-through chunks past the
 // rotary dims.  With 8 Q heads, 2 K heads and 256 dims there are exactly 128 items, so every lane
 // issues its loads at once and the whole step is one round trip plus the math.
-template <bool BF16>
+template <int IO>
 __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot)
 {
     const int item0 = threadIdx.x & 127;
@@ -762,27 +783,27 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot
             const int l = it & 7, m = l >> 1, half = l & 1;
             const int e0 = 32 * half + 8 * m;
             const int64_t off = (isq ? s * d.q_tok + h * d.q_head : s * d.k_tok + h * d.k_head) + e0;
-            const Raw8<BF16> own = load8<BF16>(isq ? d.q : d.k, off);
+            const Raw8<IO> own = load8<IO>(isq ? d.q : d.k, off);
             const int32_t plane = d.pos[s] - d.amount[s];
             double c[8], ss[8];
             pair_sincos(rot, m, half, plane, plane, plane, c, ss);
-            const Raw8<BF16> y = rotate_chunk<BF16>(own, c, ss);
+            const Raw8<IO> y = rotate_chunk<IO>(own, c, ss);
             if (isq) {
-                store8<BF16>(d.q, off, y);
+                store8<IO>(d.q, off, y);
             } else {
                 const int64_t slot = d.slots[s];
                 if (slot >= 0 && slot < d.num_slots)
-                    store8<BF16>(d.cache, (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok +
+                    store8<IO>(d.cache, (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok +
                                               h * d.c_head + e0, y);
             }
         } else {
             const int cc = it - nrq - nrk;
             const int h = cc / chunks;
             const int e = 64 + (cc % chunks) * 8;
-            const Raw8<BF16> v = load8<BF16>(d.k, s * d.k_tok + h * d.k_head + e);
+            const Raw8<IO> v = load8<IO>(d.k, s * d.k_tok + h * d.k_head + e);
             const int64_t slot = d.slots[s];
             if (slot >= 0 && slot < d.num_slots)
-                store8<BF16>(d.cache, (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok +
+                store8<IO>(d.cache, (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok +
                                           h * d.c_head + e, v);
         }
     }
@@ -853,50 +874,59 @@ static int compute_units()
     return cus > 0 ? cus : 256;
 }
 
-template <bool BF16>
+template <int IO>
 static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, hipStream_t st)
 {
     const int64_t groups = (h.n_tokens + kTokPerBlock - 1) / kTokPerBlock;
     if (h.nq == 8 && h.nk == 2) {
         const int64_t cap = (int64_t)compute_units() * kApplyBlocksPerCU;
         const unsigned blocks = (unsigned)(groups < cap ? groups : cap);
-        apply_kernel<BF16, 8, 2><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
+        apply_kernel<IO, 8, 2><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
     } else {
-        apply_any_kernel<BF16><<<(unsigned)groups, kBlock, 0, st>>>(h, r, planes, ps);
+        apply_any_kernel<IO><<<(unsigned)groups, kBlock, 0, st>>>(h, r, planes, ps);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, bool bf16,
+hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, int io,
                         hipStream_t stream)
 {
-    return bf16 ? apply_dispatch<true>(h, r, planes, ps, stream) : apply_dispatch<false>(h, r, planes, ps, stream);
+    switch (io) {
+    case kIoBF16: return apply_dispatch<kIoBF16>(h, r, planes, ps, stream);
+    case kIoF16: return apply_dispatch<kIoF16>(h, r, planes, ps, stream);
+    default: return apply_dispatch<kIoF32>(h, r, planes, ps, stream);
+    }
 }
 
-template <bool BF16>
+template <int IO>
 static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, hipStream_t st)
 {
     const unsigned n_chunks = (unsigned)((h.n_tokens + kChunk - 1) / kChunk);
     if (h.nq == 8 && h.nk == 2)
-        apply_ids_kernel<BF16, 8, 2><<<n_chunks, kBlock, 0, st>>>(h, r, s);
+        apply_ids_kernel<IO, 8, 2><<<n_chunks, kBlock, 0, st>>>(h, r, s);
     else
-        apply_ids_kernel<BF16, 0, 0><<<n_chunks, kBlock, 0, st>>>(h, r, s);
+        apply_ids_kernel<IO, 0, 0><<<n_chunks, kBlock, 0, st>>>(h, r, s);
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : bump_if_device_epoch(s, st);
 }
 
-hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, bool bf16, hipStream_t stream)
+hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, int io, hipStream_t stream)
 {
-    return bf16 ? apply_ids_dispatch<true>(h, r, s, stream) : apply_ids_dispatch<false>(h, r, s, stream);
+    switch (io) {
+    case kIoBF16: return apply_ids_dispatch<kIoBF16>(h, r, s, stream);
+    case kIoF16: return apply_ids_dispatch<kIoF16>(h, r, s, stream);
+    default: return apply_ids_dispatch<kIoF32>(h, r, s, stream);
+    }
 }
 
-hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, bool bf16, hipStream_t stream)
+hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, int io, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)((d.n_seqs + 1) / 2);
-    if (bf16)
-        decode_kernel<true><<<blocks, kBlock, 0, stream>>>(d, r);
-    else
-        decode_kernel<false><<<blocks, kBlock, 0, stream>>>(d, r);
+    switch (io) {
+    case kIoBF16: decode_kernel<kIoBF16><<<blocks, kBlock, 0, stream>>>(d, r); break;
+    case kIoF16: decode_kernel<kIoF16><<<blocks, kBlock, 0, stream>>>(d, r); break;
+    default: decode_kernel<kIoF32><<<blocks, kBlock, 0, stream>>>(d, r); break;
+    }
     return hipGetLastError();
 }
 

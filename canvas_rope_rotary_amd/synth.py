@@ -69,9 +69,37 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE half bit patterns (uint16), round to nearest even (numpy's conversion)."""
+    return np.ascontiguousarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """IEEE half bit patterns -> the float32 values they represent (exact)."""
+    return np.asarray(b, np.uint16).view(np.float16).astype(np.float32)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """bf16 bit patterns -> the float32 values they represent (exact)."""
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values in the workload's storage form (bit patterns for the 16-bit types)."""
+    if dtype == "bf16":
+        return to_bf16_bits(x)
+    if dtype == "f16":
+        return to_f16_bits(x)
+    return np.ascontiguousarray(x, np.float32)
+
+
+def to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage form back to the float32 values (exact)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x)
+    if dtype == "f16":
+        return f16_bits_to_f32(x)
+    return np.asarray(x, np.float32)
 
 
 def text_ids(g: np.random.Generator, n: int) -> np.ndarray:
@@ -102,7 +130,7 @@ class Prefill:
     ids: np.ndarray            # [L] int32
     cu_seqlens: np.ndarray     # [n+1] int32
     placed: list               # frame position used to build each sequence (None = text only)
-    dtype: str                 # "f32" | "bf16"
+    dtype: str                 # "f32" | "bf16" | "f16"
     n_q_heads: int = 8
     n_k_heads: int = 2
     head_dim: int = 256
@@ -120,13 +148,11 @@ class Prefill:
         return len(self.cu_seqlens) - 1
 
     def qk(self):
-        """(q, k) as numpy arrays [L, H, D]: float32 for "f32", uint16 bf16 bits for "bf16"."""
+        """(q, k) as numpy arrays [L, H, D]: float32 for "f32", uint16 bit patterns for "bf16" / "f16"."""
         L, D = self.n_tokens, self.head_dim
         q = normal(self.seed, _Q, L * self.n_q_heads * D).reshape(L, self.n_q_heads, D)
         k = normal(self.seed, _K, L * self.n_k_heads * D).reshape(L, self.n_k_heads, D)
-        if self.dtype == "bf16":
-            return to_bf16_bits(q), to_bf16_bits(k)
-        return q, k
+        return to_dtype(q, self.dtype), to_dtype(k, self.dtype)
 
 
 def _batch(name, seed, lengths, placed, dtype, **kw) -> Prefill:
@@ -215,9 +241,7 @@ class Decode:
         D = self.head_dim
         q = normal(self.seed, _Q, self.n_seqs * self.n_q_heads * D).reshape(self.n_seqs, self.n_q_heads, D)
         k = normal(self.seed, _K, self.n_seqs * self.n_k_heads * D).reshape(self.n_seqs, self.n_k_heads, D)
-        if self.dtype == "bf16":
-            return to_bf16_bits(q), to_bf16_bits(k)
-        return q, k
+        return to_dtype(q, self.dtype), to_dtype(k, self.dtype)
 
 
 def config4(n_seqs: int = 4096, num_blocks: int = 65536, block_size: int = 16) -> Decode:

@@ -53,7 +53,8 @@ typedef enum {
 
 typedef enum {
     MROPE_F32 = 0,   /* float32 Q/K/cache */
-    MROPE_BF16 = 1   /* bfloat16 Q/K/cache */
+    MROPE_BF16 = 1,  /* bfloat16 Q/K/cache */
+    MROPE_F16 = 2    /* IEEE half Q/K/cache (the pages' engines keep KV state in fp16) */
 } mrope_dtype;
 
 /* seq_flags bits (optional per-sequence output of the plane-deriving calls). */
@@ -142,12 +143,12 @@ mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t
  * planes     [3][plane_stride] int32 (as written by mrope_planes); |plane| < 2^24.
  * theta      rotary base (1e7 for the model), > 0 and finite.
  * Precision: the angle is the fp32 product above; cos, sin and the two products of each output are
- *            double; each output is rounded to nearest-even once to fp32 and, for bf16, once more to
- *            bf16.
+ *            double; each output is rounded to nearest-even once to fp32 and, for bf16 / fp16, once
+ *            more to the 16-bit type.
  * q_out, k_out  NULL: rotate in place (dims >= rot_dim are never read or written).  Otherwise the
  *            full heads are written there, with the same strides as q / k (no aliasing with the
  *            inputs).  Both NULL or both non-NULL (k_out may be NULL when n_k_heads == 0).
- * Alignment: q, k, q_out, k_out 16-byte aligned; strides multiples of 8 (bf16) or 4 (fp32).
+ * Alignment: q, k, q_out, k_out 16-byte aligned; strides multiples of 8 (bf16, fp16) or 4 (fp32).
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,
                          int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,

@@ -158,6 +158,11 @@ def decode(q, k, pos, amount, cache, slot_mapping, block_size: int, theta: float
     return q_out
 
 
+def round_f16(x) -> np.ndarray:
+    """fp32 -> IEEE half bit patterns (uint16), round to nearest even (numpy's IEEE conversion)."""
+    return np.ascontiguousarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
 def round_bf16(x) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
     x = _c(x, np.float32)

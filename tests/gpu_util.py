@@ -19,23 +19,26 @@ def say(*a):
     sys.stdout.flush()
 
 
+TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
 def dev_heads(x: np.ndarray, dtype: str) -> torch.Tensor:
-    """numpy heads (float32 values, or uint16 bf16 bits) -> cuda tensor of the dtype."""
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    """numpy heads (float32 values, or uint16 bit patterns for bf16 / f16) -> cuda tensor of the dtype."""
+    if dtype in ("bf16", "f16"):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(TORCH_DT[dtype]).cuda()
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
 
 
 def host_heads(t: torch.Tensor) -> np.ndarray:
-    """cuda heads -> numpy (uint16 bits for bf16, float32 otherwise)."""
+    """cuda heads -> numpy (uint16 bit patterns for the 16-bit types, float32 otherwise)."""
     t = t.detach().contiguous().cpu()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
 
 
 def as_f32(x: np.ndarray, dtype: str) -> np.ndarray:
-    return synth.bf16_bits_to_f32(x) if dtype == "bf16" else np.asarray(x, np.float32)
+    return synth.to_f32(x, dtype)
 
 
 def i32(a) -> torch.Tensor:
@@ -47,6 +50,8 @@ def compare_heads(got: np.ndarray, x_in: np.ndarray, planes: np.ndarray, dtype: 
     ref = oracle.rotate(as_f32(x_in, dtype), planes, theta)
     if dtype == "bf16":
         ok, info = check_bf16(got, oracle.round_bf16(ref))
+    elif dtype == "f16":
+        ok, info = check_bf16(got, oracle.round_f16(ref))
     else:
         ok, info = check_fp32(got, ref)
     assert ok, f"{what}: {info}"

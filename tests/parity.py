@@ -5,9 +5,9 @@ norm being that of the reference pair (it equals the input pair's norm, a rotati
 the bound never divides by a value near zero; a pair of zeros must come out exactly zero).  Dims
 past the rotary part must be bit-identical.
 
-bf16 gate: the ordered-integer distance between the bf16 bit patterns of got and of the fp32 oracle
-rounded to bf16 is at most 1 (one ulp; -0 and +0 are the same point).  Dims past the rotary part
-bit-identical.
+bf16 / fp16 gate: the ordered-integer distance between the 16-bit patterns of got and of the fp32
+oracle rounded to that type is at most 1 (one ulp; -0 and +0 are the same point).  Dims past the
+rotary part bit-identical.  Both types are sign-magnitude, so one ordering serves both.
 """
 from __future__ import annotations
 
@@ -53,6 +53,10 @@ def bf16_ulp_dist(got_bits, ref_bits) -> np.ndarray:
     return np.abs(_ordered(got_bits) - _ordered(ref_bits))
 
 
+def check_16bit(got_bits, ref_bits, max_ulp: int = BF16_ULP, rot: int = ROT):
+    return check_bf16(got_bits, ref_bits, max_ulp, rot)
+
+
 def check_bf16(got_bits, ref_bits, max_ulp: int = BF16_ULP, rot: int = ROT):
     got_bits = np.asarray(got_bits, np.uint16)
     ref_bits = np.asarray(ref_bits, np.uint16)
@@ -60,4 +64,5 @@ def check_bf16(got_bits, ref_bits, max_ulp: int = BF16_ULP, rot: int = ROT):
     worst = int(d.max()) if d.size else 0
     tail_ok = np.array_equal(got_bits[..., rot:], ref_bits[..., rot:])
     return (worst <= max_ulp and tail_ok), {"max_ulp": worst, "n_off_by_one": int((d == 1).sum()),
+                                           "frac_off_by_one": float((d == 1).mean()) if d.size else 0.0,
                                            "tail_bit_exact": tail_ok}

@@ -12,7 +12,7 @@ import torch
 import canvas_rope_rotary_amd as mr
 import oracle
 from canvas_rope_rotary_amd import synth
-from gpu_util import MARKER, as_f32, compare_heads, dev_heads, expected_flags, host_heads, i32, say
+from gpu_util import MARKER, TORCH_DT, as_f32, compare_heads, dev_heads, expected_flags, host_heads, i32, say
 from parity import check_bf16, check_fp32
 
 pytestmark = pytest.mark.gpu
@@ -91,6 +91,7 @@ def test_config1_prefix_103():
 @pytest.mark.parametrize("seed,dtype,n_seqs,max_len,empty", [
     (101, "bf16", 40, 300, 0.0), (102, "f32", 40, 300, 0.1), (103, "bf16", 300, 90, 0.2),
     (104, "bf16", 12, 3000, 0.0), (105, "f32", 5, 700, 0.0), (106, "bf16", 1, 1, 0.0),
+    (107, "f16", 40, 400, 0.05),
 ])
 def test_fuzz_small_batches(seed, dtype, n_seqs, max_len, empty):
     b = synth.random_batch(seed, n_seqs, max_len=max_len, dtype=dtype, empty_frac=empty)
@@ -476,13 +477,12 @@ def test_bf16_out_of_place_and_wide_plane_stride():
 def test_decode_fp32_and_generic_shapes():
     d = synth.config4(n_seqs=300, num_blocks=512)
     g = synth.rng(91, 5)
-    for dt, nq, nk, D in (("f32", 8, 2, 256), ("bf16", 4, 1, 128), ("f32", 3, 3, 64)):
+    for dt, nq, nk, D in (("f32", 8, 2, 256), ("bf16", 4, 1, 128), ("f32", 3, 3, 64), ("f16", 8, 2, 256)):
         qf = synth.normal(91, 70, d.n_seqs * nq * D).reshape(d.n_seqs, nq, D)
         kf = synth.normal(91, 71, d.n_seqs * nk * D).reshape(d.n_seqs, nk, D)
-        qn = synth.to_bf16_bits(qf) if dt == "bf16" else qf
-        kn = synth.to_bf16_bits(kf) if dt == "bf16" else kf
+        qn, kn = synth.to_dtype(qf, dt), synth.to_dtype(kf, dt)
         q, k = dev_heads(qn, dt), dev_heads(kn, dt)
-        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        tdt = TORCH_DT[dt]
         cache = torch.zeros((512, 16, nk, D), dtype=tdt, device="cuda")
         pos = g.integers(0, 40000, size=d.n_seqs).astype(np.int32)
         amount = np.where(g.uniform(size=d.n_seqs) < 0.5, 58, 0).astype(np.int32)
@@ -522,3 +522,17 @@ def test_workspace_init_recovers_garbage():
     assert int(ws.view.sum().item()) == 0
     pl, st, am, og, fl = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER, workspace=ws)
     _check_scan(b, pl, st, am, og, fl, "after init")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rounding_is_nearest_even(dtype):
+    """The 1-ulp gate alone would pass a kernel that truncates; nearest-even rounding of an accurate
+    result leaves only rare 1-ulp differences (results within ~1e-16 of a rounding boundary)."""
+    b = synth.random_batch(111, 40, max_len=1000, dtype=dtype)
+    qn, kn = b.qk()
+    pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    q = dev_heads(qn, dtype)
+    mr.apply(q, None, pl)
+    info = compare_heads(host_heads(q), qn, epl, dtype, what=f"{dtype} rounding")
+    assert info["frac_off_by_one"] < 1e-3, info

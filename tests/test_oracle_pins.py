@@ -353,3 +353,17 @@ def test_red_arms_fail():
             ya = oracle.rotate(x[sl], arm)
             ok, _ = check_fp32(ya, y[sl])
             assert not ok
+
+
+def test_round_f16_ties_and_range():
+    """fp16 rounding: ties go to even, subnormals and overflow follow IEEE (closed forms)."""
+    x = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -25, 3 * 2 ** -25, 65520.0, 65519.0, -0.0],
+                 np.float32)
+    with np.errstate(over="ignore"):
+        got = oracle.round_f16(x).view(np.float16).astype(np.float64)
+    assert got[0] == 1.0                      # halfway -> even (1.0)
+    assert got[1] == 1 + 2 ** -9              # halfway -> even (odd neighbour below)
+    assert got[2] == 0.0                      # half of the smallest subnormal -> 0 (even)
+    assert got[3] == 2 * 2 ** -24             # 1.5 units of the smallest subnormal -> 2 units (even)
+    assert np.isinf(got[4]) and got[5] == 65504.0
+    assert np.signbit(got[6])
