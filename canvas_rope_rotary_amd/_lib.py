@@ -58,12 +58,12 @@ def load():
     lib.mrope_workspace_init.argtypes = [P, U64, P]
     lib.mrope_workspace_init.restype = ctypes.c_int
     U32 = ctypes.c_uint32
-    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, P, I64, P, P, P, P, P, U64, U32, P]
+    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_planes.restype = ctypes.c_int
     lib.mrope_apply.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, P, I64, F64, P, P, P]
     lib.mrope_apply.restype = ctypes.c_int
     lib.mrope_apply_ids.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
-                                    P, P, I32, I32, P, I64, P, P, P, P, P, U64, U32, P]
+                                    P, P, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_apply_ids.restype = ctypes.c_int
     lib.mrope_decode.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I32, P, P, P, P, I32, I64, I64, I64, I64,
                                  I32, I32, I32, F64, P]
@@ -133,6 +133,8 @@ def _require_cuda(*ts):
 def _heads(t: torch.Tensor, name: str):
     if t.dim() != 3:
         raise ValueError(f"{name} must be [tokens, heads, head_dim]")
+    if t.numel() == 0:  # no elements: strides are free, pass those of a contiguous tensor
+        return t.shape[1] * t.shape[2], t.shape[2], t.shape[1], t.shape[2]
     if t.stride(2) != 1:
         raise ValueError(f"{name}: head_dim must be contiguous")
     return t.stride(0), t.stride(1), t.shape[1], t.shape[2]
@@ -199,14 +201,20 @@ def _workspace(ws, n_tokens, device):
 
 
 def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078, *, out=None, start=None,
-           amount=None, origin=None, seq_flags=None, workspace: Workspace | None = None):
+           amount=None, origin=None, seq_flags=None, pos_offset=None, origin_in=None,
+           workspace: Workspace | None = None):
     """Canvas planes from token ids.  Returns (planes [3, L] int32, start [n], amount [n], origin [n],
-    seq_flags [n]).  cu_seqlens[-1] must equal len(ids)."""
-    dev = _require_cuda(ids, cu_seqlens, out, start, amount, origin, seq_flags)
+    seq_flags [n]).  cu_seqlens[-1] must equal len(ids).  For a later piece of each sequence (chunked
+    prefill, a second turn) pass pos_offset (position of the piece's first token) and origin_in (the
+    previous piece's origin output)."""
+    dev = _require_cuda(ids, cu_seqlens, out, start, amount, origin, seq_flags, pos_offset, origin_in)
     _i32_vec(ids, "ids")
     _i32_vec(cu_seqlens, "cu_seqlens")
     L = ids.numel()
     n = cu_seqlens.numel() - 1
+    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in")):
+        if t is not None:
+            _i32_vec(t, name, n)
     if out is None:
         out = torch.empty((3, L), dtype=torch.int32, device=dev)
     if out.dtype != torch.int32 or out.dim() != 2 or out.shape[0] != 3 or out.shape[1] < L or out.stride(1) != 1:
@@ -216,7 +224,8 @@ def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078,
                                         mk(seq_flags, "seq_flags"))
     ws = _workspace(workspace, L, dev)
     with _on_device(dev):
-        _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), _ptr(out), out.stride(0),
+        _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), _ptr(pos_offset),
+                                   _ptr(origin_in), _ptr(out), out.stride(0),
                                    _ptr(start), _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr,
                                    ws.capacity, ws.next_epoch(), _stream(dev)))
     return out, start, amount, origin, seq_flags
@@ -258,16 +267,20 @@ def apply(q: torch.Tensor, k: torch.Tensor | None, planes_: torch.Tensor, theta:
 
 def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seqlens: torch.Tensor,
               marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
-              origin=None, seq_flags=None, q_out=None, k_out=None, workspace: Workspace | None = None,
-              rot_dim: int = ROT_DIM):
+              origin=None, seq_flags=None, pos_offset=None, origin_in=None, q_out=None, k_out=None,
+              workspace: Workspace | None = None, rot_dim: int = ROT_DIM):
     """Plane derivation fused with the rotation, one launch.  Returns (start, amount, origin,
-    seq_flags, planes_out or None)."""
-    dev = _require_cuda(q, k, ids, cu_seqlens, planes_out, start, amount, origin, seq_flags, q_out, k_out)
+    seq_flags, planes_out or None).  pos_offset / origin_in as in planes()."""
+    dev = _require_cuda(q, k, ids, cu_seqlens, planes_out, start, amount, origin, seq_flags, q_out, k_out,
+                        pos_offset, origin_in)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, q_out, k_out)
     _i32_vec(ids, "ids", q.shape[0])
     _i32_vec(cu_seqlens, "cu_seqlens")
     T = q.shape[0]
     n = cu_seqlens.numel() - 1
+    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in")):
+        if t is not None:
+            _i32_vec(t, name, n)
     ps = 0
     if planes_out is not None:
         if planes_out.dtype != torch.int32 or planes_out.dim() != 2 or planes_out.shape[0] != 3 \
@@ -281,7 +294,7 @@ def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seq
     with _on_device(dev):
         _check(load().mrope_apply_ids(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, float(theta),
                                       _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
-                                      _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
+                                      _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
                                       _ptr(seq_flags), ws.ptr, ws.capacity, ws.next_epoch(), _stream(dev)))
     return start, amount, origin, seq_flags, planes_out
 

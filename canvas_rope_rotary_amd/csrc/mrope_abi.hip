@@ -65,8 +65,8 @@ mrope_status check_heads(void *q, int64_t q_tok, int64_t q_head, int32_t nq, voi
     if (nq < 0 || nk < 0 || nq > kMaxHeads || nk > kMaxHeads)
         return fail(MROPE_ERR_UNSUPPORTED, "head counts must be in [0, %d] (got %d, %d)", kMaxHeads, nq, nk);
     if (n_tokens < 0 || n_tokens > 0x7ffffffe) return fail(MROPE_ERR_ARG, "n_tokens out of range (%lld)", (long long)n_tokens);
-    if (nq > 0 && !q) return fail(MROPE_ERR_ARG, "q is NULL");
-    if (nk > 0 && !k) return fail(MROPE_ERR_ARG, "k is NULL");
+    if (nq > 0 && n_tokens > 0 && !q) return fail(MROPE_ERR_ARG, "q is NULL");
+    if (nk > 0 && n_tokens > 0 && !k) return fail(MROPE_ERR_ARG, "k is NULL");
     if ((q_out == nullptr) != (k_out == nullptr) && nk > 0 && nq > 0)
         return fail(MROPE_ERR_ARG, "q_out and k_out must both be NULL (in place) or both be set");
     if (q_out && nk > 0 && !k_out) return fail(MROPE_ERR_ARG, "k_out is NULL while q_out is set");
@@ -121,9 +121,9 @@ mrope_status check_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, i
     return MROPE_OK;
 }
 
-Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_tokens, int32_t marker, int32_t *planes,
-               int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin, int32_t *flags, void *ws,
-               uint32_t epoch)
+Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_tokens, int32_t marker,
+               const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes, int64_t plane_stride,
+               int32_t *start, int32_t *amount, int32_t *origin, int32_t *flags, void *ws, uint32_t epoch)
 {
     Scan s;
     s.ids = ids;
@@ -137,6 +137,8 @@ Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_
     s.amount = amount;
     s.origin = origin;
     s.flags = flags;
+    s.pos_offset = pos_offset;
+    s.origin_in = origin_in;
     s.workspace = ws;
     s.epoch = epoch;
     return s;
@@ -181,14 +183,14 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream)
 }
 
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
-                          int32_t marker_id, int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount,
-                          int32_t *origin, int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
-                          void *stream)
+                          int32_t marker_id, const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes,
+                          int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin, int32_t *seq_flags,
+                          void *workspace, size_t workspace_bytes, uint32_t epoch, void *stream)
 {
     mrope_status st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes, plane_stride, workspace, workspace_bytes, true);
     if (st != MROPE_OK) return st;
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, planes, plane_stride, start, amount, origin,
-                              seq_flags, workspace, epoch);
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, pos_offset, origin_in, planes, plane_stride,
+                              start, amount, origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (n_tokens == 0) {
@@ -222,7 +224,8 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
                              int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *q_out, void *k_out,
                              const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
-                             int32_t *planes_out, int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
+                             const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
+                             int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
                              int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
                              void *stream)
 {
@@ -232,8 +235,8 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
     if (!(theta > 0.0) || !std::isfinite(theta)) return fail(MROPE_ERR_ARG, "theta must be finite and > 0");
     st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes_out, plane_stride, workspace, workspace_bytes, false);
     if (st != MROPE_OK) return st;
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, planes_out, plane_stride, start, amount,
-                              origin, seq_flags, workspace, epoch);
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, pos_offset, origin_in, planes_out,
+                              plane_stride, start, amount, origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (n_tokens == 0) {

@@ -42,6 +42,8 @@ struct Scan {
     int32_t *amount;     // nullable
     int32_t *origin;     // nullable
     int32_t *flags;      // nullable
+    const int32_t *pos_offset;  // nullable: position of each sequence's first token here (0)
+    const int32_t *origin_in;   // nullable: origin found in earlier pieces, -1 = none
     void *workspace;
     uint32_t epoch;      // tags this launch's status words; 0 = use (and advance) the device counter
 };

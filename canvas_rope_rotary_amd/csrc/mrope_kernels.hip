@@ -40,7 +40,7 @@ constexpr int kAmount = kFrameLen - kExtent;  // amount = start - (O + 9) = 58
 constexpr int32_t kTextStart = 1 << 30;       // text-only prompt: start = 2^30, amount = 0
 constexpr int32_t kNone = 0x7fffffff;         // "no marker"
 
-// Planes of position p; o = in-sequence index of the first marker at or before p, kNone if none.
+// Planes of position p; o = the sequence's canvas origin if it lies at or before p, else kNone.
 __device__ __forceinline__ void canvas_planes(int32_t p, int32_t o, int32_t &t, int32_t &h, int32_t &w)
 {
     if (o == kNone) {
@@ -357,22 +357,31 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
             mm = mm || carry_multi || (carry != kNone && f != kNone);
             f = min(f, carry);
         }
+        // the sequence's origin in its own positions: carried from an earlier piece, else found here
+        const int32_t poff = (j < n && sc.pos_offset) ? sc.pos_offset[j] : 0;
+        const int32_t oin = (j < n && sc.origin_in) ? sc.origin_in[j] : -1;
+        int32_t oseq = f == kNone ? kNone : poff + (int32_t)(f - W);
+        if (oin >= 0) {
+            mm = mm || f != kNone;
+            oseq = oin;
+        }
         if (j < n) {
             const int64_t fin = max<int64_t>(Wn - 1, 0);
-            if (fin >= c0 && fin < c_end) write_scalars(sc, j, f == kNone ? -1 : (int32_t)(f - W), mm, Wn - W);
+            if (fin >= c0 && fin < c_end) write_scalars(sc, j, oseq == kNone ? -1 : oseq, mm, poff + (Wn - W));
         }
         const int64_t w_lo = __shfl(W, 0), w_hi = __shfl(Wn, 63);
         if (s_first == s_last && s_first >= win && s_first - win < 64) {
             // the whole chunk lies in one sequence: no per-token search
             const int r = s_first - win;
-            const int32_t fr = __shfl(f, r);
+            const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r);
             const int64_t sb = __shfl(W, r);
 #pragma unroll
             for (int k = 0; k < kSub; ++k) {
                 const int64_t g = c0 + 64 * k + lane;
                 const bool ok = g < c_end;
+                const int32_t p = offr + (int32_t)(g - sb);
                 int32_t t = 0, h = 0, w = 0;
-                if (ok) canvas_planes((int32_t)(g - sb), (fr != kNone && fr <= g) ? (int32_t)(fr - sb) : kNone, t, h, w);
+                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, t, h, w);
                 sink(k, ok, t, h, w);
             }
         } else {
@@ -383,11 +392,12 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
 #pragma unroll
                 for (int step = 32; step > 0; step >>= 1)
                     if (__shfl(Wn, r + step - 1) <= g) r += step;
-                const int32_t fr = __shfl(f, r);
+                const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r);
                 const int64_t sb = __shfl(W, r);
                 const bool ok = g < c_end && g >= w_lo && g < w_hi;
+                const int32_t p = offr + (int32_t)(g - sb);
                 int32_t t = 0, h = 0, w = 0;
-                if (ok) canvas_planes((int32_t)(g - sb), (fr != kNone && fr <= g) ? (int32_t)(fr - sb) : kNone, t, h, w);
+                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, t, h, w);
                 sink(k, ok, t, h, w);
             }
         }
@@ -815,10 +825,13 @@ __global__ void zero_kernel(uint32_t *p, size_t words)
         p[i] = 0u;
 }
 
+// Scalars when the call has no tokens: every sequence keeps the origin it carries in (if any).
 __global__ void text_scalars_kernel(Scan sc)
 {
     const int32_t s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s < sc.n_seqs) write_scalars(sc, s, -1, false, 0);
+    if (s >= sc.n_seqs) return;
+    const int32_t oin = sc.origin_in ? sc.origin_in[s] : -1;
+    write_scalars(sc, s, oin >= 0 ? oin : -1, false, sc.pos_offset ? sc.pos_offset[s] : 0);
 }
 
 // Device-counter epochs: advance the counter once the scan launch before it has finished.

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MROPE_ABI_VERSION 1
+#define MROPE_ABI_VERSION 2
 
 typedef enum {
     MROPE_OK = 0,
@@ -102,6 +102,14 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  *            (n_tokens is passed explicitly so the host never reads device memory).  Empty
  *            sequences are allowed.
  * marker_id  the <image> token id (248078 for the model's tokenizer).
+ * pos_offset [n_seqs] int32 (nullable = all 0): position of each sequence's first token in this call
+ *            within the whole sequence.  A prompt may be fed in pieces -- prefill in chunks, a second
+ *            turn continuing the first ([zoo] section "Prefill in chunks and a second turn") -- and
+ *            token i of sequence s then sits at position p = pos_offset[s] + i.
+ * origin_in  [n_seqs] int32 (nullable = all -1): the canvas origin an earlier piece found (its
+ *            `origin` output), -1 if none.  The first marker of the whole sequence wins: a marker in
+ *            this piece is used only when origin_in[s] < 0.  Feeding the pieces in order, each with
+ *            the previous piece's origin, gives exactly the planes of one call on the whole sequence.
  * planes     [3][plane_stride] int32 out: row 0 = T, row 1 = H, row 2 = W; plane_stride >= n_tokens.
  *            For position p of a sequence whose first marker is at O:
  *              p < O or no marker     -> (p, p, p)
@@ -111,9 +119,11 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  *              p == O+66              -> (O, O, O)
  *              p >= start == O+67     -> (p-58, p-58, p-58)
  * start, amount  [n_seqs] int32 out (nullable): start = O+67, amount = 58 for an image sequence;
- *            2^30 and 0 for a text-only one.
- * origin     [n_seqs] int32 out (nullable): O, or -1 when the sequence has no marker.
- * seq_flags  [n_seqs] int32 out (nullable): MROPE_SEQ_* bits.
+ *            2^30 and 0 for a text-only one (so far).
+ * origin     [n_seqs] int32 out (nullable): O (a position in the whole sequence), or -1 when the
+ *            sequence has no marker so far.
+ * seq_flags  [n_seqs] int32 out (nullable): MROPE_SEQ_* bits (a marker here when origin_in >= 0
+ *            counts as a second marker; "frame past the end" means past the tokens seen so far).
  * workspace  see mrope_workspace_bytes(n_tokens).
  *
  * epoch      see mrope_workspace_bytes.
@@ -124,9 +134,10 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  * evaluated from its ids), so no tile ever waits on another.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
-                          int32_t marker_id, int32_t *planes, int64_t plane_stride, int32_t *start,
-                          int32_t *amount, int32_t *origin, int32_t *seq_flags, void *workspace,
-                          size_t workspace_bytes, uint32_t epoch, void *stream);
+                          int32_t marker_id, const int32_t *pos_offset, const int32_t *origin_in,
+                          int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount,
+                          int32_t *origin, int32_t *seq_flags, void *workspace, size_t workspace_bytes,
+                          uint32_t epoch, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * mrope_apply -- rotate Q and K heads with given planes ([card] "What it is": interleaved sections).
@@ -166,7 +177,8 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
                              int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *q_out,
                              void *k_out, const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs,
-                             int32_t marker_id, int32_t *planes_out, int64_t plane_stride, int32_t *start,
+                             int32_t marker_id, const int32_t *pos_offset, const int32_t *origin_in,
+                             int32_t *planes_out, int64_t plane_stride, int32_t *start,
                              int32_t *amount, int32_t *origin, int32_t *seq_flags, void *workspace,
                              size_t workspace_bytes, uint32_t epoch, void *stream);
 

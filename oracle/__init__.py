@@ -59,6 +59,8 @@ def _load():
     lib.oracle_frame_scalars.restype = None
     lib.oracle_planes.argtypes = [P, P, i32, i32, P, i64, P, P, P]
     lib.oracle_planes.restype = None
+    lib.oracle_planes_chunk.argtypes = [P, P, i32, i32, P, P, P, i64, P, P, P]
+    lib.oracle_planes_chunk.restype = None
     lib.oracle_inv_freq.argtypes = [f64, i32, P]
     lib.oracle_inv_freq.restype = None
     lib.oracle_plane_of_freq.argtypes = [i32]
@@ -106,6 +108,25 @@ def planes(ids, cu_seqlens, marker_id: int):
     og = np.zeros(n, np.int32)
     _load().oracle_planes(_ptr(ids), _ptr(cu), n, int(marker_id), _ptr(pl), total, _ptr(st), _ptr(am),
                           _ptr(og))
+    return pl, st, am, og
+
+
+def planes_chunk(ids, cu_seqlens, marker_id: int, pos_offset=None, origin_in=None):
+    """Planes of a later piece of each sequence: token i of sequence s sits at pos_offset[s] + i, and
+    origin_in[s] (-1 = none) is the origin found in the earlier pieces.  Returns planes [3, L],
+    start, amount, origin (the sequence's origin so far, -1 = none)."""
+    ids = _c(ids, np.int32)
+    cu = _c(cu_seqlens, np.int32)
+    n = cu.size - 1
+    total = int(cu[-1])
+    po = _c(pos_offset, np.int32) if pos_offset is not None else None
+    oi = _c(origin_in, np.int32) if origin_in is not None else None
+    pl = np.zeros((3, max(total, 1)), np.int32)[:, :total].copy()
+    st = np.zeros(n, np.int32)
+    am = np.zeros(n, np.int32)
+    og = np.zeros(n, np.int32)
+    _load().oracle_planes_chunk(_ptr(ids), _ptr(cu), n, int(marker_id), _ptr(po) if po is not None else None,
+                                _ptr(oi) if oi is not None else None, _ptr(pl), total, _ptr(st), _ptr(am), _ptr(og))
     return pl, st, am, og
 
 

@@ -137,6 +137,41 @@ void oracle_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs
 }
 
 /* ---------------------------------------------------------------------------------------------
+ * Planes of a later piece of each sequence (chunked prefill, a second turn: Core AI model-zoo page,
+ * section "Prefill in chunks and a second turn"; Hugging Face card, section "Measured", the chunked
+ * prefill and second-question paragraphs).  The tokens of sequence s continue its earlier ones:
+ * token i sits at position pos_offset[s] + i.  origin_in[s] is the canvas origin found in the earlier
+ * pieces (-1: none yet); the first marker of the whole sequence wins, so a marker in this piece
+ * counts only when no earlier piece had one.  pos_offset / origin_in may be NULL (0 / -1).
+ * ------------------------------------------------------------------------------------------- */
+void oracle_planes_chunk(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
+                         const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes,
+                         int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin)
+{
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        int32_t b = cu_seqlens[s], n = cu_seqlens[s + 1] - cu_seqlens[s];
+        int32_t off = pos_offset ? pos_offset[s] : 0;
+        int32_t o = (origin_in && origin_in[s] >= 0) ? origin_in[s] : -1;
+        if (o < 0) {
+            int32_t f = oracle_first_marker(ids + b, n, marker_id);
+            if (f >= 0) o = off + f;
+        }
+        int32_t st, am;
+        oracle_frame_scalars(o, &st, &am);
+        start[s] = st;
+        amount[s] = am;
+        if (origin) origin[s] = o;
+        for (int32_t i = 0; i < n; ++i) {
+            int32_t thw[3];
+            canvas_planes_at(off + i, o, st, am, thw);
+            planes[0 * plane_stride + b + i] = thw[0];
+            planes[1 * plane_stride + b + i] = thw[1];
+            planes[2 * plane_stride + b + i] = thw[2];
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
  * Rotary frequencies: inv_freq[j] = 1 / theta^(2j/rot_dim), j = 0 .. rot_dim/2 - 1.
  * theta^(2j/rot_dim) is evaluated in double and rounded once to fp32; the reciprocal is one IEEE
  * fp32 division (the model keeps inv_freq as an fp32 buffer).

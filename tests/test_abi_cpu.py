@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.mrope_abi_version() == 1
+    assert lib.mrope_abi_version() == 2
     for code, text in ((OK, "ok"), (ARG, "invalid argument"), (HIP, "HIP runtime error")):
         assert lib.mrope_status_string(code).decode() == text
     assert lib.mrope_status_string(99).decode() == "unknown status"
@@ -70,8 +70,8 @@ def test_apply_nothing_to_do(lib):
 def _planes(lib, **kw):
     a = dict(ids=A, cu=A, ns=4, n=1000, marker=248078, planes=A, ps=1000, ws=A, wsb=10 ** 6)
     a.update(kw)
-    return lib.mrope_planes(a["ids"], a["cu"], a["ns"], a["n"], a["marker"], a["planes"], a["ps"], None, None, None,
-                            None, a["ws"], a["wsb"], 1, None)
+    return lib.mrope_planes(a["ids"], a["cu"], a["ns"], a["n"], a["marker"], None, None, a["planes"], a["ps"], None,
+                            None, None, None, a["ws"], a["wsb"], 1, None)
 
 
 @pytest.mark.parametrize("kw,code", [

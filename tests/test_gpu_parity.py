@@ -166,6 +166,119 @@ def test_zero_tokens_text_scalars():
     assert st.tolist() == [1 << 30] * 2 and am.tolist() == [0, 0] and og.tolist() == [-1, -1]
 
 
+def _piece_cuts(b, n_pieces, seed):
+    """Per sequence, n_pieces + 1 increasing cut positions from 0 to its length.  Image sequences get
+    cuts at the marker and inside the frame (the row tokens, the closing tokens); one whole round
+    of pieces is empty for every sequence."""
+    g = np.random.default_rng(seed)
+    _, _, _, og = _oracle_planes(b)
+    cuts = []
+    for s in range(b.n_seqs):
+        n = int(b.cu_seqlens[s + 1] - b.cu_seqlens[s])
+        pts = set(g.integers(0, n + 1, size=n_pieces - 2).tolist())
+        if og[s] >= 0:
+            o = int(og[s])
+            pts.add(min(n, o + int(g.choice([0, 1, 9, 33, 65, 66, 67]))))
+        pts = sorted(pts)[: n_pieces - 2]
+        pts = pts + [n] * (n_pieces - 2 - len(pts))
+        c = [0] + sorted(pts)
+        c.insert(2, c[1])  # the empty round
+        cuts.append(c + [n])
+    return np.array(cuts, np.int64)  # [n_seqs, n_pieces + 1]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_chunked_pieces_match_whole_sequences(fused):
+    """Prefill in pieces (chunked prefill, a second turn): each piece passes the position of its
+    first token and the origin the earlier pieces found; planes and rotated Q/K of every piece equal
+    the one-call result on the whole sequences, and the last piece's scalars equal the whole
+    sequences' scalars."""
+    b = synth.random_batch(71, 36, max_len=2600, dtype="bf16", empty_frac=0.05)
+    n_pieces = 5
+    cuts = _piece_cuts(b, n_pieces, 72)
+    epl, est, eam, eog = _oracle_planes(b)
+    eflags = expected_flags(b, eog)
+    qn, kn = b.qk()
+    say(f"case: chunked pieces fused={fused} seqs={b.n_seqs} tokens={b.n_tokens} pieces={n_pieces}")
+    got_pl = np.full((3, b.n_tokens), -7, np.int32)
+    got_q = np.zeros_like(qn)
+    got_k = np.zeros_like(kn)
+    multi_or = np.zeros(b.n_seqs, np.int32)
+    origin_prev = None
+    for k in range(n_pieces):
+        rows = np.concatenate([np.arange(b.cu_seqlens[s] + cuts[s, k], b.cu_seqlens[s] + cuts[s, k + 1])
+                               for s in range(b.n_seqs)]).astype(np.int64)
+        lens = cuts[:, k + 1] - cuts[:, k]
+        cu = np.zeros(b.n_seqs + 1, np.int32)
+        cu[1:] = np.cumsum(lens)
+        ids_k = b.ids[rows].astype(np.int32)
+        off = cuts[:, k].astype(np.int32)
+        oin = None if origin_prev is None else origin_prev
+        if fused:
+            q, kk = dev_heads(qn[rows], "bf16"), dev_heads(kn[rows], "bf16")
+            pl = torch.full((3, rows.size), -7, dtype=torch.int32, device="cuda")
+            st, am, og, fl, _ = mr.apply_ids(q, kk, i32(ids_k), i32(cu), MARKER, planes_out=pl,
+                                             pos_offset=i32(off), origin_in=oin)
+            got_q[rows], got_k[rows] = host_heads(q), host_heads(kk)
+        else:
+            pl, st, am, og, fl = mr.planes(i32(ids_k), i32(cu), MARKER, pos_offset=i32(off), origin_in=oin)
+        pl_h = pl.cpu().numpy()
+        got_pl[:, rows] = pl_h[:, :rows.size]
+        # the piece alone against the oracle's piece rule
+        cpl, cst, cam, cog = oracle.planes_chunk(ids_k, cu, MARKER, off,
+                                                 None if oin is None else oin.cpu().numpy())
+        np.testing.assert_array_equal(pl_h[:, :rows.size], cpl, err_msg=f"piece {k} planes")
+        np.testing.assert_array_equal(st.cpu().numpy(), cst, err_msg=f"piece {k} start")
+        np.testing.assert_array_equal(am.cpu().numpy(), cam, err_msg=f"piece {k} amount")
+        np.testing.assert_array_equal(og.cpu().numpy(), cog, err_msg=f"piece {k} origin")
+        multi_or |= fl.cpu().numpy() & 1
+        origin_prev = og
+    np.testing.assert_array_equal(got_pl, epl, err_msg="pieces vs whole planes")
+    np.testing.assert_array_equal(st.cpu().numpy(), est)
+    np.testing.assert_array_equal(am.cpu().numpy(), eam)
+    np.testing.assert_array_equal(og.cpu().numpy(), eog)
+    np.testing.assert_array_equal(multi_or, eflags & 1, err_msg="multi-marker bit over the pieces")
+    np.testing.assert_array_equal(fl.cpu().numpy() & 2, eflags & 2, err_msg="overrun bit of the last piece")
+    if fused:
+        compare_heads(got_q, qn, epl, "bf16", what="pieces q")
+        compare_heads(got_k, kn, epl, "bf16", what="pieces k")
+
+
+def test_second_turn_long_pieces():
+    """A second turn after a long first turn.  Sequence 0 (100,000 tokens, marker at 85,000): a
+    text-only first piece of 30,000, then 70,000 tokens whose marker sits 55,000 deep (look-back
+    across many chunks, with a position offset).  Sequence 1 (60,000 tokens, marker at 45,000): a
+    first piece of 50,000 holding the frame, then a text piece that only carries the origin in."""
+    lens = [100000, 60000]
+    placed = [85000, 45000]
+    g = synth.rng(19, 4)
+    ids = np.concatenate([synth.prompt_ids(g, n, o) for n, o in zip(lens, placed)])
+    cu = np.zeros(3, np.int32)
+    cu[1:] = np.cumsum(lens)
+    b = synth.Prefill("turns", ids, cu, placed, "bf16", seed=19)
+    epl, est, eam, eog = _oracle_planes(b)
+    say(f"case: two long turns tokens={b.n_tokens}")
+    seen = np.zeros(b.n_tokens, bool)
+    turns = [[(0, 30000), (int(cu[1]), int(cu[1]) + 50000)],
+             [(30000, 100000), (int(cu[1]) + 50000, int(cu[2]))]]
+    og_prev = None
+    for k, segs in enumerate(turns):
+        rows = np.concatenate([np.arange(a, e) for a, e in segs]).astype(np.int64)
+        ccu = np.array([0, segs[0][1] - segs[0][0], rows.size], np.int32)
+        off = np.array([segs[0][0], segs[1][0] - int(cu[1])], np.int32)
+        pl, st, am, og, fl = mr.planes(i32(b.ids[rows]), i32(ccu), MARKER, pos_offset=i32(off),
+                                       origin_in=og_prev)
+        np.testing.assert_array_equal(pl.cpu().numpy(), epl[:, rows], err_msg=f"turn {k} planes")
+        og_prev = og
+        seen[rows] = True
+    assert seen.all()
+    np.testing.assert_array_equal(st.cpu().numpy(), est)
+    np.testing.assert_array_equal(am.cpu().numpy(), eam)
+    np.testing.assert_array_equal(og.cpu().numpy(), eog)
+    assert og.tolist() == [85000, 45000]
+    assert fl.tolist() == [0, 0]
+
+
 def test_origin_zero_negative_planes():
     ids = synth.prompt_ids(synth.rng(3, 9), 200, 0)
     b = synth.Prefill("o0", ids, np.array([0, 200], np.int32), [0], "bf16", seed=3)
@@ -381,8 +494,8 @@ def test_device_epoch_mode_through_c_abi():
         st, am, og, fl = (torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(4))
         p = lambda t: ctypes.c_void_p(t.data_ptr())
         ws.ensure(L)
-        rc = lib.mrope_planes(p(ids), p(cu), n, L, MARKER, p(pl), L, p(st), p(am), p(og), p(fl), ws.ptr, ws.capacity,
-                              0, stream)
+        rc = lib.mrope_planes(p(ids), p(cu), n, L, MARKER, None, None, p(pl), L, p(st), p(am), p(og), p(fl), ws.ptr,
+                              ws.capacity, 0, stream)
         assert rc == 0
         _check_scan(b, pl, st, am, og, fl, f"device epoch call {i}")
     hdr = ws.view[:4].view(torch.int32).item()

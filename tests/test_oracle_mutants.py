@@ -33,6 +33,9 @@ MUTANTS = [
     ("passthrough dims zeroed", "y[d] = x[d];", "y[d] = 0.0f;"),
     ("bf16 rounds half up", "out[i] = (uint16_t)((u + 0x7fffu + lsb) >> 16);", "out[i] = (uint16_t)((u + 0x8000u + 0 * lsb) >> 16);"),
     ("decode ignores amount", "int32_t plane = pos[s] - amount[s];", "int32_t plane = pos[s];"),
+    ("pieces ignore the carried origin", "int32_t o = (origin_in && origin_in[s] >= 0) ? origin_in[s] : -1;",
+     "int32_t o = -1;"),
+    ("pieces ignore the position offset", "int32_t off = pos_offset ? pos_offset[s] : 0;", "int32_t off = 0;"),
 ]
 
 

@@ -367,3 +367,50 @@ def test_round_f16_ties_and_range():
     assert got[3] == 2 * 2 ** -24             # 1.5 units of the smallest subnormal -> 2 units (even)
     assert np.isinf(got[4]) and got[5] == 65504.0
     assert np.signbit(got[6])
+
+
+def test_chunked_pieces_equal_whole_sequences():
+    """Zoo page, "Prefill in chunks and a second turn": a prompt fed in pieces (16-token prefill
+    calls; a second question continuing turn one's state) must see the positions of the whole
+    prompt.  Pieces fed with pos_offset and the carried origin give the whole-sequence planes, for
+    cuts anywhere, inside the frame included."""
+    g = np.random.default_rng(5)
+    b = synth.random_batch(17, 60, max_len=400, min_len=1, text_frac=0.25)
+    whole, wst, wam, wog = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    for trial in range(4):
+        # cut every sequence into 1..4 pieces at random points
+        cuts = []
+        for s in range(b.n_seqs):
+            lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
+            k = int(g.integers(0, 4))
+            pts = sorted(set(int(x) for x in g.integers(lo, hi + 1, size=k)))
+            cuts.append([lo] + [p for p in pts if lo < p < hi] + [hi])
+        n_pieces = max(len(c) - 1 for c in cuts)
+        origin = np.full(b.n_seqs, -1, np.int32)
+        got = np.zeros_like(whole)
+        for piece in range(n_pieces):
+            # one call per round: the next piece of every sequence that still has one
+            seqs = [s for s in range(b.n_seqs) if piece < len(cuts[s]) - 1]
+            ids, cu, off, oin, where = [], [0], [], [], []
+            for s in seqs:
+                a, z = cuts[s][piece], cuts[s][piece + 1]
+                ids.append(b.ids[a:z])
+                cu.append(cu[-1] + z - a)
+                off.append(a - int(b.cu_seqlens[s]))
+                oin.append(origin[s])
+                where.append((a, z))
+            pl, st, am, og = oracle.planes_chunk(np.concatenate(ids), cu, MARKER, off, oin)
+            for i, s in enumerate(seqs):
+                a, z = where[i]
+                got[:, a:z] = pl[:, cu[i]:cu[i + 1]]
+                origin[s] = og[i]
+                if piece == len(cuts[s]) - 2:   # last piece: scalars of the whole sequence
+                    assert (st[i], am[i], og[i]) == (wst[s], wam[s], wog[s])
+        np.testing.assert_array_equal(got, whole)
+
+
+def test_chunk_second_turn_positions():
+    """A second turn after an image prompt: every new token sits past the frame, at p - 58."""
+    pl, st, am, og = oracle.planes_chunk(synth.text_ids(synth.rng(3, 1), 20), [0, 20], MARKER, [110], [6])
+    assert (st[0], am[0], og[0]) == (73, 58, 6)
+    np.testing.assert_array_equal(pl[0], np.arange(110, 130) - 58)
