@@ -1,16 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of the canvas M-RoPE hot path on one MI355X.
 
-A step is one pass of the whole prefill path over one batch: mrope_planes (token ids -> first
-marker per sequence -> (T, H, W) planes, start, amount) and mrope_apply (rotate-half of the first
-64 dims of Q [L, 8, 256] and K [L, 2, 256], bf16, in place).  Workload: 64 image prompts of 4096
-tokens (262,144 tokens), <image> at O ~ U{0..512}, Q/K ~ N(0, 1) from a fixed seed, inputs resident
-in HBM before the timed region.
+A step is one pass of the whole prefill path over one batch, in one launch: mrope_apply_ids (token
+ids -> first marker per sequence -> (T, H, W) planes, start, amount -> rotate-half of the first 64
+dims of Q [L, 8, 256] and K [L, 2, 256], bf16, in place).  Workload: 64 image prompts of 4096 tokens
+(262,144 tokens), <image> at O ~ U{0..512}, Q/K ~ N(0, 1) from a fixed seed, inputs resident in HBM
+before the timed region.
 
-Prints one JSON line: tokens/s over the timed steps, the roofline of the dominant kernel
-(mrope_apply: algorithmic bytes / mean time of back-to-back launches from HIP events on its stream,
-against 8 TB/s),
-and the CPU oracle timed on this host over the same workload.
+Prints one JSON line: tokens/s over the timed steps; the roofline of the step's kernel
+(mrope_apply_ids: algorithmic bytes / mean time of back-to-back launches from HIP events on its
+stream, against 8 TB/s) and, beside it, that of the two-launch form's rotary kernel mrope_apply with
+planes given; and the CPU oracle timed on this host over the same workload.
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "canvas M-RoPE Q+K tokens/sec and achieved HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "mrope_apply_64x4096_bf16_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "rotary_kernels_64x4096_bf16_counters.json")
 
 
 def log(*a):
@@ -156,16 +156,17 @@ def extras(args, dev, timed):
     return out
 
 
-def traffic_from_counters(launch_tokens: int):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, scaled by the
-    copy-kernel calibration -- only if it was taken on the current kernel sources."""
+def traffic_from_counters(kernel: str, launch_tokens: int):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    scaled by the copy-kernel calibration -- only if it was taken on the current kernel sources."""
     try:
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
         return None
     if c.get("kernel_source_sha256") != kernel_source_hash() or c.get("tokens") != launch_tokens:
         return None
-    return int(c["hbm_bytes_per_launch"])
+    k = c.get("kernels", {}).get(kernel)
+    return int(k["hbm_bytes_per_launch"]) if k else None
 
 
 def cpu_baseline(b, qn, kn, min_seconds: float = 10.0, max_passes: int = 8):
@@ -249,9 +250,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        mr.planes(ids, cu, synth.IMAGE_ID, out=planes, start=start, amount=amount, origin=origin,
-                  seq_flags=flags, workspace=ws)
-        mr.apply(q, k, planes)
+        mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, start=start, amount=amount, origin=origin, seq_flags=flags,
+                     workspace=ws)
 
     def timed(fn, reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -274,29 +274,31 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = step_s * 1e3
 
-    # the dominant kernel alone, `steps` back-to-back launches on the same stream (HIP events)
-    apply_mean_s = timed(lambda: mr.apply(q, k, planes), args.steps)
+    # each kernel alone, `steps` back-to-back launches on the same stream (HIP events): the step's
+    # kernel again, and the two-launch form (mrope_planes, then mrope_apply on its planes)
+    fused_s = timed(step, args.steps)
     planes_us = timed(lambda: mr.planes(ids, cu, synth.IMAGE_ID, out=planes, start=start, amount=amount,
                                         origin=origin, seq_flags=flags, workspace=ws), args.steps) * 1e6
+    apply_mean_s = timed(lambda: mr.apply(q, k, planes), args.steps)
     log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us/step); "
-        f"mrope_apply {apply_mean_s * 1e6:.1f} us, mrope_planes {planes_us:.1f} us per launch")
+        f"mrope_apply_ids {fused_s * 1e6:.1f} us, mrope_planes {planes_us:.1f} us, mrope_apply "
+        f"{apply_mean_s * 1e6:.1f} us per launch")
 
     cold = None
     if args.cold:
         # one launch after streaming 1 GiB through the caches (read only, so no dirty lines are left
         # to write back): the HBM-only figure, without hits in the 256 MB memory-side cache
         sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        ts = []
+        ts, tf = [], []
         for _ in range(10):
             sweep.sum()
             torch.cuda.synchronize()
             ts.append(timed(lambda: mr.apply(q, k, planes), 1))
-        cold = sorted(ts)[len(ts) // 2]
+            sweep.sum()
+            torch.cuda.synchronize()
+            tf.append(timed(step, 1))
+        cold = (sorted(ts)[len(ts) // 2], sorted(tf)[len(tf) // 2])
         del sweep
-
-    # the fused one-launch variant on the same batch (context)
-    fused_us = timed(lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, planes_out=None, start=start, amount=amount,
-                                          origin=origin, seq_flags=flags, workspace=ws), args.steps) * 1e6
 
     # plain device-to-device copy of 1 GiB: the practical streaming ceiling on this machine (context)
     src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
@@ -305,8 +307,10 @@ def main():
     copy_gbs = 2 * src.numel() * 2 / timed(lambda: dst.copy_(src), 10) / 1e9
     del src, dst
 
+    fb = algorithmic_bytes_fused(L)
+    achieved = fb / fused_s / 1e9
     ab = algorithmic_bytes_apply(L)
-    achieved = ab / apply_mean_s / 1e9
+    a_achieved = ab / apply_mean_s / 1e9
     out = {
         "metric": METRIC,
         "value": L / step_s,
@@ -323,21 +327,26 @@ def main():
         "angle_dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "64 image prompts x 4096 tokens, bf16: planes from int32 ids + in-place "
-                               "rotary of Q[262144,8,256] and K[262144,2,256]",
+                               "rotary of Q[262144,8,256] and K[262144,2,256], one launch",
                    "tokens": L, "seqs": b.n_seqs, "q_heads": 8, "k_heads": 2, "head_dim": 256, "rot_dim": 64,
                    "theta": 1e7, "sections": [11, 11, 10]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(L),
-                     "kernel": "mrope_apply", "algorithmic_bytes_per_launch": ab,
-                     "mean_launch_us": apply_mean_s * 1e6},
-        "kernels_us": {"mrope_planes": planes_us, "mrope_apply": apply_mean_s * 1e6, "mrope_apply_ids": fused_us},
-        "fused_gbs": algorithmic_bytes_fused(L) / (fused_us / 1e6) / 1e9,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters("mrope_apply_ids", L),
+                     "kernel": "mrope_apply_ids", "algorithmic_bytes_per_launch": fb,
+                     "mean_launch_us": fused_s * 1e6},
+        "apply_roofline": {"bound": "hbm", "achieved": a_achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": a_achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters("mrope_apply", L),
+                           "kernel": "mrope_apply", "algorithmic_bytes_per_launch": ab,
+                           "mean_launch_us": apply_mean_s * 1e6},
+        "kernels_us": {"mrope_apply_ids": fused_s * 1e6, "mrope_planes": planes_us, "mrope_apply": apply_mean_s * 1e6},
+        "two_launch_tokens_per_s": L / (planes_us / 1e6 + apply_mean_s),
         "planes_gbs": algorithmic_bytes_planes(L) / (planes_us / 1e6) / 1e9,
         "copy_ceiling_gbs": copy_gbs,
     }
     if cold is not None:
-        out["apply_cold"] = {"us": cold * 1e6, "gbs": ab / cold / 1e9,
-                             "note": "median single launch after a 1 GiB read sweep (no memory-side cache hits)"}
+        out["cold"] = {"mrope_apply_us": cold[0] * 1e6, "mrope_apply_gbs": ab / cold[0] / 1e9,
+                       "mrope_apply_ids_us": cold[1] * 1e6, "mrope_apply_ids_gbs": fb / cold[1] / 1e9,
+                       "note": "median single launch after a 1 GiB read sweep (no memory-side cache hits)"}
     if args.extras:
         out["extras"] = extras(args, dev, timed)
     if not args.no_cpu_baseline:

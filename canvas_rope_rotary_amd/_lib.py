@@ -177,6 +177,8 @@ class Workspace:
         need = int(load().mrope_workspace_bytes(int(n_tokens)))
         if self.buf is not None and need <= self.capacity:
             return self
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(f"workspace too small for {n_tokens} tokens; size it before graph capture")
         buf = torch.zeros(need + 256, dtype=torch.uint8, device=self.device)
         off = (-buf.data_ptr()) % 256
         self.buf = buf
@@ -193,10 +195,16 @@ _default_ws: dict = {}
 
 
 def _workspace(ws, n_tokens, device):
+    """The caller's workspace, else one kept per (device, stream): calls on one stream are ordered,
+    so they may share it; calls on different streams never do.  Under graph capture pass one made
+    before the capture."""
     if ws is None:
-        ws = _default_ws.get(device)
+        key = (device, torch.cuda.current_stream(device).cuda_stream)
+        ws = _default_ws.get(key)
         if ws is None:
-            ws = _default_ws[device] = Workspace(n_tokens, device)
+            if torch.cuda.is_current_stream_capturing():
+                raise RuntimeError("pass workspace= to calls captured in a graph (a Workspace made before capture)")
+            ws = _default_ws[key] = Workspace(n_tokens, device)
     return ws.ensure(n_tokens)
 
 
@@ -251,8 +259,9 @@ def _qk_args(q, k, q_out, k_out):
 
 def apply(q: torch.Tensor, k: torch.Tensor | None, planes_: torch.Tensor, theta: float = 1e7, *, q_out=None,
           k_out=None, rot_dim: int = ROT_DIM):
-    """Rotate Q and K ([T, heads, head_dim], bf16 or fp32) with planes [3, >= T] int32.  In place
-    unless q_out / k_out are given (then full heads are written there).  Returns (q, k) as written."""
+    """Rotate Q and K ([T, heads, head_dim], bf16 / fp16 / fp32) with planes [3, >= T] int32.  In
+    place unless q_out / k_out are given (then full heads are written there).  Returns (q, k) as
+    written."""
     dev = _require_cuda(q, k, planes_, q_out, k_out)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, q_out, k_out)
     T = q.shape[0]

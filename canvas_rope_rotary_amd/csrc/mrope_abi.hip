@@ -178,7 +178,8 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream)
 {
     if (!workspace) return fail(MROPE_ERR_WORKSPACE, "workspace is NULL");
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(MROPE_ERR_WORKSPACE, "workspace not 256-byte aligned");
-    if (bytes < kWsHeaderBytes || bytes % 8) return fail(MROPE_ERR_WORKSPACE, "workspace size must be >= 256 and a multiple of 8");
+    if (bytes < kWsHeaderBytes || bytes % 8)
+        return fail(MROPE_ERR_WORKSPACE, "workspace size must be >= %zu and a multiple of 8", kWsHeaderBytes);
     return hip_status(launch_workspace_init(workspace, bytes, static_cast<hipStream_t>(stream)), "mrope_workspace_init");
 }
 

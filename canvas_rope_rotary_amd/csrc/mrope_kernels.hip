@@ -530,20 +530,49 @@ __device__ __forceinline__ Raw8<IO> swap_pair(const Raw8<IO> &r)
     return o;
 }
 
-// (cos, sign*sin) of frequencies 8m .. 8m+7 for lane pair m.  Each lane evaluates four of them
-// (half 0: 8m..8m+3, half 1: 8m+4..8m+7) and the pair swaps results.  ss = -sin on the x_j side
-// and +sin on the x_{j+32} side, so every output is y = own*c + partner*ss.
-__device__ __forceinline__ void pair_sincos(const Rotary &rot, int m, int half, int32_t pt, int32_t ph, int32_t pw,
-                                            double (&c)[8], double (&ss)[8])
+// The four inverse frequencies a lane evaluates (half 0: 8m..8m+3, half 1: 8m+4..8m+7) and the
+// plane each reads, 2 bits apiece.  Taken from the kernel arguments once, before the token loop, by
+// uniform selects: a lane-dependent index into the argument block would be a vector memory load
+// inside the loop, and the wait for it would also wait for the prefetched Q/K loads.
+struct LaneFreq {
+    float f[4];
+    uint32_t sel;
+    int half;
+};
+
+__device__ __forceinline__ LaneFreq lane_freq(const Rotary &rot, int m, int half)
 {
-    const int j0 = 8 * m + 4 * half;
-    const uint32_t sel = (uint32_t)(rot.plane_sel >> (2 * j0));
+    LaneFreq r;
+    const int q = 2 * m + half;  // j0 = 4q
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float x = rot.inv_freq[4 * t + i];
+            asm volatile("" : "+s"(x));  // keep the selects: no indexed reload of the argument block
+            v = q == t ? x : v;
+        }
+        r.f[i] = v;
+    }
+    r.sel = (uint32_t)(rot.plane_sel >> (8 * q));
+    r.half = half;
+    return r;
+}
+
+// (cos, sign*sin) of frequencies 8m .. 8m+7 for lane pair m.  Each lane evaluates its four and the
+// pair swaps results.  ss = -sin on the x_j side and +sin on the x_{j+32} side, so every output is
+// y = own*c + partner*ss.
+__device__ __forceinline__ void pair_sincos(const LaneFreq &lf, int32_t pt, int32_t ph, int32_t pw, double (&c)[8],
+                                            double (&ss)[8])
+{
+    const int half = lf.half;
     double oc[4], os[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t pl = (sel >> (2 * i)) & 3u;
+        const uint32_t pl = (lf.sel >> (2 * i)) & 3u;
         const int32_t pos = pl == 1u ? ph : (pl == 2u ? pw : pt);
-        const float a = (float)pos * rot.inv_freq[j0 + i];
+        const float a = (float)pos * lf.f[i];
         sincos_angle(a, &os[i], &oc[i]);
     }
 #pragma unroll
@@ -627,9 +656,13 @@ constexpr int kBlock = 256;                 // 4 waves
 constexpr int kLanesPerTok = 8;
 constexpr int kTokPerBlock = kBlock / kLanesPerTok;
 
-// Fixed head counts: a grid-stride loop over tokens (the grid is sized to the chip by the host).
-// Each 8-lane group prefetches the next token's planes and head chunks before it rotates and
-// stores the current one, so loads stay in flight while the sincos and rotation math runs.
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Fixed head counts: a grid-stride loop over 8-token groups, one group per wave per step (the grid
+// is sized to the chip by the host).  Each 8-lane group prefetches its next token's planes and head
+// chunks before it rotates and stores the current one, so loads stay in flight while the sincos
+// and rotation math runs.  Control flow is wave-uniform.
 template <int IO, int NQ, int NK>
 __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
                                                        int64_t ps)
@@ -637,28 +670,44 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
     const int tid = threadIdx.x;
     const int l = tid & 7, m = l >> 1, half = l & 1;
     const int e0 = 32 * half + 8 * m;
+    const LaneFreq lf = lane_freq(rot, m, half);
     const int64_t stride = (int64_t)gridDim.x * kTokPerBlock;
-    int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 3);
-    if (g >= hd.n_tokens) return;   // the eight lanes of a token leave together
-    int32_t pt = planes[g], ph = planes[ps + g], pw = planes[2 * ps + g];
+    int64_t G = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 6) * 8;  // first token of the wave's group
+    const int sub = (tid & 63) >> 3;
+    int64_t g = G + sub;
+    bool ok = g < hd.n_tokens;
+    int32_t pt = 0, ph = 0, pw = 0;
     Raw8<IO> qv[NQ], kv[NK];
-    load_token_fixed<IO, NQ, NK>(hd, g, e0, qv, kv);
-    while (true) {
-        const int64_t gn = g + stride;
-        const bool more = gn < hd.n_tokens;
+    if (ok) {
+        pt = planes[g];
+        ph = planes[ps + g];
+        pw = planes[2 * ps + g];
+        load_token_fixed<IO, NQ, NK>(hd, g, e0, qv, kv);
+    }
+    // Let the first token's loads land here.  Otherwise the compiler's wait counting, merging the
+    // loop entry with the back edge, takes them as possibly in flight inside the loop and makes
+    // every store wait for the matching prefetch load of the next token.
+    wait_vm_all();
+    while (G < hd.n_tokens) {
+        const int64_t Gn = G + stride;
+        const int64_t gn = Gn + sub;
+        const bool okn = gn < hd.n_tokens;
         int32_t nt = 0, nh = 0, nw = 0;
         Raw8<IO> qn[NQ], kn[NK];
-        if (more) {
+        if (okn) {
             nt = planes[gn];
             nh = planes[ps + gn];
             nw = planes[2 * ps + gn];
             load_token_fixed<IO, NQ, NK>(hd, gn, e0, qn, kn);
         }
-        double c[8], ss[8];
-        pair_sincos(rot, m, half, pt, ph, pw, c, ss);
-        rotate_token_fixed<IO, NQ, NK>(hd, g, e0, l, c, ss, qv, kv);
-        if (!more) break;
+        if (ok) {
+            double c[8], ss[8];
+            pair_sincos(lf, pt, ph, pw, c, ss);
+            rotate_token_fixed<IO, NQ, NK>(hd, g, e0, l, c, ss, qv, kv);
+        }
+        G = Gn;
         g = gn;
+        ok = okn;
         pt = nt;
         ph = nh;
         pw = nw;
@@ -680,7 +729,7 @@ __global__ __launch_bounds__(kBlock) void apply_any_kernel(Heads hd, Rotary rot,
     const int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 3);
     if (g >= hd.n_tokens) return;
     double c[8], ss[8];
-    pair_sincos(rot, m, half, planes[g], planes[ps + g], planes[2 * ps + g], c, ss);
+    pair_sincos(lane_freq(rot, m, half), planes[g], planes[ps + g], planes[2 * ps + g], c, ss);
     rotate_token_any<IO>(hd, g, e0, l, c, ss);
 }
 
@@ -713,6 +762,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     const int lane = tid & 63;
     const int l = tid & 7, m = l >> 1, half = l & 1;
     const int e0 = 32 * half + 8 * m;
+    const LaneFreq lf = lane_freq(rot, m, half);
     const int64_t chunk = blockIdx.x;
     const int64_t c0 = chunk * kChunk;
     const int64_t c_end = min<int64_t>(c0 + kChunk, hd.n_tokens);
@@ -746,6 +796,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
                    });
     }
     __syncthreads();
+    wait_vm_all();  // the first token's loads: see apply_kernel
 
     while (g < c_end) {  // the eight lanes of a token stay together
         const int p = (int)(g - c0);
@@ -756,7 +807,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
             Raw8<IO> qn[AQ], kn[AK];
             if (gn < c_end) load_token_fixed<IO, AQ, AK>(hd, gn, e0, qn, kn);
             if (ok) {
-                pair_sincos(rot, m, half, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
+                pair_sincos(lf, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
                 rotate_token_fixed<IO, AQ, AK>(hd, g, e0, l, c, ss, qv, kv);
             }
 #pragma unroll
@@ -765,7 +816,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
             for (int h = 0; h < AK; ++h) kv[h] = kn[h];
         } else {
             if (ok) {
-                pair_sincos(rot, m, half, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
+                pair_sincos(lf, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
                 rotate_token_any<IO>(hd, g, e0, l, c, ss);
             }
         }
@@ -796,7 +847,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot
             const Raw8<IO> own = load8<IO>(isq ? d.q : d.k, off);
             const int32_t plane = d.pos[s] - d.amount[s];
             double c[8], ss[8];
-            pair_sincos(rot, m, half, plane, plane, plane, c, ss);
+            pair_sincos(lane_freq(rot, m, half), plane, plane, plane, c, ss);
             const Raw8<IO> y = rotate_chunk<IO>(own, c, ss);
             if (isq) {
                 store8<IO>(d.q, off, y);

@@ -5,6 +5,8 @@ Planes, start, amount, origin and flags: bit-exact.  Rotated Q/K: fp32 within 2e
 rotary part bit-identical.  Small inputs are compared element by element; the full-size workloads
 in full for planes and on sampled tokens for the rotation.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -481,7 +483,6 @@ def test_workspace_reuse_across_sizes():
 def test_device_epoch_mode_through_c_abi():
     """epoch = 0: the library tags status words from its device counter and advances it after each
     call (one extra one-thread kernel); back-to-back calls with new inputs stay exact."""
-    import ctypes
 
     lib = mr._lib.load()
     ws = mr.Workspace(1 << 15)
@@ -624,7 +625,6 @@ def test_binding_raises_library_status():
 def test_workspace_init_recovers_garbage():
     """A workspace full of garbage words (which can carry any epoch tag) is made safe by
     mrope_workspace_init; results are then exact in both epoch modes."""
-    import ctypes
 
     lib = mr._lib.load()
     b = synth.random_batch(95, 30, max_len=2000)
