@@ -67,7 +67,9 @@ def _load():
     lib.oracle_plane_of_freq.restype = i32
     lib.oracle_rotate.argtypes = [P, i64, i32, i64, i64, i32, i32, P, i64, f64, P, P]
     lib.oracle_rotate.restype = None
-    lib.oracle_decode.argtypes = [P, i32, P, i32, i32, P, P, i32, i32, f64, P, P, P, i32, i64, i64, i64]
+    lib.oracle_decode.argtypes = [P, i32, P, i32, i32, P, P, i32, i32, f64, P, P, P, i32, i64, i64, i64, i64, P, P]
+    lib.oracle_scatter_rows.argtypes = [P, i64, i64, P, i32, i64, P]
+    lib.oracle_scatter_rows.restype = None
     lib.oracle_decode.restype = None
     lib.oracle_round_bf16.argtypes = [P, P, i64]
     lib.oracle_round_bf16.restype = None
@@ -159,9 +161,27 @@ def rotate(x, planes_, theta: float = 1e7, rot_dim: int = 64, want_f64: bool = F
     return (y, y64) if want_f64 else y
 
 
-def decode(q, k, pos, amount, cache, slot_mapping, block_size: int, theta: float = 1e7, rot_dim: int = 64):
+def scatter_paged(rows, slot_mapping, cache):
+    """Paged cache write: rows [n, H, D] go to cache[slot // B, slot % B] of a [blocks, B, H, D]
+    float32 cache (modified in place); slots < 0 or >= blocks * B are skipped."""
+    rows = _c(rows, np.float32)
+    slots = _c(slot_mapping, np.int64)
+    if not (cache.flags["C_CONTIGUOUS"] and cache.dtype == np.float32):
+        raise ValueError("cache must be a C-contiguous float32 array")
+    n = rows.shape[0]
+    row_elems = int(np.prod(rows.shape[1:])) if rows.ndim > 1 else 1
+    if slots.size != n or int(np.prod(cache.shape[2:])) != row_elems:
+        raise ValueError("rows, slot_mapping and cache do not match")
+    _load().oracle_scatter_rows(_ptr(rows), n, row_elems, _ptr(slots), int(cache.shape[1]), int(cache.shape[0]),
+                                _ptr(cache))
+    return cache
+
+
+def decode(q, k, pos, amount, cache, slot_mapping, block_size: int, theta: float = 1e7, rot_dim: int = 64,
+           v=None, v_cache=None):
     """Decode step.  q [S, Hq, D], k [S, Hk, D]; returns rotated q (fp32) and writes the rotated k
-    heads into ``cache`` ([blocks, block_size, Hk, D] float32, modified in place)."""
+    heads into ``cache`` ([blocks, block_size, Hk, D] float32, modified in place); v [S, Hk, D]
+    (optional) goes unrotated into ``v_cache`` (same shape as cache) at the same slots."""
     q = _c(q, np.float32)
     k = _c(k, np.float32)
     S, Hq, D = q.shape
@@ -169,13 +189,21 @@ def decode(q, k, pos, amount, cache, slot_mapping, block_size: int, theta: float
     pos = _c(pos, np.int32)
     amount = _c(amount, np.int32)
     slots = _c(slot_mapping, np.int64)
-    if not (cache.flags["C_CONTIGUOUS"] and cache.dtype == np.float32):
-        raise ValueError("cache must be a C-contiguous float32 array")
-    if cache.shape[1:] != (block_size, Hk, D):
-        raise ValueError("cache must be [blocks, block_size, n_k_heads, head_dim]")
+    for c in (cache, v_cache):
+        if c is None:
+            continue
+        if not (c.flags["C_CONTIGUOUS"] and c.dtype == np.float32):
+            raise ValueError("caches must be C-contiguous float32 arrays")
+        if c.shape[1:] != (block_size, Hk, D):
+            raise ValueError("caches must be [blocks, block_size, n_k_heads, head_dim]")
+    if (v is None) != (v_cache is None) or (v_cache is not None and v_cache.shape != cache.shape):
+        raise ValueError("v and v_cache go together, v_cache shaped like cache")
+    vv = _c(v, np.float32) if v is not None else None
     q_out = np.empty_like(q)
     _load().oracle_decode(_ptr(q), Hq, _ptr(k), Hk, S, _ptr(pos), _ptr(amount), D, rot_dim, float(theta),
-                          _ptr(q_out), _ptr(cache), _ptr(slots), block_size, block_size * Hk * D, D, Hk * D)
+                          _ptr(q_out), _ptr(cache), _ptr(slots), block_size, int(cache.shape[0]),
+                          block_size * Hk * D, D, Hk * D, _ptr(vv) if vv is not None else None,
+                          _ptr(v_cache) if v_cache is not None else None)
     return q_out
 
 

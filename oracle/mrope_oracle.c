@@ -244,19 +244,40 @@ void oracle_rotate(const float *x, int64_t n_tokens, int32_t n_heads, int64_t to
 }
 
 /* ---------------------------------------------------------------------------------------------
+ * Paged cache write.  Row r (row_elems floats: every KV head of one token) goes to the cache slot
+ * slots[r]: block slot / block_size, row slot % block_size of a cache laid out
+ * [num_blocks][block_size][row_elems].  A slot < 0 or >= num_blocks * block_size writes nothing.
+ * The K and V caches are the decoder's state ("How the VLM rides the text-only engine": the
+ * keyCache [6, 1, 2, -1, 256]); the paging is the serving engine's layout, not the pages'.
+ * ------------------------------------------------------------------------------------------- */
+void oracle_scatter_rows(const float *rows, int64_t n_rows, int64_t row_elems, const int64_t *slots,
+                         int32_t block_size, int64_t num_blocks, float *cache)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t slot = slots[r];
+        if (slot < 0 || slot >= num_blocks * (int64_t)block_size) continue;
+        const int64_t block = slot / block_size, within = slot % block_size;
+        memcpy(cache + (block * block_size + within) * row_elems, rows + r * row_elems,
+               sizeof(float) * (size_t)row_elems);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
  * Decode: a generated token of sequence s sits at position pos[s]; every position from start on,
  * generated tokens included, takes p - amount on all three planes (canvas table, last row).
  * q: [n_seqs][n_q_heads][head_dim] dense, rotated into q_out (dense, same shape).
  * k: [n_seqs][n_k_heads][head_dim] dense; the rotated head is written into the paged cache copy at
- * slot_mapping[s] (block = slot / block_size, row = slot % block_size); slot < 0 skips the write.
+ * slot_mapping[s] (block = slot / block_size, row = slot % block_size); a slot < 0 or
+ * >= num_blocks * block_size skips the write.  v (nullable): [n_seqs][n_k_heads][head_dim], written
+ * unrotated into v_cache at the same slot (V takes no position).
  * cache element (block, row, head, d) is at block*cache_block_stride + row*cache_tok_stride +
- * head*cache_head_stride + d (float elements).
+ * head*cache_head_stride + d (float elements), the same for both caches.
  * ------------------------------------------------------------------------------------------- */
 void oracle_decode(const float *q, int32_t n_q_heads, const float *k, int32_t n_k_heads, int32_t n_seqs,
                    const int32_t *pos, const int32_t *amount, int32_t head_dim, int32_t rot_dim,
                    double theta, float *q_out, float *cache, const int64_t *slot_mapping,
-                   int32_t block_size, int64_t cache_block_stride, int64_t cache_head_stride,
-                   int64_t cache_tok_stride)
+                   int32_t block_size, int64_t num_blocks, int64_t cache_block_stride, int64_t cache_head_stride,
+                   int64_t cache_tok_stride, const float *v, float *v_cache)
 {
     float inv_freq[512];
     float y[4096];
@@ -269,13 +290,14 @@ void oracle_decode(const float *q, int32_t n_q_heads, const float *k, int32_t n_
             rotate_head(q + o, q_out + o, NULL, head_dim, rot_dim, thw, inv_freq);
         }
         int64_t slot = slot_mapping[s];
-        if (slot < 0) continue;
+        if (slot < 0 || slot >= num_blocks * (int64_t)block_size) continue;
         int64_t blk = slot / block_size, row = slot % block_size;
         for (int32_t hd = 0; hd < n_k_heads; ++hd) {
-            rotate_head(k + ((int64_t)s * n_k_heads + hd) * head_dim, y, NULL, head_dim, rot_dim, thw,
-                        inv_freq);
-            float *dst = cache + blk * cache_block_stride + row * cache_tok_stride + hd * cache_head_stride;
-            memcpy(dst, y, sizeof(float) * (size_t)head_dim);
+            const int64_t src = ((int64_t)s * n_k_heads + hd) * head_dim;
+            const int64_t dst = blk * cache_block_stride + row * cache_tok_stride + hd * cache_head_stride;
+            rotate_head(k + src, y, NULL, head_dim, rot_dim, thw, inv_freq);
+            memcpy(cache + dst, y, sizeof(float) * (size_t)head_dim);
+            if (v) memcpy(v_cache + dst, v + src, sizeof(float) * (size_t)head_dim);
         }
     }
 }

@@ -36,6 +36,12 @@ MUTANTS = [
     ("pieces ignore the carried origin", "int32_t o = (origin_in && origin_in[s] >= 0) ? origin_in[s] : -1;",
      "int32_t o = -1;"),
     ("pieces ignore the position offset", "int32_t off = pos_offset ? pos_offset[s] : 0;", "int32_t off = 0;"),
+    ("paged block and row swapped", "const int64_t block = slot / block_size, within = slot % block_size;",
+     "const int64_t block = slot % block_size, within = slot / block_size;"),
+    ("paged slot 0 skipped", "if (slot < 0 || slot >= num_blocks * (int64_t)block_size) continue;\n        const int64_t block",
+     "if (slot <= 0 || slot >= num_blocks * (int64_t)block_size) continue;\n        const int64_t block"),
+    ("decode V rotated like K", "if (v) memcpy(v_cache + dst, v + src, sizeof(float) * (size_t)head_dim);",
+     "if (v) rotate_head(v + src, v_cache + dst, NULL, head_dim, rot_dim, thw, inv_freq);"),
 ]
 
 

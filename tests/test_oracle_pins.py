@@ -322,6 +322,47 @@ def test_decode_matches_prefill_planes():
     assert (cache[[0, 1, 3]] == 0).all() and (np.delete(cache[2], 5, axis=0) == 0).all()
 
 
+def test_decode_writes_v_unrotated_at_the_slot():
+    """V takes no position: the decode step copies the new V heads into the V cache at the same
+    slot as K, bit for bit; a slot past the cache end writes nothing."""
+    x = _rand_heads(16, 2, H=3)
+    xk = _rand_heads(17, 2, H=2)
+    xv = _rand_heads(18, 2, H=2)
+    kc = np.zeros((4, 16, 2, 256), np.float32)
+    vc = np.zeros_like(kc)
+    oracle.decode(x, xk, [200, 300], [58, 58], kc, [3 * 16 + 15, 4 * 16], 16, v=xv, v_cache=vc)
+    np.testing.assert_array_equal(vc[3, 15], xv[0])
+    assert np.count_nonzero(vc) == np.count_nonzero(xv[0])
+    assert np.count_nonzero(kc[3, 15]) and np.count_nonzero(kc) == np.count_nonzero(kc[3, 15])
+
+
+def test_scatter_paged_hand_example():
+    """Slot s of a cache of 16-token blocks is block s // 16, row s % 16: slot 37 -> (2, 5), slot 0
+    -> (0, 0), slot 63 -> (3, 15); slots -1 and 64 (= 4 blocks x 16) write nothing."""
+    rows = _rand_heads(19, 5, H=2)
+    cache = np.zeros((4, 16, 2, 256), np.float32)
+    oracle.scatter_paged(rows, [37, 0, -1, 63, 64], cache)
+    np.testing.assert_array_equal(cache[2, 5], rows[0])
+    np.testing.assert_array_equal(cache[0, 0], rows[1])
+    np.testing.assert_array_equal(cache[3, 15], rows[3])
+    touched = np.zeros((4, 16), bool)
+    touched[2, 5] = touched[0, 0] = touched[3, 15] = True
+    assert not cache[~touched].any()
+
+
+def test_scatter_paged_permutation_roundtrip():
+    """Every slot of the cache written once through a random permutation: reading the flat cache
+    back through the same permutation returns the rows (numpy fancy indexing, an independent
+    formulation of the same map)."""
+    g = np.random.default_rng(5)
+    blocks, bs = 6, 8
+    rows = _rand_heads(20, blocks * bs, H=2)
+    perm = g.permutation(blocks * bs)
+    cache = np.zeros((blocks, bs, 2, 256), np.float32)
+    oracle.scatter_paged(rows, perm, cache)
+    np.testing.assert_array_equal(cache.reshape(blocks * bs, 2, 256)[perm], rows)
+
+
 def test_round_bf16_against_torch():
     x = synth.normal(8, 51, 100000)
     x[:4] = [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]   # ties to even
