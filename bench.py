@@ -59,6 +59,13 @@ def algorithmic_bytes_fused(tokens: int, heads: int = 10, rot_dim: int = 64, ele
     return tokens * (heads * rot_dim * elem * 2 + 4)
 
 
+def algorithmic_bytes_fused_kv(tokens: int, q_heads: int = 8, kv_heads: int = 2, head_dim: int = 256,
+                               rot_dim: int = 64, elem: int = 2) -> int:
+    """mrope_apply_ids_kv: Q's rotated dims read and written, K and V heads read whole and written
+    whole into the caches, one int32 id and one int64 slot, per token."""
+    return tokens * (q_heads * rot_dim * elem * 2 + kv_heads * head_dim * elem * 4 + 4 + 8)
+
+
 def graph_timed(fn, reps, warm=2):
     """Mean GPU time per call of `reps` calls captured in one HIP graph and replayed (no host launch
     overhead: for kernels shorter than the binding's per-call host time)."""
@@ -140,6 +147,29 @@ def extras(args, dev, timed):
     del q, k, pl
     torch.cuda.empty_cache()
 
+    # prefill with the paged K/V cache write fused in (64 x 4096 bf16, V from the same seed stream)
+    cfg = synth.config2()
+    log("extras: 64x4096 bf16 with the K/V cache write")
+    qn, kn = cfg.qk()
+    q, k = heads(qn, "bf16"), heads(kn, "bf16")
+    v = torch.randn(k.shape, device=dev).to(torch.bfloat16)
+    ids = torch.from_numpy(cfg.ids).to(dev)
+    cu = torch.from_numpy(cfg.cu_seqlens).to(dev)
+    nb = (cfg.n_tokens + 15) // 16
+    kc = torch.zeros((nb, 16, 2, 256), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    slots = torch.randperm(nb * 16, device=dev)[:cfg.n_tokens].to(torch.int64)
+    ws = mr.Workspace(cfg.n_tokens, dev)
+    kv_us = timed(lambda: mr.apply_ids_kv(q, k, v, ids, cu, kc, vc, slots, synth.IMAGE_ID, workspace=ws),
+                  args.steps) * 1e6
+    out["64x4096-image-bf16-kv-cache"] = {
+        "tokens": cfg.n_tokens, "fused_kv_us": kv_us, "tokens_per_s": cfg.n_tokens / (kv_us / 1e6),
+        "gbs": algorithmic_bytes_fused_kv(cfg.n_tokens) / kv_us / 1e3,
+        "note": "mrope_apply_ids_kv: Q in place, K rotated and V copied into 16-token paged caches at a random "
+                "slot permutation"}
+    del q, k, v, kc, vc
+    torch.cuda.empty_cache()
+
     d = synth.config4()
     log(f"extras: {d.name}")
     qn, kn = d.qk()
@@ -151,6 +181,13 @@ def extras(args, dev, timed):
     dbytes = d.n_seqs * (8 * 64 * 2 * 2 + 2 * 256 * 2 * 2 + 4 + 4 + 8)
     out[d.name] = {"seqs": d.n_seqs, "decode_us": d_us, "tokens_per_s": d.n_seqs / (d_us / 1e6),
                    "gbs": dbytes / d_us / 1e3, "timing": "hip graph replay"}
+    v = torch.randn(k.shape, device=dev).to(torch.bfloat16)
+    vcache = torch.zeros_like(cache)
+    dv_us = graph_timed(lambda: mr.decode(q, k, pos, amount, cache, slots, v=v, v_cache=vcache), args.steps) * 1e6
+    dvbytes = dbytes + d.n_seqs * 2 * 256 * 2 * 2
+    out[d.name + "-with-v"] = {"seqs": d.n_seqs, "decode_us": dv_us, "tokens_per_s": d.n_seqs / (dv_us / 1e6),
+                               "gbs": dvbytes / dv_us / 1e3, "timing": "hip graph replay"}
+    del v, vcache
     del q, k, cache
     torch.cuda.empty_cache()
     return out

@@ -19,7 +19,8 @@ ROT_DIM = 64
 
 # every symbol include/mrope.h declares
 EXPORTS = ("mrope_abi_version", "mrope_status_string", "mrope_last_error", "mrope_workspace_bytes",
-           "mrope_workspace_init", "mrope_planes", "mrope_apply", "mrope_apply_ids", "mrope_decode")
+           "mrope_workspace_init", "mrope_planes", "mrope_apply", "mrope_apply_ids", "mrope_apply_kv",
+           "mrope_apply_ids_kv", "mrope_decode")
 
 
 class MarkerFlags(enum.IntFlag):
@@ -65,7 +66,14 @@ def load():
     lib.mrope_apply_ids.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
                                     P, P, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_apply_ids.restype = ctypes.c_int
-    lib.mrope_decode.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I32, P, P, P, P, I32, I64, I64, I64, I64,
+    cache = [P, P, P, I32, I64, I64, I64, I64]  # k_cache, v_cache, slot_mapping, block_size, num_blocks, strides
+    lib.mrope_apply_kv.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I64, I32, I32, I32, P, I64, F64,
+                                   *cache, P]
+    lib.mrope_apply_kv.restype = ctypes.c_int
+    lib.mrope_apply_ids_kv.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I64, I32, I32, I32, F64,
+                                       P, P, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, *cache, P]
+    lib.mrope_apply_ids_kv.restype = ctypes.c_int
+    lib.mrope_decode.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I32, P, P, *cache,
                                  I32, I32, I32, F64, P]
     lib.mrope_decode.restype = ctypes.c_int
     _lib = lib
@@ -308,32 +316,105 @@ def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seq
     return start, amount, origin, seq_flags, planes_out
 
 
+def _paged(k_cache, v_cache, slot_mapping, v, n_rows: int, nk: int, D: int, dtype, what: str):
+    """Check a paged K/V cache pair and its slots; returns the C arguments (v strides, cache args)."""
+    if k_cache is None or slot_mapping is None:
+        raise ValueError(f"{what}: k_cache and slot_mapping are required")
+    if (v is None) != (v_cache is None):
+        raise ValueError(f"{what}: v and v_cache go together")
+    for c, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if c is None:
+            continue
+        if c.dim() != 4 or c.shape[2] != nk or c.shape[3] != D or c.stride(3) != 1 or c.dtype != dtype:
+            raise ValueError(f"{name} must be [num_blocks, block_size, n_kv_heads, head_dim] of q's dtype")
+    if v_cache is not None and (v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride()):
+        raise ValueError("v_cache must have k_cache's shape and strides")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or slot_mapping.numel() != n_rows \
+            or not slot_mapping.is_contiguous():
+        raise ValueError(f"slot_mapping must be a contiguous int64 [{n_rows}] tensor")
+    vt = vh = 0
+    if v is not None:
+        vt, vh, nv, Dv = _heads(v, "v")
+        if nv != nk or Dv != D or v.shape[0] != n_rows or v.dtype != dtype:
+            raise ValueError("v must match k's shape and dtype")
+    return (vt, vh), (_ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), k_cache.shape[1], k_cache.shape[0],
+                      k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
+
+
+def apply_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, planes_: torch.Tensor, k_cache: torch.Tensor,
+             v_cache: torch.Tensor | None, slot_mapping: torch.Tensor, theta: float = 1e7, *, rot_dim: int = ROT_DIM):
+    """Prefill rotation with the paged K/V cache write: q [T, Hq, D] rotated in place; k [T, Hk, D]
+    rotated and written whole into k_cache [num_blocks, block_size, Hk, D] at slot_mapping (int64
+    [T]; slots outside the cache are skipped); v [T, Hk, D] copied into v_cache.  k and v are not
+    modified.  Returns (q, k_cache, v_cache)."""
+    dev = _require_cuda(q, k, v, planes_, k_cache, v_cache, slot_mapping)
+    dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, None, None)
+    T = q.shape[0]
+    if planes_.dtype != torch.int32 or planes_.dim() != 2 or planes_.shape[0] != 3 or planes_.shape[1] < T \
+            or planes_.stride(1) != 1:
+        raise ValueError("planes must be an int32 [3, >= tokens] tensor with unit column stride")
+    (vt, vh), cache = _paged(k_cache, v_cache, slot_mapping, v, T, nk, D, q.dtype, "apply_kv")
+    with _on_device(dev):
+        _check(load().mrope_apply_kv(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
+                                     _ptr(planes_), planes_.stride(0), float(theta), *cache, _stream(dev)))
+    return q, k_cache, v_cache
+
+
+def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: torch.Tensor, cu_seqlens: torch.Tensor,
+                 k_cache: torch.Tensor, v_cache: torch.Tensor | None, slot_mapping: torch.Tensor,
+                 marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
+                 origin=None, seq_flags=None, pos_offset=None, origin_in=None, workspace: Workspace | None = None,
+                 rot_dim: int = ROT_DIM):
+    """apply_ids with the cache write of apply_kv, in one launch: ids -> planes -> q rotated in
+    place, k rotated into k_cache, v copied into v_cache.  Returns (start, amount, origin,
+    seq_flags, planes_out or None)."""
+    dev = _require_cuda(q, k, v, ids, cu_seqlens, k_cache, v_cache, slot_mapping, planes_out, start, amount, origin,
+                        seq_flags, pos_offset, origin_in)
+    dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, None, None)
+    _i32_vec(ids, "ids", q.shape[0])
+    _i32_vec(cu_seqlens, "cu_seqlens")
+    T = q.shape[0]
+    n = cu_seqlens.numel() - 1
+    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in")):
+        if t is not None:
+            _i32_vec(t, name, n)
+    ps = 0
+    if planes_out is not None:
+        if planes_out.dtype != torch.int32 or planes_out.dim() != 2 or planes_out.shape[0] != 3 \
+                or planes_out.shape[1] < T or planes_out.stride(1) != 1:
+            raise ValueError("planes_out must be an int32 [3, >= tokens] tensor with unit column stride")
+        ps = planes_out.stride(0)
+    (vt, vh), cache = _paged(k_cache, v_cache, slot_mapping, v, T, nk, D, q.dtype, "apply_ids_kv")
+    mk = lambda t, name: _i32_vec(t, name, n) if t is not None else torch.empty(n, dtype=torch.int32, device=dev)
+    start, amount, origin, seq_flags = (mk(start, "start"), mk(amount, "amount"), mk(origin, "origin"),
+                                        mk(seq_flags, "seq_flags"))
+    ws = _workspace(workspace, T, dev)
+    with _on_device(dev):
+        _check(load().mrope_apply_ids_kv(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
+                                         float(theta), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
+                                         _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start),
+                                         _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr, ws.capacity,
+                                         ws.next_epoch(), *cache, _stream(dev)))
+    return start, amount, origin, seq_flags, planes_out
+
+
 def decode(q: torch.Tensor, k: torch.Tensor | None, pos: torch.Tensor, amount: torch.Tensor,
            k_cache: torch.Tensor | None, slot_mapping: torch.Tensor | None, theta: float = 1e7, *,
-           rot_dim: int = ROT_DIM):
+           v: torch.Tensor | None = None, v_cache: torch.Tensor | None = None, rot_dim: int = ROT_DIM):
     """One generated token per sequence: rotate q [S, Hq, D] in place at plane pos - amount; rotate
     k [S, Hk, D] and write it into k_cache [num_blocks, block_size, Hk, D] at slot_mapping (int64,
-    slot < 0 skips)."""
-    dev = _require_cuda(q, k, pos, amount, k_cache, slot_mapping)
+    slots outside the cache are skipped); copy v [S, Hk, D] (optional) into v_cache at the same
+    slots."""
+    dev = _require_cuda(q, k, pos, amount, k_cache, slot_mapping, v, v_cache)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, None, None)
     S = q.shape[0]
     _i32_vec(pos, "pos", S)
     _i32_vec(amount, "amount", S)
     if nk:
-        if k_cache is None or slot_mapping is None:
-            raise ValueError("k_cache and slot_mapping are required with k")
-        if k_cache.dim() != 4 or k_cache.shape[2] != nk or k_cache.shape[3] != D or k_cache.stride(3) != 1 \
-                or k_cache.dtype != q.dtype:
-            raise ValueError("k_cache must be [num_blocks, block_size, n_k_heads, head_dim] of q's dtype")
-        if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or slot_mapping.numel() != S \
-                or not slot_mapping.is_contiguous():
-            raise ValueError("slot_mapping must be a contiguous int64 [S] tensor")
-        nb, bs = k_cache.shape[0], k_cache.shape[1]
-        cb, ct, ch = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+        (vt, vh), cache = _paged(k_cache, v_cache, slot_mapping, v, S, nk, D, q.dtype, "decode")
     else:
-        nb, bs, cb, ct, ch = 0, 1, 0, 0, 0
+        (vt, vh), cache = (0, 0), (None, None, None, 1, 0, 0, 0, 0)
     with _on_device(dev):
-        _check(load().mrope_decode(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, S, _ptr(pos), _ptr(amount),
-                                   _ptr(k_cache), _ptr(slot_mapping), bs, nb, cb, ct, ch, D, rot_dim, dt,
-                                   float(theta), _stream(dev)))
+        _check(load().mrope_decode(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, S, _ptr(pos),
+                                   _ptr(amount), *cache, D, rot_dim, dt, float(theta), _stream(dev)))
     return q, k_cache

@@ -146,6 +146,50 @@ Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_
 
 bool any_scalar(const Scan &s) { return s.start || s.amount || s.origin || s.flags; }
 
+// Paged K/V cache arguments; n_kv_heads == 0 needs none of them.
+mrope_status check_paged(int32_t n_kv_heads, const void *v, int64_t v_tok, int64_t v_head, void *k_cache,
+                         void *v_cache, const int64_t *slots, int32_t block_size, int64_t num_blocks,
+                         int64_t c_block, int64_t c_tok, int64_t c_head, int32_t head_dim, int32_t dtype)
+{
+    if (n_kv_heads == 0) return MROPE_OK;
+    if (!k_cache || !slots) return fail(MROPE_ERR_ARG, "k_cache / slot_mapping is NULL");
+    if ((v == nullptr) != (v_cache == nullptr)) return fail(MROPE_ERR_ARG, "v and v_cache must both be NULL or both set");
+    if (block_size <= 0 || num_blocks < 0) return fail(MROPE_ERR_ARG, "block_size must be > 0 and num_blocks >= 0");
+    if (c_block < 0 || c_tok < 0 || c_head < 0 || v_tok < 0 || v_head < 0) return fail(MROPE_ERR_ARG, "negative stride");
+    if (n_kv_heads > 1 && c_head < head_dim) return fail(MROPE_ERR_ARG, "cache_head_stride < head_dim");
+    if (v && n_kv_heads > 1 && v_head < head_dim) return fail(MROPE_ERR_ARG, "v_head_stride < head_dim");
+    const int64_t vec = dtype == MROPE_F32 ? 4 : 8;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || c_block % vec || c_tok % vec || c_head % vec)
+        return fail(MROPE_ERR_ALIGN, "cache pointers / strides break 16-byte alignment");
+    if (v && (!aligned16(v) || v_tok % vec || v_head % vec))
+        return fail(MROPE_ERR_ALIGN, "v pointer / strides break 16-byte alignment");
+    return MROPE_OK;
+}
+
+PagedKV make_paged(const void *v, int64_t v_tok, int64_t v_head, void *k_cache, void *v_cache, const int64_t *slots,
+                   int32_t block_size, int64_t num_blocks, int64_t c_block, int64_t c_tok, int64_t c_head)
+{
+    PagedKV p{};
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.v = v;
+    p.v_tok = v_tok;
+    p.v_head = v_head;
+    p.slots = slots;
+    p.block_size = block_size > 0 ? block_size : 1;
+    p.num_slots = k_cache ? num_blocks * (int64_t)p.block_size : 0;
+    p.bs_shift = -1;
+    if ((p.block_size & (p.block_size - 1)) == 0) {
+        int sh = 0;
+        while ((1 << sh) < p.block_size) ++sh;
+        p.bs_shift = sh;
+    }
+    p.c_block = c_block;
+    p.c_tok = c_tok;
+    p.c_head = c_head;
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,9 +260,39 @@ mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, i
     const Heads h = make_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
                                n_tokens, head_dim, q_out, k_out);
     (void)hipGetLastError();
-    return hip_status(launch_apply(h, make_rotary(theta), planes, plane_stride, dtype,
+    return hip_status(launch_apply(h, make_rotary(theta), planes, plane_stride, PagedKV{}, dtype,
                                    static_cast<hipStream_t>(stream)),
                       "mrope_apply");
+}
+
+mrope_status mrope_apply_kv(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, const void *k,
+                            int64_t k_tok_stride, int64_t k_head_stride, int32_t n_kv_heads, const void *v,
+                            int64_t v_tok_stride, int64_t v_head_stride, int64_t n_tokens, int32_t head_dim,
+                            int32_t rot_dim, int32_t dtype, const int32_t *planes, int64_t plane_stride, double theta,
+                            void *k_cache, void *v_cache, const int64_t *slot_mapping, int32_t block_size,
+                            int64_t num_blocks, int64_t cache_block_stride, int64_t cache_tok_stride,
+                            int64_t cache_head_stride, void *stream)
+{
+    mrope_status st = check_heads(q, q_tok_stride, q_head_stride, n_q_heads, const_cast<void *>(k), k_tok_stride,
+                                  k_head_stride, n_kv_heads, n_tokens, head_dim, rot_dim, dtype, nullptr, nullptr);
+    if (st != MROPE_OK) return st;
+    if (!(theta > 0.0) || !std::isfinite(theta)) return fail(MROPE_ERR_ARG, "theta must be finite and > 0");
+    st = check_paged(n_kv_heads, v, v_tok_stride, v_head_stride, k_cache, v_cache, slot_mapping, block_size, num_blocks,
+                     cache_block_stride, cache_tok_stride, cache_head_stride, head_dim, dtype);
+    if (st != MROPE_OK) return st;
+    if (n_tokens == 0 || n_q_heads + n_kv_heads == 0) return MROPE_OK;
+    if (!planes) return fail(MROPE_ERR_ARG, "planes is NULL");
+    if (plane_stride < n_tokens) return fail(MROPE_ERR_ARG, "plane_stride < n_tokens");
+    const Heads h = make_heads(q, q_tok_stride, q_head_stride, n_q_heads, const_cast<void *>(k), k_tok_stride,
+                               k_head_stride, n_kv_heads, n_tokens, head_dim, nullptr, nullptr);
+    const PagedKV pc = n_kv_heads > 0 ? make_paged(v, v_tok_stride, v_head_stride, k_cache, v_cache, slot_mapping,
+                                                   block_size, num_blocks, cache_block_stride, cache_tok_stride,
+                                                   cache_head_stride)
+                                      : PagedKV{};
+    (void)hipGetLastError();
+    return hip_status(launch_apply(h, make_rotary(theta), planes, plane_stride, pc, dtype,
+                                   static_cast<hipStream_t>(stream)),
+                      "mrope_apply_kv");
 }
 
 mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,
@@ -246,12 +320,51 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
     }
     const Heads h = make_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
                                n_tokens, head_dim, q_out, k_out);
-    return hip_status(launch_apply_ids(h, make_rotary(theta), sc, dtype, s), "mrope_apply_ids");
+    return hip_status(launch_apply_ids(h, make_rotary(theta), sc, PagedKV{}, dtype, s), "mrope_apply_ids");
+}
+
+mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads,
+                                const void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_kv_heads,
+                                const void *v, int64_t v_tok_stride, int64_t v_head_stride, int64_t n_tokens,
+                                int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, const int32_t *ids,
+                                const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
+                                const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
+                                int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
+                                int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
+                                void *k_cache, void *v_cache, const int64_t *slot_mapping, int32_t block_size,
+                                int64_t num_blocks, int64_t cache_block_stride, int64_t cache_tok_stride,
+                                int64_t cache_head_stride, void *stream)
+{
+    mrope_status st = check_heads(q, q_tok_stride, q_head_stride, n_q_heads, const_cast<void *>(k), k_tok_stride,
+                                  k_head_stride, n_kv_heads, n_tokens, head_dim, rot_dim, dtype, nullptr, nullptr);
+    if (st != MROPE_OK) return st;
+    if (!(theta > 0.0) || !std::isfinite(theta)) return fail(MROPE_ERR_ARG, "theta must be finite and > 0");
+    st = check_paged(n_kv_heads, v, v_tok_stride, v_head_stride, k_cache, v_cache, slot_mapping, block_size, num_blocks,
+                     cache_block_stride, cache_tok_stride, cache_head_stride, head_dim, dtype);
+    if (st != MROPE_OK) return st;
+    st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes_out, plane_stride, workspace, workspace_bytes, false);
+    if (st != MROPE_OK) return st;
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, pos_offset, origin_in, planes_out,
+                              plane_stride, start, amount, origin, seq_flags, workspace, epoch);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (n_tokens == 0) {
+        if (n_seqs > 0 && any_scalar(sc)) return hip_status(launch_text_scalars(sc, s), "mrope_apply_ids_kv");
+        return MROPE_OK;
+    }
+    const Heads h = make_heads(q, q_tok_stride, q_head_stride, n_q_heads, const_cast<void *>(k), k_tok_stride,
+                               k_head_stride, n_kv_heads, n_tokens, head_dim, nullptr, nullptr);
+    const PagedKV pc = n_kv_heads > 0 ? make_paged(v, v_tok_stride, v_head_stride, k_cache, v_cache, slot_mapping,
+                                                   block_size, num_blocks, cache_block_stride, cache_tok_stride,
+                                                   cache_head_stride)
+                                      : PagedKV{};
+    return hip_status(launch_apply_ids(h, make_rotary(theta), sc, pc, dtype, s), "mrope_apply_ids_kv");
 }
 
 mrope_status mrope_decode(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, const void *k,
-                          int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int32_t n_seqs,
-                          const int32_t *pos, const int32_t *amount, void *k_cache, const int64_t *slot_mapping,
+                          int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, const void *v,
+                          int64_t v_tok_stride, int64_t v_head_stride, int32_t n_seqs, const int32_t *pos,
+                          const int32_t *amount, void *k_cache, void *v_cache, const int64_t *slot_mapping,
                           int32_t block_size, int64_t num_blocks, int64_t cache_block_stride, int64_t cache_tok_stride,
                           int64_t cache_head_stride, int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta,
                           void *stream)
@@ -260,18 +373,13 @@ mrope_status mrope_decode(void *q, int64_t q_tok_stride, int64_t q_head_stride, 
                                   k_head_stride, n_k_heads, n_seqs, head_dim, rot_dim, dtype, nullptr, nullptr);
     if (st != MROPE_OK) return st;
     if (!(theta > 0.0) || !std::isfinite(theta)) return fail(MROPE_ERR_ARG, "theta must be finite and > 0");
-    if (n_seqs == 0) return MROPE_OK;
+    if (n_seqs < 0) return fail(MROPE_ERR_ARG, "n_seqs < 0");
+    st = check_paged(n_k_heads, v, v_tok_stride, v_head_stride, k_cache, v_cache, slot_mapping, block_size, num_blocks,
+                     cache_block_stride, cache_tok_stride, cache_head_stride, head_dim, dtype);
+    if (st != MROPE_OK) return st;
+    if (n_seqs == 0 || n_q_heads + n_k_heads == 0) return MROPE_OK;
     if (!pos || !amount) return fail(MROPE_ERR_ARG, "pos / amount is NULL");
-    if (n_k_heads > 0) {
-        if (!k_cache || !slot_mapping) return fail(MROPE_ERR_ARG, "k_cache / slot_mapping is NULL");
-        if (block_size <= 0 || num_blocks < 0) return fail(MROPE_ERR_ARG, "block_size must be > 0 and num_blocks >= 0");
-        if (cache_block_stride < 0 || cache_tok_stride < 0 || cache_head_stride < 0)
-            return fail(MROPE_ERR_ARG, "negative cache stride");
-        const int64_t vec = dtype == MROPE_F32 ? 4 : 8;
-        if (!aligned16(k_cache) || cache_block_stride % vec || cache_tok_stride % vec || cache_head_stride % vec)
-            return fail(MROPE_ERR_ALIGN, "cache pointer / strides break 16-byte alignment");
-    }
-    DecodeArgs d;
+    DecodeArgs d{};
     d.q = q;
     d.k = k;
     d.q_tok = q_tok_stride;
@@ -284,16 +392,11 @@ mrope_status mrope_decode(void *q, int64_t q_tok_stride, int64_t q_head_stride, 
     d.n_seqs = n_seqs;
     d.pos = pos;
     d.amount = amount;
-    d.cache = k_cache;
-    d.slots = slot_mapping;
-    d.block_size = block_size > 0 ? block_size : 1;
-    d.num_slots = n_k_heads > 0 ? num_blocks * (int64_t)block_size : 0;
-    d.c_block = cache_block_stride;
-    d.c_tok = cache_tok_stride;
-    d.c_head = cache_head_stride;
+    if (n_k_heads > 0)
+        d.kv = make_paged(v, v_tok_stride, v_head_stride, k_cache, v_cache, slot_mapping, block_size, num_blocks,
+                          cache_block_stride, cache_tok_stride, cache_head_stride);
     (void)hipGetLastError();
-    return hip_status(launch_decode(d, make_rotary(theta), dtype, static_cast<hipStream_t>(stream)),
-                      "mrope_decode");
+    return hip_status(launch_decode(d, make_rotary(theta), dtype, static_cast<hipStream_t>(stream)), "mrope_decode");
 }
 
 }  // extern "C"

@@ -48,6 +48,20 @@ struct Scan {
     uint32_t epoch;      // tags this launch's status words; 0 = use (and advance) the device counter
 };
 
+// Paged K/V cache destination.  Element (block, row, head, d) of either cache is at
+// block*c_block + row*c_tok + head*c_head + d; slot -> (slot / block_size, slot % block_size).
+struct PagedKV {
+    void *k_cache;          // nullptr: no cache write
+    void *v_cache;          // nullptr together with v
+    const void *v;          // new V heads, element (t, h, d) at t*v_tok + h*v_head + d
+    int64_t v_tok, v_head;
+    const int64_t *slots;   // one per token (prefill) or per sequence (decode)
+    int64_t num_slots;      // num_blocks * block_size; slots outside [0, num_slots) are skipped
+    int64_t c_block, c_tok, c_head;
+    int32_t block_size;
+    int32_t bs_shift;       // log2(block_size) when it is a power of two, else -1
+};
+
 struct DecodeArgs {
     void *q;
     const void *k;
@@ -56,20 +70,18 @@ struct DecodeArgs {
     int32_t n_seqs;
     const int32_t *pos;
     const int32_t *amount;
-    void *cache;
-    const int64_t *slots;
-    int32_t block_size;
-    int64_t num_slots;
-    int64_t c_block, c_tok, c_head;
+    PagedKV kv;
 };
 
 hipError_t launch_workspace_init(void *ws, size_t bytes, hipStream_t stream);
 hipError_t launch_text_scalars(const Scan &s, hipStream_t stream);
 hipError_t launch_planes(const Scan &s, hipStream_t stream);
 // io: the C ABI's dtype code (0 fp32, 1 bf16, 2 fp16)
-hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t plane_stride, int io,
-                        hipStream_t stream);
-hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, int io, hipStream_t stream);
+// kv.k_cache == nullptr: K rotated in place (or into k_out); else K and V go to the paged caches.
+hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t plane_stride,
+                        const PagedKV &kv, int io, hipStream_t stream);
+hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, const PagedKV &kv, int io,
+                            hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, int io, hipStream_t stream);
 
 }  // namespace mrope

@@ -531,29 +531,36 @@ __device__ __forceinline__ Raw8<IO> swap_pair(const Raw8<IO> &r)
 }
 
 // The four inverse frequencies a lane evaluates (half 0: 8m..8m+3, half 1: 8m+4..8m+7) and the
-// plane each reads, 2 bits apiece.  Taken from the kernel arguments once, before the token loop, by
-// uniform selects: a lane-dependent index into the argument block would be a vector memory load
-// inside the loop, and the wait for it would also wait for the prefetched Q/K loads.
+// plane each reads, 2 bits apiece.  kSelect: taken from the kernel arguments by uniform selects, for
+// kernels that read them once before a token loop -- a lane-dependent index into the argument block
+// is a vector memory load, and inside the loop the wait for it would also wait for the prefetched
+// Q/K loads.  Otherwise (decode: one token, no prefetch) that indexed load is the cheaper form: it
+// travels with the data load and needs no registers for all 32 values.
 struct LaneFreq {
     float f[4];
     uint32_t sel;
     int half;
 };
 
+template <bool kSelect>
 __device__ __forceinline__ LaneFreq lane_freq(const Rotary &rot, int m, int half)
 {
     LaneFreq r;
     const int q = 2 * m + half;  // j0 = 4q
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float v = 0.0f;
+        if constexpr (kSelect) {
+            float v = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            float x = rot.inv_freq[4 * t + i];
-            asm volatile("" : "+s"(x));  // keep the selects: no indexed reload of the argument block
-            v = q == t ? x : v;
+            for (int t = 0; t < 8; ++t) {
+                float x = rot.inv_freq[4 * t + i];
+                asm volatile("" : "+s"(x));  // keep the selects: no indexed reload of the argument block
+                v = q == t ? x : v;
+            }
+            r.f[i] = v;
+        } else {
+            r.f[i] = rot.inv_freq[4 * q + i];
         }
-        r.f[i] = v;
     }
     r.sel = (uint32_t)(rot.plane_sel >> (8 * q));
     r.half = half;
@@ -598,15 +605,75 @@ __device__ __forceinline__ Raw8<IO> rotate_chunk(const Raw8<IO> &own, const doub
     return pack8<IO>(y);
 }
 
-// Copy this lane's share of the dims past the rotary part (out-of-place calls only).
+// Copy this lane's share of the 8-element chunks of one head from dim `from` on: src at soff, dst
+// at doff (element offsets of the head's dim 0).  Out-of-place calls and cache writes.
 template <int IO>
-__device__ __forceinline__ void copy_tail(const void *src, void *dst, int64_t off, int head_dim, int l)
+__device__ __forceinline__ void copy_span(const void *src, int64_t soff, void *dst, int64_t doff, int from,
+                                          int head_dim, int l)
 {
-    for (int d = 64 + 8 * l; d < head_dim; d += 64) store8<IO>(dst, off + d, load8<IO>(src, off + d));
+    for (int d = from + 8 * l; d < head_dim; d += 64) store8<IO>(dst, doff + d, load8<IO>(src, soff + d));
 }
 
 __device__ __forceinline__ int64_t q_off(const Heads &hd, int64_t g, int h) { return g * hd.q_tok + h * hd.q_head; }
 __device__ __forceinline__ int64_t k_off(const Heads &hd, int64_t g, int h) { return g * hd.k_tok + h * hd.k_head; }
+
+// ------------------------------------------------------------------ paged K/V cache ------------
+__device__ __forceinline__ bool slot_ok(const PagedKV &pc, int64_t slot) { return slot >= 0 && slot < pc.num_slots; }
+
+// Element offset of head h of a cache slot (0 <= slot < num_slots), the same in both caches.
+__device__ __forceinline__ int64_t cache_off(const PagedKV &pc, int64_t slot, int h)
+{
+    int64_t blk, row;
+    if (pc.bs_shift >= 0) {
+        blk = slot >> pc.bs_shift;
+        row = slot & (int64_t)(pc.block_size - 1);
+    } else {
+        blk = slot / pc.block_size;
+        row = slot - blk * pc.block_size;
+    }
+    return blk * pc.c_block + row * pc.c_tok + h * pc.c_head;
+}
+
+__device__ __forceinline__ int64_t v_off(const PagedKV &pc, int64_t g, int h) { return g * pc.v_tok + h * pc.v_head; }
+
+// The chunks of a token's K and V heads that a cache write copies unchanged (head_dim 256): K dims
+// 64..255 (three 64-dim row segments) and all of V (four), 8 elements per lane per segment.
+template <int IO, int NK>
+struct CopyChunks {
+    Raw8<IO> k[NK][3];
+    Raw8<IO> v[NK][4];
+};
+
+template <int IO, int NK>
+__device__ __forceinline__ void load_copy_chunks(const Heads &hd, const PagedKV &pc, int64_t g, int l,
+                                                 CopyChunks<IO, NK> &cc)
+{
+#pragma unroll
+    for (int h = 0; h < NK; ++h)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) cc.k[h][i] = load8<IO>(hd.k, k_off(hd, g, h) + 64 * (i + 1) + 8 * l);
+    if (pc.v) {
+#pragma unroll
+        for (int h = 0; h < NK; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cc.v[h][i] = load8<IO>(pc.v, v_off(pc, g, h) + 64 * i + 8 * l);
+    }
+}
+
+template <int IO, int NK>
+__device__ __forceinline__ void store_copy_chunks(const PagedKV &pc, int64_t slot, int l, const CopyChunks<IO, NK> &cc)
+{
+#pragma unroll
+    for (int h = 0; h < NK; ++h) {
+        const int64_t o = cache_off(pc, slot, h);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) store8<IO>(pc.k_cache, o + 64 * (i + 1) + 8 * l, cc.k[h][i]);
+        if (pc.v) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) store8<IO>(pc.v_cache, o + 64 * i + 8 * l, cc.v[h][i]);
+        }
+    }
+}
 
 template <int IO, int NQ, int NK>
 __device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int e0, Raw8<IO> (&qv)[NQ],
@@ -618,36 +685,58 @@ __device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int
     for (int h = 0; h < NK; ++h) kv[h] = load8<IO>(hd.k, k_off(hd, g, h) + e0);
 }
 
-template <int IO, int NQ, int NK>
-__device__ __forceinline__ void rotate_token_fixed(const Heads &hd, int64_t g, int e0, int l, const double (&c)[8],
-                                                   const double (&ss)[8], const Raw8<IO> (&qv)[NQ],
-                                                   const Raw8<IO> (&kv)[NK])
+// Rotate one token's chunks and store them: Q in place (or into q_out); K in place (or into k_out),
+// or with KV into the cache slot (nothing when the slot is outside the cache).
+template <int IO, int NQ, int NK, bool KV>
+__device__ __forceinline__ void rotate_token_fixed(const Heads &hd, const PagedKV &pc, int64_t slot, int64_t g, int e0,
+                                                   int l, const double (&c)[8], const double (&ss)[8],
+                                                   const Raw8<IO> (&qv)[NQ], const Raw8<IO> (&kv)[NK])
 {
     void *qo = hd.q_out ? hd.q_out : hd.q;
-    void *ko = hd.k_out ? hd.k_out : hd.k;
 #pragma unroll
     for (int h = 0; h < NQ; ++h) store8<IO>(qo, q_off(hd, g, h) + e0, rotate_chunk<IO>(qv[h], c, ss));
+    if constexpr (KV) {
+        if (slot_ok(pc, slot)) {
 #pragma unroll
-    for (int h = 0; h < NK; ++h) store8<IO>(ko, k_off(hd, g, h) + e0, rotate_chunk<IO>(kv[h], c, ss));
-    if (hd.q_out) {
-        for (int h = 0; h < NQ; ++h) copy_tail<IO>(hd.q, hd.q_out, q_off(hd, g, h), hd.head_dim, l);
-        for (int h = 0; h < NK; ++h) copy_tail<IO>(hd.k, hd.k_out, k_off(hd, g, h), hd.head_dim, l);
+            for (int h = 0; h < NK; ++h) store8<IO>(pc.k_cache, cache_off(pc, slot, h) + e0, rotate_chunk<IO>(kv[h], c, ss));
+        }
+    } else {
+        void *ko = hd.k_out ? hd.k_out : hd.k;
+#pragma unroll
+        for (int h = 0; h < NK; ++h) store8<IO>(ko, k_off(hd, g, h) + e0, rotate_chunk<IO>(kv[h], c, ss));
+        if (hd.q_out) {
+            for (int h = 0; h < NQ; ++h) copy_span<IO>(hd.q, q_off(hd, g, h), hd.q_out, q_off(hd, g, h), 64, hd.head_dim, l);
+            for (int h = 0; h < NK; ++h) copy_span<IO>(hd.k, k_off(hd, g, h), hd.k_out, k_off(hd, g, h), 64, hd.head_dim, l);
+        }
     }
 }
 
-// Any head counts: one head at a time.
+// Any head counts and head_dim: one head at a time.  With a cache (pc.k_cache), K heads go whole
+// into the slot and V heads are copied there; slot is the token's (ignored without a cache).
 template <int IO>
-__device__ __forceinline__ void rotate_token_any(const Heads &hd, int64_t g, int e0, int l, const double (&c)[8],
-                                                 const double (&ss)[8])
+__device__ __forceinline__ void rotate_token_any(const Heads &hd, const PagedKV &pc, int64_t slot, int64_t g, int e0,
+                                                 int l, const double (&c)[8], const double (&ss)[8])
 {
+    const bool to_cache = pc.k_cache != nullptr;
+    const bool cache_ok = to_cache && slot_ok(pc, slot);
     for (int hh = 0; hh < hd.nq + hd.nk; ++hh) {
         const bool isq = hh < hd.nq;
         const int h = isq ? hh : hh - hd.nq;
-        void *src = isq ? hd.q : hd.k;
-        void *dst = isq ? (hd.q_out ? hd.q_out : hd.q) : (hd.k_out ? hd.k_out : hd.k);
+        const void *src = isq ? hd.q : hd.k;
         const int64_t base = isq ? q_off(hd, g, h) : k_off(hd, g, h);
+        if (!isq && to_cache) {
+            if (!cache_ok) continue;
+            const int64_t o = cache_off(pc, slot, h);
+            store8<IO>(pc.k_cache, o + e0, rotate_chunk<IO>(load8<IO>(src, base + e0), c, ss));
+            copy_span<IO>(src, base, pc.k_cache, o, 64, hd.head_dim, l);
+            continue;
+        }
+        void *dst = isq ? (hd.q_out ? hd.q_out : hd.q) : (hd.k_out ? hd.k_out : hd.k);
         store8<IO>(dst, base + e0, rotate_chunk<IO>(load8<IO>(src, base + e0), c, ss));
-        if (hd.q_out) copy_tail<IO>(src, dst, base, hd.head_dim, l);
+        if (hd.q_out) copy_span<IO>(src, base, dst, base, 64, hd.head_dim, l);
+    }
+    if (cache_ok && pc.v) {
+        for (int h = 0; h < hd.nk; ++h) copy_span<IO>(pc.v, v_off(pc, g, h), pc.v_cache, cache_off(pc, slot, h), 0, hd.head_dim, l);
     }
 }
 
@@ -670,7 +759,7 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
     const int tid = threadIdx.x;
     const int l = tid & 7, m = l >> 1, half = l & 1;
     const int e0 = 32 * half + 8 * m;
-    const LaneFreq lf = lane_freq(rot, m, half);
+    const LaneFreq lf = lane_freq<true>(rot, m, half);
     const int64_t stride = (int64_t)gridDim.x * kTokPerBlock;
     int64_t G = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 6) * 8;  // first token of the wave's group
     const int sub = (tid & 63) >> 3;
@@ -703,7 +792,7 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
         if (ok) {
             double c[8], ss[8];
             pair_sincos(lf, pt, ph, pw, c, ss);
-            rotate_token_fixed<IO, NQ, NK>(hd, g, e0, l, c, ss, qv, kv);
+            rotate_token_fixed<IO, NQ, NK, false>(hd, PagedKV{}, -1, g, e0, l, c, ss, qv, kv);
         }
         G = Gn;
         g = gn;
@@ -718,19 +807,57 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
     }
 }
 
-// Any head counts: one token per 8-lane group, one head at a time.
+// One token of the cache-writing path (fixed head counts, head_dim 256): every load of the token --
+// its Q and K rotation chunks, K pass-through and V chunks -- goes out at once, then the math, then
+// the stores (Q in place, K and V into the cache slot, nothing for a slot outside the cache).  No
+// prefetch of the next token: 24 chunks a lane already keep enough bytes in flight per wave, and
+// the registers of a second set would halve the waves per SIMD.
+template <int IO, int NQ, int NK>
+__device__ __forceinline__ void kv_token(const Heads &hd, const PagedKV &pc, const LaneFreq &lf, int64_t g, int e0,
+                                         int l, int32_t pt, int32_t ph, int32_t pw, int64_t slot)
+{
+    Raw8<IO> qv[NQ], kv[NK];
+    CopyChunks<IO, NK> cc;
+    load_token_fixed<IO, NQ, NK>(hd, g, e0, qv, kv);
+    load_copy_chunks<IO, NK>(hd, pc, g, l, cc);
+    double c[8], ss[8];
+    pair_sincos(lf, pt, ph, pw, c, ss);
+    rotate_token_fixed<IO, NQ, NK, true>(hd, pc, slot, g, e0, l, c, ss, qv, kv);
+    if (slot_ok(pc, slot)) store_copy_chunks<IO, NK>(pc, slot, l, cc);
+}
+
+// mrope_apply_kv, fixed head counts: a grid-stride loop over 8-token groups like apply_kernel.
+template <int IO, int NQ, int NK>
+__global__ __launch_bounds__(kBlock) void apply_kv_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
+                                                          int64_t ps, PagedKV pc)
+{
+    const int tid = threadIdx.x;
+    const int l = tid & 7, m = l >> 1, half = l & 1;
+    const int e0 = 32 * half + 8 * m;
+    const LaneFreq lf = lane_freq<true>(rot, m, half);
+    const int64_t stride = (int64_t)gridDim.x * kTokPerBlock;
+    const int sub = (tid & 63) >> 3;
+    for (int64_t G = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 6) * 8; G < hd.n_tokens; G += stride) {
+        const int64_t g = G + sub;
+        if (g < hd.n_tokens)
+            kv_token<IO, NQ, NK>(hd, pc, lf, g, e0, l, planes[g], planes[ps + g], planes[2 * ps + g], pc.slots[g]);
+    }
+}
+
+// Any head counts and head_dim: one token per 8-lane group, one head at a time.
 template <int IO>
 __global__ __launch_bounds__(kBlock) void apply_any_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
-                                                           int64_t ps)
+                                                           int64_t ps, PagedKV pc)
 {
     const int tid = threadIdx.x;
     const int l = tid & 7, m = l >> 1, half = l & 1;
     const int e0 = 32 * half + 8 * m;
     const int64_t g = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 3);
     if (g >= hd.n_tokens) return;
+    const int64_t slot = pc.k_cache ? pc.slots[g] : -1;
     double c[8], ss[8];
-    pair_sincos(lane_freq(rot, m, half), planes[g], planes[ps + g], planes[2 * ps + g], c, ss);
-    rotate_token_any<IO>(hd, g, e0, l, c, ss);
+    pair_sincos(lane_freq<false>(rot, m, half), planes[g], planes[ps + g], planes[2 * ps + g], c, ss);
+    rotate_token_any<IO>(hd, pc, slot, g, e0, l, c, ss);
 }
 
 // One wave per chunk, four chunks per workgroup.
@@ -752,9 +879,10 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
 
 // Fused: one chunk per workgroup.  Every lane issues the Q/K loads of its first token, wave 0 scans
 // the chunk into LDS meanwhile, then the workgroup rotates the chunk 32 tokens at a time, each
-// 8-lane group prefetching its next token before rotating the current one.
-template <int IO, int NQ, int NK>
-__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc)
+// 8-lane group prefetching its next token before rotating the current one.  KV as in apply_kernel
+// (fixed head counts); the generic path writes the cache when pc.k_cache is set.
+template <int IO, int NQ, int NK, bool KV>
+__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, PagedKV pc)
 {
     __shared__ int32_t s_pl[3][kChunk];
     __shared__ uint64_t s_ok[kSub];
@@ -762,7 +890,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     const int lane = tid & 63;
     const int l = tid & 7, m = l >> 1, half = l & 1;
     const int e0 = 32 * half + 8 * m;
-    const LaneFreq lf = lane_freq(rot, m, half);
+    const LaneFreq lf = lane_freq<true>(rot, m, half);
     const int64_t chunk = blockIdx.x;
     const int64_t c0 = chunk * kChunk;
     const int64_t c_end = min<int64_t>(c0 + kChunk, hd.n_tokens);
@@ -771,7 +899,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
 
     int64_t g = c0 + (tid >> 3);
     Raw8<IO> qv[AQ], kv[AK];
-    if constexpr (kFixed) {
+    if constexpr (kFixed && !KV) {
         if (g < c_end) load_token_fixed<IO, AQ, AK>(hd, g, e0, qv, kv);
     }
 
@@ -803,12 +931,14 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         const bool ok = (s_ok[p >> 6] >> (p & 63)) & 1u;
         const int64_t gn = g + kTokPerBlock;
         double c[8], ss[8];
-        if constexpr (kFixed) {
+        if constexpr (kFixed && KV) {
+            if (ok) kv_token<IO, AQ, AK>(hd, pc, lf, g, e0, l, s_pl[0][p], s_pl[1][p], s_pl[2][p], pc.slots[g]);
+        } else if constexpr (kFixed) {
             Raw8<IO> qn[AQ], kn[AK];
             if (gn < c_end) load_token_fixed<IO, AQ, AK>(hd, gn, e0, qn, kn);
             if (ok) {
                 pair_sincos(lf, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
-                rotate_token_fixed<IO, AQ, AK>(hd, g, e0, l, c, ss, qv, kv);
+                rotate_token_fixed<IO, AQ, AK, false>(hd, pc, -1, g, e0, l, c, ss, qv, kv);
             }
 #pragma unroll
             for (int h = 0; h < AQ; ++h) qv[h] = qn[h];
@@ -817,56 +947,69 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         } else {
             if (ok) {
                 pair_sincos(lf, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
-                rotate_token_any<IO>(hd, g, e0, l, c, ss);
+                rotate_token_any<IO>(hd, pc, pc.k_cache ? pc.slots[g] : -1, g, e0, l, c, ss);
             }
         }
         g = gn;
     }
 }
 
-// Two waves per sequence.  Work items, one 8-element chunk each: the Q heads (eight lanes per head,
-// rotated in place), the K heads (rotated into the cache), then the K pass-through chunks past the
-// rotary dims.  With 8 Q heads, 2 K heads and 256 dims there are exactly 128 items, so every lane
-// issues its loads at once and the whole step is one round trip plus the math.
+// `per` lanes (a multiple of 64) per sequence, several sequences per workgroup; one 8-element chunk
+// per work item: Q rotation chunks (eight lanes per head, rotated in place), K rotation chunks
+// (rotated into the cache), K pass-through chunks and, with V, the V chunks (copied into the
+// caches).  Every item issues all of its loads -- the sequence's position, amount and slot and its
+// data chunk -- before any math, so a step is one round trip plus the math.
 template <int IO>
-__global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs d, Rotary rot)
+__global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs d, Rotary rot, int per)
 {
-    const int item0 = threadIdx.x & 127;
-    const int64_t s = (int64_t)blockIdx.x * (kBlock / 128) + (threadIdx.x >> 7);
+    const int64_t s = (int64_t)blockIdx.x * (blockDim.x / per) + threadIdx.x / per;
     if (s >= d.n_seqs) return;
+    const PagedKV &pc = d.kv;
     const int nrq = d.nq * 8, nrk = d.nk * 8;
-    const int chunks = (d.head_dim - 64) / 8;
-    const int total = nrq + nrk + d.nk * chunks;
-    for (int it = item0; it < total; it += 128) {
-        if (it < nrq + nrk) {   // a whole 8-lane group takes this branch together
+    const int kpass = (d.head_dim - 64) / 8;
+    const int vch = d.head_dim / 8;
+    const int n_rot = nrq + nrk, n_k = n_rot + d.nk * kpass;
+    const int total = n_k + (pc.v ? d.nk * vch : 0);
+    for (int it = threadIdx.x % per; it < total; it += per) {
+        // kind 0: Q rotation, 1: K rotation, 2: K pass-through, 3: V (a rotation group of eight
+        // items never straddles two kinds)
+        int kind, h, e, m = 0, half = 0;
+        if (it < n_rot) {
             const bool isq = it < nrq;
-            const int h = (isq ? it : it - nrq) >> 3;
-            const int l = it & 7, m = l >> 1, half = l & 1;
-            const int e0 = 32 * half + 8 * m;
-            const int64_t off = (isq ? s * d.q_tok + h * d.q_head : s * d.k_tok + h * d.k_head) + e0;
-            const Raw8<IO> own = load8<IO>(isq ? d.q : d.k, off);
-            const int32_t plane = d.pos[s] - d.amount[s];
-            double c[8], ss[8];
-            pair_sincos(lane_freq(rot, m, half), plane, plane, plane, c, ss);
-            const Raw8<IO> y = rotate_chunk<IO>(own, c, ss);
-            if (isq) {
-                store8<IO>(d.q, off, y);
-            } else {
-                const int64_t slot = d.slots[s];
-                if (slot >= 0 && slot < d.num_slots)
-                    store8<IO>(d.cache, (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok +
-                                              h * d.c_head + e0, y);
-            }
+            kind = isq ? 0 : 1;
+            h = (isq ? it : it - nrq) >> 3;
+            const int l = it & 7;
+            m = l >> 1;
+            half = l & 1;
+            e = 32 * half + 8 * m;
+        } else if (it < n_k) {
+            const int c = it - n_rot;
+            kind = 2;
+            h = c / kpass;
+            e = 64 + (c - h * kpass) * 8;
         } else {
-            const int cc = it - nrq - nrk;
-            const int h = cc / chunks;
-            const int e = 64 + (cc % chunks) * 8;
-            const Raw8<IO> v = load8<IO>(d.k, s * d.k_tok + h * d.k_head + e);
-            const int64_t slot = d.slots[s];
-            if (slot >= 0 && slot < d.num_slots)
-                store8<IO>(d.cache, (slot / d.block_size) * d.c_block + (slot % d.block_size) * d.c_tok +
-                                          h * d.c_head + e, v);
+            const int c = it - n_k;
+            kind = 3;
+            h = c / vch;
+            e = (c - h * vch) * 8;
         }
+        const void *src = kind == 0 ? d.q : (kind == 3 ? pc.v : d.k);
+        const int64_t soff = kind == 0 ? s * d.q_tok + h * d.q_head + e
+                                       : (kind == 3 ? s * pc.v_tok + h * pc.v_head + e : s * d.k_tok + h * d.k_head + e);
+        // the lane's frequencies, the data chunk and the sequence's scalars: one round trip for all
+        const LaneFreq lf = lane_freq<false>(rot, m, half);
+        Raw8<IO> x = load8<IO>(src, soff);
+        const int32_t plane = d.pos[s] - d.amount[s];
+        const int64_t slot = kind != 0 ? pc.slots[s] : -1;
+        if (kind <= 1) {
+            double c[8], ss[8];
+            pair_sincos(lf, plane, plane, plane, c, ss);
+            x = rotate_chunk<IO>(x, c, ss);
+        }
+        if (kind == 0)
+            store8<IO>(d.q, soff, x);
+        else if (slot_ok(pc, slot))
+            store8<IO>(kind == 3 ? pc.v_cache : pc.k_cache, cache_off(pc, slot, h) + e, x);
     }
 }
 
@@ -938,58 +1081,91 @@ static int compute_units()
     return cus > 0 ? cus : 256;
 }
 
+// The fixed-head kernels cover the model's shape (8 Q heads, 2 KV heads); with a cache they also
+// need head_dim 256 and 16-bit I/O (fp32 copy chunks would not fit the register budget).
+static bool fixed_heads(const Heads &h, const PagedKV &pc, int io)
+{
+    if (h.nq != 8 || h.nk != 2) return false;
+    return !pc.k_cache || (h.head_dim == 256 && io != kIoF32);
+}
+
 template <int IO>
-static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, hipStream_t st)
+static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps,
+                                 const PagedKV &pc, hipStream_t st)
 {
     const int64_t groups = (h.n_tokens + kTokPerBlock - 1) / kTokPerBlock;
-    if (h.nq == 8 && h.nk == 2) {
+    if (fixed_heads(h, pc, IO)) {
         const int64_t cap = (int64_t)compute_units() * kApplyBlocksPerCU;
         const unsigned blocks = (unsigned)(groups < cap ? groups : cap);
+        if constexpr (IO != kIoF32) {
+            if (pc.k_cache) {
+                apply_kv_kernel<IO, 8, 2><<<blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
+                return hipGetLastError();
+            }
+        }
         apply_kernel<IO, 8, 2><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
     } else {
-        apply_any_kernel<IO><<<(unsigned)groups, kBlock, 0, st>>>(h, r, planes, ps);
+        apply_any_kernel<IO><<<(unsigned)groups, kBlock, 0, st>>>(h, r, planes, ps, pc);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, int io,
+hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps, const PagedKV &pc, int io,
                         hipStream_t stream)
 {
     switch (io) {
-    case kIoBF16: return apply_dispatch<kIoBF16>(h, r, planes, ps, stream);
-    case kIoF16: return apply_dispatch<kIoF16>(h, r, planes, ps, stream);
-    default: return apply_dispatch<kIoF32>(h, r, planes, ps, stream);
+    case kIoBF16: return apply_dispatch<kIoBF16>(h, r, planes, ps, pc, stream);
+    case kIoF16: return apply_dispatch<kIoF16>(h, r, planes, ps, pc, stream);
+    default: return apply_dispatch<kIoF32>(h, r, planes, ps, pc, stream);
     }
 }
 
 template <int IO>
-static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, hipStream_t st)
+static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, const PagedKV &pc, hipStream_t st)
 {
     const unsigned n_chunks = (unsigned)((h.n_tokens + kChunk - 1) / kChunk);
-    if (h.nq == 8 && h.nk == 2)
-        apply_ids_kernel<IO, 8, 2><<<n_chunks, kBlock, 0, st>>>(h, r, s);
-    else
-        apply_ids_kernel<IO, 0, 0><<<n_chunks, kBlock, 0, st>>>(h, r, s);
+    if (fixed_heads(h, pc, IO)) {
+        bool done = false;
+        if constexpr (IO != kIoF32) {
+            if (pc.k_cache) {
+                apply_ids_kernel<IO, 8, 2, true><<<n_chunks, kBlock, 0, st>>>(h, r, s, pc);
+                done = true;
+            }
+        }
+        if (!done) apply_ids_kernel<IO, 8, 2, false><<<n_chunks, kBlock, 0, st>>>(h, r, s, pc);
+    } else {
+        apply_ids_kernel<IO, 0, 0, false><<<n_chunks, kBlock, 0, st>>>(h, r, s, pc);
+    }
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : bump_if_device_epoch(s, st);
 }
 
-hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, int io, hipStream_t stream)
+hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, const PagedKV &pc, int io,
+                            hipStream_t stream)
 {
     switch (io) {
-    case kIoBF16: return apply_ids_dispatch<kIoBF16>(h, r, s, stream);
-    case kIoF16: return apply_ids_dispatch<kIoF16>(h, r, s, stream);
-    default: return apply_ids_dispatch<kIoF32>(h, r, s, stream);
+    case kIoBF16: return apply_ids_dispatch<kIoBF16>(h, r, s, pc, stream);
+    case kIoF16: return apply_ids_dispatch<kIoF16>(h, r, s, pc, stream);
+    default: return apply_ids_dispatch<kIoF32>(h, r, s, pc, stream);
     }
 }
 
+#ifndef MROPE_DECODE_BLOCK
+#define MROPE_DECODE_BLOCK 256
+#endif
+
 hipError_t launch_decode(const DecodeArgs &d, const Rotary &r, int io, hipStream_t stream)
 {
-    const unsigned blocks = (unsigned)((d.n_seqs + 1) / 2);
+    const int items = (d.nq + d.nk) * 8 + d.nk * (d.head_dim - 64) / 8 + (d.kv.v ? d.nk * d.head_dim / 8 : 0);
+    const int per = items >= 1024 ? 1024 : (items + 63) / 64 * 64;  // lanes per sequence
+    if (per == 0 || d.n_seqs == 0) return hipSuccess;
+    const int spb = per >= MROPE_DECODE_BLOCK ? 1 : MROPE_DECODE_BLOCK / per;  // sequences per workgroup
+    const unsigned blocks = (unsigned)((d.n_seqs + spb - 1) / spb);
+    const unsigned threads = (unsigned)(per * spb);
     switch (io) {
-    case kIoBF16: decode_kernel<kIoBF16><<<blocks, kBlock, 0, stream>>>(d, r); break;
-    case kIoF16: decode_kernel<kIoF16><<<blocks, kBlock, 0, stream>>>(d, r); break;
-    default: decode_kernel<kIoF32><<<blocks, kBlock, 0, stream>>>(d, r); break;
+    case kIoBF16: decode_kernel<kIoBF16><<<blocks, threads, 0, stream>>>(d, r, per); break;
+    case kIoF16: decode_kernel<kIoF16><<<blocks, threads, 0, stream>>>(d, r, per); break;
+    default: decode_kernel<kIoF32><<<blocks, threads, 0, stream>>>(d, r, per); break;
     }
     return hipGetLastError();
 }

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MROPE_ABI_VERSION 2
+#define MROPE_ABI_VERSION 3
 
 typedef enum {
     MROPE_OK = 0,
@@ -183,22 +183,69 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              size_t workspace_bytes, uint32_t epoch, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Paged K/V cache (mrope_apply_kv, mrope_apply_ids_kv, mrope_decode).  The K and V caches are the
+ * decoder's state ([card] "How the VLM rides the text-only engine": the keyCache [6, 1, 2, -1, 256],
+ * 2 KV heads of 256 dims); their paging is the serving engine's layout.
+ *
+ * k_cache, v_cache  element (block, row, head, d) at block*cache_block_stride + row*cache_tok_stride
+ *            + head*cache_head_stride + d, in elements of `dtype`; both caches use these strides.
+ * slot_mapping  int64, one per token (prefill) or per sequence (decode).  The token goes to block
+ *            slot / block_size, row slot % block_size.  slot < 0 or slot >= num_blocks*block_size:
+ *            nothing is written for it.  Two tokens with one slot: undefined which lands.
+ * A token's K heads are written whole: the first rot_dim dims rotated, the rest copied.  Its V
+ * heads (as many as K heads) are copied unrotated.  The caches must not overlap q, k or v.
+ * Alignment: caches 16-byte aligned, cache strides multiples of 8 (bf16, fp16) or 4 (fp32).
+ * ------------------------------------------------------------------------------------------- */
+
+/* ---------------------------------------------------------------------------------------------
+ * mrope_apply_kv -- prefill rotation with the K/V cache write fused in: Q rotated in place (as
+ * mrope_apply), K rotated and written whole into k_cache, V copied into v_cache, both at
+ * slot_mapping[t] of each token t.  k and v are read only.  Arguments as in mrope_apply and the
+ * paged-cache block above; v (n_kv_heads heads, element (t, h, d) at t*v_tok_stride +
+ * h*v_head_stride + d) may be NULL together with v_cache (then only K is written).
+ * ------------------------------------------------------------------------------------------- */
+mrope_status mrope_apply_kv(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads,
+                            const void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_kv_heads,
+                            const void *v, int64_t v_tok_stride, int64_t v_head_stride, int64_t n_tokens,
+                            int32_t head_dim, int32_t rot_dim, int32_t dtype, const int32_t *planes,
+                            int64_t plane_stride, double theta, void *k_cache, void *v_cache,
+                            const int64_t *slot_mapping, int32_t block_size, int64_t num_blocks,
+                            int64_t cache_block_stride, int64_t cache_tok_stride, int64_t cache_head_stride,
+                            void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * mrope_apply_ids_kv -- mrope_apply_ids with the K/V cache write of mrope_apply_kv: ids -> planes
+ * -> Q rotated in place, K rotated into k_cache, V copied into v_cache, in one launch.  The whole
+ * prefill step of an attention layer's positions and cache update.
+ * ------------------------------------------------------------------------------------------- */
+mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads,
+                                const void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_kv_heads,
+                                const void *v, int64_t v_tok_stride, int64_t v_head_stride, int64_t n_tokens,
+                                int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta,
+                                const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
+                                const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
+                                int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
+                                int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
+                                void *k_cache, void *v_cache, const int64_t *slot_mapping, int32_t block_size,
+                                int64_t num_blocks, int64_t cache_block_stride, int64_t cache_tok_stride,
+                                int64_t cache_head_stride, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * mrope_decode -- one generated token per sequence ([card] canvas table, last row: every position
  * from start on, generated tokens included, takes p - amount on all three planes).
  *
  * q          [n_seqs] tokens of Q heads (strides as in mrope_apply), rotated in place.
- * k          [n_seqs] tokens of new K heads (read only).
+ * k          [n_seqs] tokens of new K heads (read only), written whole into k_cache at
+ *            slot_mapping[s], the first rot_dim dims rotated (paged-cache block above).
+ * v          nullable: [n_seqs] tokens of new V heads (n_k_heads heads, read only), copied
+ *            unrotated into v_cache at the same slot.  NULL together with v_cache.
  * pos, amount  [n_seqs] int32: the token's position p and its sequence's amount; plane = p - amount.
- * k_cache    paged cache: element (block, row, head, d) at block*cache_block_stride +
- *            row*cache_tok_stride + head*cache_head_stride + d.  The full head_dim dims of every K
- *            head, first rot_dim rotated, are written at slot_mapping[s] (block = slot / block_size,
- *            row = slot % block_size).  slot < 0 or slot >= num_blocks*block_size: nothing written.
- *            Two sequences with the same slot: undefined which one lands.
  * slot_mapping [n_seqs] int64.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_decode(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads,
                           const void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads,
-                          int32_t n_seqs, const int32_t *pos, const int32_t *amount, void *k_cache,
+                          const void *v, int64_t v_tok_stride, int64_t v_head_stride, int32_t n_seqs,
+                          const int32_t *pos, const int32_t *amount, void *k_cache, void *v_cache,
                           const int64_t *slot_mapping, int32_t block_size, int64_t num_blocks,
                           int64_t cache_block_stride, int64_t cache_tok_stride, int64_t cache_head_stride,
                           int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *stream);

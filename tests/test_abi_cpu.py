@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.mrope_abi_version() == 2
+    assert lib.mrope_abi_version() == 3
     for code, text in ((OK, "ok"), (ARG, "invalid argument"), (HIP, "HIP runtime error")):
         assert lib.mrope_status_string(code).decode() == text
     assert lib.mrope_status_string(99).decode() == "unknown status"
@@ -93,26 +93,81 @@ def test_workspace_init_validation(lib):
     assert lib.mrope_workspace_init(A, 100, None) == WS
 
 
+_CACHE = dict(kc=A, vc=None, slots=A, bs=16, nb=64, cb=8192, ct=512, ch=256)
+
+
+def _cache_args(a):
+    return (a["kc"], a["vc"], a["slots"], a["bs"], a["nb"], a["cb"], a["ct"], a["ch"])
+
+
 def _decode(lib, **kw):
-    a = dict(q=A, qt=2048, qh=256, nq=8, k=A, kt=512, kh=256, nk=2, ns=16, pos=A, am=A, cache=A, slots=A, bs=16,
-             nb=64, cb=8192, ct=512, ch=256, hd=256, rot=64, dt=BF16, theta=1e7)
+    a = dict(q=A, qt=2048, qh=256, nq=8, k=A, kt=512, kh=256, nk=2, v=None, vt=512, vh=256, ns=16, pos=A, am=A,
+             hd=256, rot=64, dt=BF16, theta=1e7, **_CACHE)
     a.update(kw)
-    return lib.mrope_decode(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["ns"], a["pos"],
-                            a["am"], a["cache"], a["slots"], a["bs"], a["nb"], a["cb"], a["ct"], a["ch"], a["hd"],
-                            a["rot"], a["dt"], a["theta"], None)
+    return lib.mrope_decode(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["v"], a["vt"],
+                            a["vh"], a["ns"], a["pos"], a["am"], *_cache_args(a), a["hd"], a["rot"], a["dt"],
+                            a["theta"], None)
+
+
+_PAGED_CASES = [
+    (dict(kc=None), ARG), (dict(slots=None), ARG), (dict(bs=0), ARG), (dict(nb=-1), ARG), (dict(ct=-512), ARG),
+    (dict(kc=A + 2), ALIGN), (dict(ch=260), ALIGN), (dict(cb=8190), ALIGN), (dict(ch=128), ARG),
+    (dict(v=A), ARG), (dict(vc=A), ARG), (dict(v=A, vc=A + 8), ALIGN), (dict(v=A + 8, vc=A), ALIGN),
+    (dict(v=A, vc=A, vh=260), ALIGN), (dict(v=A, vc=A, vh=128), ARG), (dict(v=A, vc=A, vt=-8), ARG),
+]
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(pos=None), ARG), (dict(am=None), ARG), (dict(cache=None), ARG), (dict(slots=None), ARG),
-    (dict(bs=0), ARG), (dict(nb=-1), ARG), (dict(ct=-512), ARG), (dict(cache=A + 2), ALIGN), (dict(ch=250), ALIGN),
-    (dict(rot=128), UNSUP), (dict(theta=-1.0), ARG),
-])
+    (dict(pos=None), ARG), (dict(am=None), ARG), (dict(rot=128), UNSUP), (dict(theta=-1.0), ARG),
+    (dict(ns=-1), ARG),
+] + _PAGED_CASES)
 def test_decode_validation(lib, kw, code):
     assert _decode(lib, **kw) == code
 
 
 def test_decode_nothing_to_do(lib):
     assert _decode(lib, ns=0) == OK
+
+
+def _apply_kv(lib, **kw):
+    a = dict(q=A, qt=2048, qh=256, nq=8, k=A, kt=512, kh=256, nk=2, v=A, vt=512, vh=256, n=100, hd=256, rot=64,
+             dt=BF16, planes=A, ps=100, theta=1e7, **_CACHE)
+    a["vc"] = A
+    a.update(kw)
+    return lib.mrope_apply_kv(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["v"], a["vt"],
+                              a["vh"], a["n"], a["hd"], a["rot"], a["dt"], a["planes"], a["ps"], a["theta"],
+                              *_cache_args(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(planes=None), ARG), (dict(ps=99), ARG), (dict(rot=32), UNSUP), (dict(q=A + 8), ALIGN),
+    (dict(v=None), ARG), (dict(vc=None), ARG),
+] + [(kw, c) for kw, c in _PAGED_CASES if "v" not in kw and "vc" not in kw])
+def test_apply_kv_validation(lib, kw, code):
+    assert _apply_kv(lib, **kw) == code
+
+
+def test_apply_kv_nothing_to_do(lib):
+    assert _apply_kv(lib, n=0) == OK
+    assert _apply_kv(lib, nq=0, nk=0, kc=None, slots=None) == OK
+
+
+def _apply_ids_kv(lib, **kw):
+    a = dict(q=A, qt=2048, qh=256, nq=8, k=A, kt=512, kh=256, nk=2, v=A, vt=512, vh=256, n=1000, hd=256, rot=64,
+             dt=BF16, theta=1e7, ids=A, cu=A, ns=4, marker=248078, ws=A, wsb=10 ** 6, **_CACHE)
+    a["vc"] = A
+    a.update(kw)
+    return lib.mrope_apply_ids_kv(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["v"],
+                                  a["vt"], a["vh"], a["n"], a["hd"], a["rot"], a["dt"], a["theta"], a["ids"], a["cu"],
+                                  a["ns"], a["marker"], None, None, None, 0, None, None, None, None, a["ws"],
+                                  a["wsb"], 1, *_cache_args(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ids=None), ARG), (dict(cu=None), ARG), (dict(ws=None), WS), (dict(wsb=100), WS), (dict(dt=9), UNSUP),
+] + [(kw, c) for kw, c in _PAGED_CASES if "v" not in kw and "vc" not in kw])
+def test_apply_ids_kv_validation(lib, kw, code):
+    assert _apply_ids_kv(lib, **kw) == code
 
 
 def test_product_path_never_touches_the_oracle():
