@@ -59,7 +59,9 @@ def _load():
     lib.oracle_frame_scalars.restype = None
     lib.oracle_planes.argtypes = [P, P, i32, i32, P, i64, P, P, P]
     lib.oracle_planes.restype = None
-    lib.oracle_planes_chunk.argtypes = [P, P, i32, i32, P, P, P, i64, P, P, P]
+    lib.oracle_planes_chunk.argtypes = [P, P, i32, i32, i32, P, P, P, i64, P, P, P]
+    lib.oracle_frame_scalars_len.argtypes = [i32, i32, P, P]
+    lib.oracle_frame_scalars_len.restype = None
     lib.oracle_planes_chunk.restype = None
     lib.oracle_inv_freq.argtypes = [f64, i32, P]
     lib.oracle_inv_freq.restype = None
@@ -90,6 +92,12 @@ def first_marker(ids, marker_id: int) -> int:
     return int(_load().oracle_first_marker(_ptr(ids), ids.size, marker_id))
 
 
+def frame_scalars_len(origin: int, frame_len: int) -> tuple[int, int]:
+    st, am = ctypes.c_int32(), ctypes.c_int32()
+    _load().oracle_frame_scalars_len(int(origin), int(frame_len), ctypes.byref(st), ctypes.byref(am))
+    return st.value, am.value
+
+
 def frame_scalars(origin: int) -> tuple[int, int]:
     st, am = ctypes.c_int32(), ctypes.c_int32()
     _load().oracle_frame_scalars(int(origin), ctypes.byref(st), ctypes.byref(am))
@@ -113,10 +121,11 @@ def planes(ids, cu_seqlens, marker_id: int):
     return pl, st, am, og
 
 
-def planes_chunk(ids, cu_seqlens, marker_id: int, pos_offset=None, origin_in=None):
+def planes_chunk(ids, cu_seqlens, marker_id: int, pos_offset=None, origin_in=None, frame_len: int = 67):
     """Planes of a later piece of each sequence: token i of sequence s sits at pos_offset[s] + i, and
-    origin_in[s] (-1 = none) is the origin found in the earlier pieces.  Returns planes [3, L],
-    start, amount, origin (the sequence's origin so far, -1 = none)."""
+    origin_in[s] (-1 = none) is the origin found in the earlier pieces; frame_len tokens from the
+    origin to start.  Returns planes [3, L], start, amount, origin (the sequence's origin so far,
+    -1 = none)."""
     ids = _c(ids, np.int32)
     cu = _c(cu_seqlens, np.int32)
     n = cu.size - 1
@@ -127,7 +136,8 @@ def planes_chunk(ids, cu_seqlens, marker_id: int, pos_offset=None, origin_in=Non
     st = np.zeros(n, np.int32)
     am = np.zeros(n, np.int32)
     og = np.zeros(n, np.int32)
-    _load().oracle_planes_chunk(_ptr(ids), _ptr(cu), n, int(marker_id), _ptr(po) if po is not None else None,
+    _load().oracle_planes_chunk(_ptr(ids), _ptr(cu), n, int(marker_id), int(frame_len),
+                                _ptr(po) if po is not None else None,
                                 _ptr(oi) if oi is not None else None, _ptr(pl), total, _ptr(st), _ptr(am), _ptr(og))
     return pl, st, am, og
 

@@ -55,9 +55,9 @@ int32_t oracle_first_marker(const int32_t *ids, int32_t n, int32_t marker_id)
     return -1;
 }
 
-/* The frame's (T,H,W) offsets from O, one entry per frame token, in prompt order: <image>, the 64
- * rows k = 0..63 (row-major over the 8x8 grid), </image>, "\n".  Returns the frame length. */
-static int32_t frame_offsets(int32_t off[][3])
+/* The canvas: (T,H,W) offsets from O of <image>, the 64 rows k = 0..63 (row-major over the 8x8
+ * grid) and </image>, in prompt order.  Returns the number of entries (66). */
+static int32_t canvas_offsets(int32_t off[][3])
 {
     int32_t n = 0;
     off[n][0] = 0; off[n][1] = -1; off[n][2] = -1; ++n;            /* <image>          */
@@ -65,31 +65,53 @@ static int32_t frame_offsets(int32_t off[][3])
         off[n][0] = 0; off[n][1] = k / 8; off[n][2] = k % 8; ++n;
     }
     off[n][0] = 0; off[n][1] = 8; off[n][2] = 8; ++n;               /* </image>         */
-    off[n][0] = 0; off[n][1] = 0; off[n][2] = 0; ++n;               /* the "\n" after it */
     return n;
 }
 
+/* The frame: its first frame_len tokens from O, the canvas then the marker tokens that follow
+ * </image> at (O, O, O).  frame_len is 67 for this model's template (<image>, 64 rows, </image>, one
+ * "\n"); a run of k such tokens gives 66 + k; Qwen-VL's rule counts neither </image> nor the "\n"
+ * (65).  The offsets of frame token i (0 <= i < frame_len). */
+static void frame_offset(int32_t i, int32_t thw[3])
+{
+    int32_t off[66][3];
+    int32_t n = canvas_offsets(off);
+    if (i < n) {
+        thw[0] = off[i][0]; thw[1] = off[i][1]; thw[2] = off[i][2];
+    } else {                                                        /* marker after </image> */
+        thw[0] = 0; thw[1] = 0; thw[2] = 0;
+    }
+}
+
+#define ORACLE_FRAME_LEN 67
+
 /* ---------------------------------------------------------------------------------------------
- * Step 2: frame scalars.  start = the index after </image> and the "\n" that follows it;
- * amount = start - (O + 9) with 9 = max(H, W) + 1 taken over the canvas (the frame's offsets).
+ * Step 2: frame scalars.  start = the index after the frame (</image> and the marker tokens that
+ * follow it, frame_len tokens from O); amount = start - (O + 9), with 9 = max(H, W) + 1 taken over
+ * the canvas of the 8x8 grid (its </image> corner included, whichever tokens the frame counts).
  * Text-only: start = 2^30, amount = 0.
  * ------------------------------------------------------------------------------------------- */
-void oracle_frame_scalars(int32_t origin, int32_t *start, int32_t *amount)
+void oracle_frame_scalars_len(int32_t origin, int32_t frame_len, int32_t *start, int32_t *amount)
 {
     if (origin < 0) {
         *start = ORACLE_TEXT_ONLY_START;
         *amount = 0;
         return;
     }
-    int32_t off[67][3];
-    int32_t len = frame_offsets(off);
+    int32_t off[66][3];
+    int32_t n = canvas_offsets(off);
     int32_t max_hw = 0;
-    for (int32_t i = 0; i < len; ++i) {
+    for (int32_t i = 0; i < n; ++i) {
         if (off[i][1] > max_hw) max_hw = off[i][1];
         if (off[i][2] > max_hw) max_hw = off[i][2];
     }
-    *start = origin + len;
+    *start = origin + frame_len;
     *amount = *start - (origin + max_hw + 1);
+}
+
+void oracle_frame_scalars(int32_t origin, int32_t *start, int32_t *amount)
+{
+    oracle_frame_scalars_len(origin, ORACLE_FRAME_LEN, start, amount);
 }
 
 /* ---------------------------------------------------------------------------------------------
@@ -102,12 +124,11 @@ static void canvas_planes_at(int32_t p, int32_t origin, int32_t start, int32_t a
     } else if (p >= start) {                        /* everything after the frame */
         thw[0] = thw[1] = thw[2] = p - amount;
     } else {                                        /* inside the frame */
-        int32_t off[67][3];
-        frame_offsets(off);
-        int32_t i = p - origin;
-        thw[0] = origin + off[i][0];
-        thw[1] = origin + off[i][1];
-        thw[2] = origin + off[i][2];
+        int32_t d[3];
+        frame_offset(p - origin, d);
+        thw[0] = origin + d[0];
+        thw[1] = origin + d[1];
+        thw[2] = origin + d[2];
     }
 }
 
@@ -143,9 +164,10 @@ void oracle_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs
  * token i sits at position pos_offset[s] + i.  origin_in[s] is the canvas origin found in the earlier
  * pieces (-1: none yet); the first marker of the whole sequence wins, so a marker in this piece
  * counts only when no earlier piece had one.  pos_offset / origin_in may be NULL (0 / -1).
+ * frame_len: tokens from O to start (67 for this model's template; see frame_offset).
  * ------------------------------------------------------------------------------------------- */
 void oracle_planes_chunk(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
-                         const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes,
+                         int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes,
                          int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin)
 {
     for (int32_t s = 0; s < n_seqs; ++s) {
@@ -157,7 +179,7 @@ void oracle_planes_chunk(const int32_t *ids, const int32_t *cu_seqlens, int32_t 
             if (f >= 0) o = off + f;
         }
         int32_t st, am;
-        oracle_frame_scalars(o, &st, &am);
+        oracle_frame_scalars_len(o, frame_len, &st, &am);
         start[s] = st;
         amount[s] = am;
         if (origin) origin[s] = o;

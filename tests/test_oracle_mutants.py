@@ -16,7 +16,12 @@ MUTANTS = [
     ("grid row index off by one", "off[n][1] = k / 8; off[n][2] = k % 8;", "off[n][1] = (k + 1) / 8; off[n][2] = (k + 1) % 8;"),
     ("<image> at (O,O,O)", "off[n][0] = 0; off[n][1] = -1; off[n][2] = -1;", "off[n][0] = 0; off[n][1] = 0; off[n][2] = 0;"),
     ("</image> one short", "off[n][0] = 0; off[n][1] = 8; off[n][2] = 8;", "off[n][0] = 0; off[n][1] = 7; off[n][2] = 7;"),
-    ("newline dropped from the frame", "*start = origin + len;", "*start = origin + len - 1;"),
+    ("newline dropped from the frame", "#define ORACLE_FRAME_LEN 67", "#define ORACLE_FRAME_LEN 66"),
+    ("frame length ignored", "*start = origin + frame_len;", "*start = origin + ORACLE_FRAME_LEN;"),
+    ("amount from the frame's own offsets", "int32_t n = canvas_offsets(off);\n    int32_t max_hw = 0;",
+     "int32_t n = canvas_offsets(off);\n    if (frame_len < n) n = frame_len;\n    int32_t max_hw = 0;"),
+    ("</image> kept in a short frame", "} else if (p >= start) {                        /* everything after the frame */",
+     "} else if (p >= start && p - origin != 65) {"),
     ("amount + 1", "*amount = *start - (origin + max_hw + 1);", "*amount = *start - (origin + max_hw);"),
     ("text-only start 2^29", "#define ORACLE_TEXT_ONLY_START (1 << 30)", "#define ORACLE_TEXT_ONLY_START (1 << 29)"),
     ("last marker wins", "for (int32_t p = 0; p < n; ++p)\n        if (ids[p] == marker_id)\n            return p;",

@@ -455,3 +455,57 @@ def test_chunk_second_turn_positions():
     pl, st, am, og = oracle.planes_chunk(synth.text_ids(synth.rng(3, 1), 20), [0, 20], MARKER, [110], [6])
     assert (st[0], am[0], og[0]) == (73, 58, 6)
     np.testing.assert_array_equal(pl[0], np.arange(110, 130) - 58)
+
+
+# ---------------------------------------------------------------- generalised frames ---
+
+def _frame(n, origin, frame_len, seed=3):
+    ids = synth.prompt_ids(synth.rng(seed, 98), n, origin)
+    pl, st, am, og = oracle.planes_chunk(ids, [0, n], MARKER, frame_len=frame_len)
+    return pl, int(st[0]), int(am[0])
+
+
+def test_frame_len_kit_numbers():
+    """Model-zoo page, "CoreAIKit (VLChat)": the kit shifts the canvas from the index where the 64
+    pads begin + 66 by 58; Qwen-VL's rule would give + 64 and 56 (</image> and the "\\n" outside the
+    frame).  With the pads beginning at O + 1 these are frame lengths 67 and 65."""
+    o = 6
+    assert oracle.frame_scalars_len(o, 67) == (o + 1 + 66, 58)
+    assert oracle.frame_scalars_len(o, 65) == (o + 1 + 64, 56)
+    assert oracle.frame_scalars_len(o, 67) == oracle.frame_scalars(o)
+    assert oracle.frame_scalars_len(-1, 65) == (1 << 30, 0)
+
+
+@pytest.mark.parametrize("frame_len", [65, 66, 67, 68, 70, 90])
+def test_frame_len_table(frame_len):
+    """Card canvas table with a frame of frame_len tokens: the canvas rows as before; </image> at
+    (O, O+8, O+8) only when it is inside the frame; further marker tokens (O, O, O) up to start;
+    then p - amount.  The first position after the frame lands at O + 9 on every plane for any
+    frame length (closed form: amount = start - (O + 9))."""
+    n, o = 260, 12
+    pl, st, am = _frame(n, o, frame_len)
+    assert st == o + frame_len and am == frame_len - 9
+    for p in range(n):
+        if p < o:
+            want = (p, p, p)
+        elif p == o:
+            want = (o, o - 1, o - 1)
+        elif p - o <= 64 and p < st:
+            k = p - o - 1
+            want = (o, o + k // 8, o + k % 8)
+        elif p - o == 65 and p < st:
+            want = (o, o + 8, o + 8)
+        elif p < st:
+            want = (o, o, o)
+        else:
+            want = (p - am,) * 3
+        assert tuple(pl[:, p]) == want, (frame_len, p)
+    assert tuple(pl[:, st]) == (o + 9,) * 3
+
+
+def test_frame_len_67_is_the_default_rule():
+    b = synth.random_batch(31, 30, max_len=400)
+    a = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    c = oracle.planes_chunk(b.ids, b.cu_seqlens, MARKER, frame_len=67)
+    for x, y in zip(a, c):
+        np.testing.assert_array_equal(x, y)
