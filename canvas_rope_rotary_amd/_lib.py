@@ -59,19 +59,19 @@ def load():
     lib.mrope_workspace_init.argtypes = [P, U64, P]
     lib.mrope_workspace_init.restype = ctypes.c_int
     U32 = ctypes.c_uint32
-    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
+    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_planes.restype = ctypes.c_int
     lib.mrope_apply.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, P, I64, F64, P, P, P]
     lib.mrope_apply.restype = ctypes.c_int
     lib.mrope_apply_ids.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
-                                    P, P, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
+                                    P, P, I32, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_apply_ids.restype = ctypes.c_int
     cache = [P, P, P, I32, I64, I64, I64, I64]  # k_cache, v_cache, slot_mapping, block_size, num_blocks, strides
     lib.mrope_apply_kv.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I64, I32, I32, I32, P, I64, F64,
                                    *cache, P]
     lib.mrope_apply_kv.restype = ctypes.c_int
     lib.mrope_apply_ids_kv.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I64, I32, I32, I32, F64,
-                                       P, P, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, *cache, P]
+                                       P, P, I32, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, *cache, P]
     lib.mrope_apply_ids_kv.restype = ctypes.c_int
     lib.mrope_decode.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I32, P, P, *cache,
                                  I32, I32, I32, F64, P]
@@ -217,12 +217,13 @@ def _workspace(ws, n_tokens, device):
 
 
 def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078, *, out=None, start=None,
-           amount=None, origin=None, seq_flags=None, pos_offset=None, origin_in=None,
+           amount=None, origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67,
            workspace: Workspace | None = None):
     """Canvas planes from token ids.  Returns (planes [3, L] int32, start [n], amount [n], origin [n],
     seq_flags [n]).  cu_seqlens[-1] must equal len(ids).  For a later piece of each sequence (chunked
     prefill, a second turn) pass pos_offset (position of the piece's first token) and origin_in (the
-    previous piece's origin output)."""
+    previous piece's origin output).  frame_len: tokens from <image> to start (67: this template's
+    frame; 66 + k for k marker tokens after </image>; 65: Qwen-VL's rule)."""
     dev = _require_cuda(ids, cu_seqlens, out, start, amount, origin, seq_flags, pos_offset, origin_in)
     _i32_vec(ids, "ids")
     _i32_vec(cu_seqlens, "cu_seqlens")
@@ -240,7 +241,7 @@ def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078,
                                         mk(seq_flags, "seq_flags"))
     ws = _workspace(workspace, L, dev)
     with _on_device(dev):
-        _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), _ptr(pos_offset),
+        _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), int(frame_len), _ptr(pos_offset),
                                    _ptr(origin_in), _ptr(out), out.stride(0),
                                    _ptr(start), _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr,
                                    ws.capacity, ws.next_epoch(), _stream(dev)))
@@ -284,10 +285,10 @@ def apply(q: torch.Tensor, k: torch.Tensor | None, planes_: torch.Tensor, theta:
 
 def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seqlens: torch.Tensor,
               marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
-              origin=None, seq_flags=None, pos_offset=None, origin_in=None, q_out=None, k_out=None,
-              workspace: Workspace | None = None, rot_dim: int = ROT_DIM):
+              origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67, q_out=None,
+              k_out=None, workspace: Workspace | None = None, rot_dim: int = ROT_DIM):
     """Plane derivation fused with the rotation, one launch.  Returns (start, amount, origin,
-    seq_flags, planes_out or None).  pos_offset / origin_in as in planes()."""
+    seq_flags, planes_out or None).  pos_offset / origin_in / frame_len as in planes()."""
     dev = _require_cuda(q, k, ids, cu_seqlens, planes_out, start, amount, origin, seq_flags, q_out, k_out,
                         pos_offset, origin_in)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, q_out, k_out)
@@ -311,7 +312,7 @@ def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seq
     with _on_device(dev):
         _check(load().mrope_apply_ids(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, float(theta),
                                       _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
-                                      _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
+                                      int(frame_len), _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
                                       _ptr(seq_flags), ws.ptr, ws.capacity, ws.next_epoch(), _stream(dev)))
     return start, amount, origin, seq_flags, planes_out
 
@@ -363,8 +364,8 @@ def apply_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, planes_: 
 def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: torch.Tensor, cu_seqlens: torch.Tensor,
                  k_cache: torch.Tensor, v_cache: torch.Tensor | None, slot_mapping: torch.Tensor,
                  marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
-                 origin=None, seq_flags=None, pos_offset=None, origin_in=None, workspace: Workspace | None = None,
-                 rot_dim: int = ROT_DIM):
+                 origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67,
+                 workspace: Workspace | None = None, rot_dim: int = ROT_DIM):
     """apply_ids with the cache write of apply_kv, in one launch: ids -> planes -> q rotated in
     place, k rotated into k_cache, v copied into v_cache.  Returns (start, amount, origin,
     seq_flags, planes_out or None)."""
@@ -392,7 +393,7 @@ def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: 
     with _on_device(dev):
         _check(load().mrope_apply_ids_kv(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
                                          float(theta), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
-                                         _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start),
+                                         int(frame_len), _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start),
                                          _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr, ws.capacity,
                                          ws.next_epoch(), *cache, _stream(dev)))
     return start, amount, origin, seq_flags, planes_out

@@ -122,8 +122,9 @@ mrope_status check_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, i
 }
 
 Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_tokens, int32_t marker,
-               const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes, int64_t plane_stride,
-               int32_t *start, int32_t *amount, int32_t *origin, int32_t *flags, void *ws, uint32_t epoch)
+               int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes,
+               int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin, int32_t *flags, void *ws,
+               uint32_t epoch)
 {
     Scan s;
     s.ids = ids;
@@ -139,12 +140,20 @@ Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_
     s.flags = flags;
     s.pos_offset = pos_offset;
     s.origin_in = origin_in;
+    s.frame_len = frame_len == 0 ? kDefaultFrameLen : frame_len;
     s.workspace = ws;
     s.epoch = epoch;
     return s;
 }
 
 bool any_scalar(const Scan &s) { return s.start || s.amount || s.origin || s.flags; }
+
+mrope_status check_frame_len(int32_t frame_len)
+{
+    if (frame_len != 0 && (frame_len < 65 || frame_len > kMaxFrameLen))
+        return fail(MROPE_ERR_ARG, "frame_len must be 0 (67) or in [65, %d] (got %d)", kMaxFrameLen, frame_len);
+    return MROPE_OK;
+}
 
 // Paged K/V cache arguments; n_kv_heads == 0 needs none of them.
 mrope_status check_paged(int32_t n_kv_heads, const void *v, int64_t v_tok, int64_t v_head, void *k_cache,
@@ -228,14 +237,15 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream)
 }
 
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
-                          int32_t marker_id, const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes,
-                          int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin, int32_t *seq_flags,
-                          void *workspace, size_t workspace_bytes, uint32_t epoch, void *stream)
+                          int32_t marker_id, int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
+                          int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
+                          int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch, void *stream)
 {
     mrope_status st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes, plane_stride, workspace, workspace_bytes, true);
     if (st != MROPE_OK) return st;
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, pos_offset, origin_in, planes, plane_stride,
-                              start, amount, origin, seq_flags, workspace, epoch);
+    if ((st = check_frame_len(frame_len)) != MROPE_OK) return st;
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, pos_offset, origin_in, planes,
+                              plane_stride, start, amount, origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (n_tokens == 0) {
@@ -299,10 +309,10 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
                              int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *q_out, void *k_out,
                              const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
-                             const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
-                             int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
-                             int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
-                             void *stream)
+                             int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
+                             int32_t *planes_out, int64_t plane_stride, int32_t *start, int32_t *amount,
+                             int32_t *origin, int32_t *seq_flags, void *workspace, size_t workspace_bytes,
+                             uint32_t epoch, void *stream)
 {
     mrope_status st = check_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
                                   n_tokens, head_dim, rot_dim, dtype, q_out, k_out);
@@ -310,8 +320,9 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
     if (!(theta > 0.0) || !std::isfinite(theta)) return fail(MROPE_ERR_ARG, "theta must be finite and > 0");
     st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes_out, plane_stride, workspace, workspace_bytes, false);
     if (st != MROPE_OK) return st;
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, pos_offset, origin_in, planes_out,
-                              plane_stride, start, amount, origin, seq_flags, workspace, epoch);
+    if ((st = check_frame_len(frame_len)) != MROPE_OK) return st;
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, pos_offset, origin_in,
+                              planes_out, plane_stride, start, amount, origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (n_tokens == 0) {
@@ -327,7 +338,7 @@ mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_st
                                 const void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_kv_heads,
                                 const void *v, int64_t v_tok_stride, int64_t v_head_stride, int64_t n_tokens,
                                 int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, const int32_t *ids,
-                                const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
+                                const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id, int32_t frame_len,
                                 const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
                                 int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
                                 int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
@@ -344,8 +355,9 @@ mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_st
     if (st != MROPE_OK) return st;
     st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes_out, plane_stride, workspace, workspace_bytes, false);
     if (st != MROPE_OK) return st;
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, pos_offset, origin_in, planes_out,
-                              plane_stride, start, amount, origin, seq_flags, workspace, epoch);
+    if ((st = check_frame_len(frame_len)) != MROPE_OK) return st;
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, pos_offset, origin_in,
+                              planes_out, plane_stride, start, amount, origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (n_tokens == 0) {

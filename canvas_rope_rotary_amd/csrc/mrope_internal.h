@@ -7,6 +7,8 @@
 namespace mrope {
 
 constexpr int kMaxHeads = 64;
+constexpr int kDefaultFrameLen = 67;    // <image>, 64 rows, </image>, "\n"
+constexpr int kMaxFrameLen = 4096;
 constexpr int kTile = 64;               // tokens per scan tile: one wavefront, one lane per token
 constexpr size_t kWsHeaderBytes = 256;  // device epoch counter (+ padding)
 
@@ -44,6 +46,7 @@ struct Scan {
     int32_t *flags;      // nullable
     const int32_t *pos_offset;  // nullable: position of each sequence's first token here (0)
     const int32_t *origin_in;   // nullable: origin found in earlier pieces, -1 = none
+    int32_t frame_len;          // tokens from <image> to start (65 .. kMaxFrameLen)
     void *workspace;
     uint32_t epoch;      // tags this launch's status words; 0 = use (and advance) the device counter
 };

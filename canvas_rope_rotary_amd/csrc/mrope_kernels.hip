@@ -34,22 +34,24 @@ namespace {
 // ------------------------------------------------------------------ the canvas rule ------------
 constexpr int kGrid = 8;                      // 8x8 merged grid of one 448x448 image
 constexpr int kRows = kGrid * kGrid;          // 64 image rows, row-major
-constexpr int kFrameLen = 1 + kRows + 1 + 1;  // <image>, rows, </image>, "\n"  -> start = O + 67
 constexpr int kExtent = kGrid + 1;            // largest H/W offset on the canvas (</image>) + 1
-constexpr int kAmount = kFrameLen - kExtent;  // amount = start - (O + 9) = 58
+// The frame runs frame_len tokens from O to start: <image>, the rows, then </image> and the marker
+// tokens after it (67 for this model's template: one "\n"; 66 + k for a run of k; 65 under
+// Qwen-VL's rule, which leaves </image> and the "\n" out).  amount = start - (O + 9) = frame_len - 9.
 constexpr int32_t kTextStart = 1 << 30;       // text-only prompt: start = 2^30, amount = 0
 constexpr int32_t kNone = 0x7fffffff;         // "no marker"
 
-// Planes of position p; o = the sequence's canvas origin if it lies at or before p, else kNone.
-__device__ __forceinline__ void canvas_planes(int32_t p, int32_t o, int32_t &t, int32_t &h, int32_t &w)
+// Planes of position p; o = the sequence's canvas origin if it lies at or before p, else kNone;
+// fl = frame length (tokens from o to start).
+__device__ __forceinline__ void canvas_planes(int32_t p, int32_t o, int32_t fl, int32_t &t, int32_t &h, int32_t &w)
 {
     if (o == kNone) {
         t = h = w = p;
         return;
     }
     const int32_t d = p - o;
-    if (d >= kFrameLen) {
-        t = h = w = p - kAmount;
+    if (d >= fl) {
+        t = h = w = p - (fl - kExtent);
         return;
     }
     t = o;
@@ -288,10 +290,10 @@ __device__ void lookback(const Scan &sc, const uint64_t *status, int64_t chunk, 
 __device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t origin, bool multi, int64_t len)
 {
     const bool img = origin >= 0;
-    if (sc.start) sc.start[s] = img ? origin + kFrameLen : kTextStart;
-    if (sc.amount) sc.amount[s] = img ? kAmount : 0;
+    if (sc.start) sc.start[s] = img ? origin + sc.frame_len : kTextStart;
+    if (sc.amount) sc.amount[s] = img ? sc.frame_len - kExtent : 0;
     if (sc.origin) sc.origin[s] = img ? origin : -1;
-    if (sc.flags) sc.flags[s] = (multi ? 1 : 0) | ((img && (int64_t)origin + kFrameLen > len) ? 2 : 0);
+    if (sc.flags) sc.flags[s] = (multi ? 1 : 0) | ((img && (int64_t)origin + sc.frame_len > len) ? 2 : 0);
 }
 
 // Scan of one chunk by one full wave.  Publishes the chunk's status word, looks back when the
@@ -381,7 +383,7 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
                 const bool ok = g < c_end;
                 const int32_t p = offr + (int32_t)(g - sb);
                 int32_t t = 0, h = 0, w = 0;
-                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, t, h, w);
+                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, sc.frame_len, t, h, w);
                 sink(k, ok, t, h, w);
             }
         } else {
@@ -397,7 +399,7 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
                 const bool ok = g < c_end && g >= w_lo && g < w_hi;
                 const int32_t p = offr + (int32_t)(g - sb);
                 int32_t t = 0, h = 0, w = 0;
-                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, t, h, w);
+                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, sc.frame_len, t, h, w);
                 sink(k, ok, t, h, w);
             }
         }

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MROPE_ABI_VERSION 3
+#define MROPE_ABI_VERSION 4
 
 typedef enum {
     MROPE_OK = 0,
@@ -102,6 +102,11 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  *            (n_tokens is passed explicitly so the host never reads device memory).  Empty
  *            sequences are allowed.
  * marker_id  the <image> token id (248078 for the model's tokenizer).
+ * frame_len  tokens from <image> to start: the canvas (<image>, 64 rows), then </image> and the
+ *            marker tokens after it ([card] canvas table: start is the index after </image> and the
+ *            markers that follow).  0 = 67, this template's one "\n"; 66 + k for a run of k such
+ *            tokens; 65 for Qwen-VL's rule ([zoo] "CoreAIKit (VLChat)": +64 and 56 from the first
+ *            pad).  Allowed: 0 or 65..4096.  amount = frame_len - 9 for every length.
  * pos_offset [n_seqs] int32 (nullable = all 0): position of each sequence's first token in this call
  *            within the whole sequence.  A prompt may be fed in pieces -- prefill in chunks, a second
  *            turn continuing the first ([zoo] section "Prefill in chunks and a second turn") -- and
@@ -111,15 +116,16 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  *            this piece is used only when origin_in[s] < 0.  Feeding the pieces in order, each with
  *            the previous piece's origin, gives exactly the planes of one call on the whole sequence.
  * planes     [3][plane_stride] int32 out: row 0 = T, row 1 = H, row 2 = W; plane_stride >= n_tokens.
- *            For position p of a sequence whose first marker is at O:
- *              p < O or no marker     -> (p, p, p)
- *              p == O                 -> (O, O-1, O-1)
- *              p == O+1+k, k < 64     -> (O, O + k/8, O + k%8)
- *              p == O+65              -> (O, O+8, O+8)
- *              p == O+66              -> (O, O, O)
- *              p >= start == O+67     -> (p-58, p-58, p-58)
- * start, amount  [n_seqs] int32 out (nullable): start = O+67, amount = 58 for an image sequence;
- *            2^30 and 0 for a text-only one (so far).
+ *            For position p of a sequence whose first marker is at O, with F = frame_len,
+ *            start = O + F and amount = F - 9 (67 and 58 by default):
+ *              p < O or no marker          -> (p, p, p)
+ *              p == O                      -> (O, O-1, O-1)
+ *              p == O+1+k, k < 64          -> (O, O + k/8, O + k%8)
+ *              p == O+65 < start           -> (O, O+8, O+8)
+ *              O+66 <= p < start           -> (O, O, O)
+ *              p >= start                  -> (p-amount, p-amount, p-amount)
+ * start, amount  [n_seqs] int32 out (nullable): start = O + frame_len, amount = frame_len - 9 for
+ *            an image sequence; 2^30 and 0 for a text-only one (so far).
  * origin     [n_seqs] int32 out (nullable): O (a position in the whole sequence), or -1 when the
  *            sequence has no marker so far.
  * seq_flags  [n_seqs] int32 out (nullable): MROPE_SEQ_* bits (a marker here when origin_in >= 0
@@ -134,7 +140,7 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  * evaluated from its ids), so no tile ever waits on another.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
-                          int32_t marker_id, const int32_t *pos_offset, const int32_t *origin_in,
+                          int32_t marker_id, int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
                           int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount,
                           int32_t *origin, int32_t *seq_flags, void *workspace, size_t workspace_bytes,
                           uint32_t epoch, void *stream);
@@ -177,7 +183,7 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
                              int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *q_out,
                              void *k_out, const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs,
-                             int32_t marker_id, const int32_t *pos_offset, const int32_t *origin_in,
+                             int32_t marker_id, int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
                              int32_t *planes_out, int64_t plane_stride, int32_t *start,
                              int32_t *amount, int32_t *origin, int32_t *seq_flags, void *workspace,
                              size_t workspace_bytes, uint32_t epoch, void *stream);
@@ -223,7 +229,8 @@ mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_st
                                 const void *v, int64_t v_tok_stride, int64_t v_head_stride, int64_t n_tokens,
                                 int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta,
                                 const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
-                                const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
+                                int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
+                                int32_t *planes_out,
                                 int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
                                 int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
                                 void *k_cache, void *v_cache, const int64_t *slot_mapping, int32_t block_size,

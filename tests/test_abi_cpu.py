@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.mrope_abi_version() == 3
+    assert lib.mrope_abi_version() == 4
     for code, text in ((OK, "ok"), (ARG, "invalid argument"), (HIP, "HIP runtime error")):
         assert lib.mrope_status_string(code).decode() == text
     assert lib.mrope_status_string(99).decode() == "unknown status"
@@ -68,9 +68,9 @@ def test_apply_nothing_to_do(lib):
 
 
 def _planes(lib, **kw):
-    a = dict(ids=A, cu=A, ns=4, n=1000, marker=248078, planes=A, ps=1000, ws=A, wsb=10 ** 6)
+    a = dict(ids=A, cu=A, ns=4, n=1000, marker=248078, fl=0, planes=A, ps=1000, ws=A, wsb=10 ** 6)
     a.update(kw)
-    return lib.mrope_planes(a["ids"], a["cu"], a["ns"], a["n"], a["marker"], None, None, a["planes"], a["ps"], None,
+    return lib.mrope_planes(a["ids"], a["cu"], a["ns"], a["n"], a["marker"], a["fl"], None, None, a["planes"], a["ps"], None,
                             None, None, None, a["ws"], a["wsb"], 1, None)
 
 
@@ -78,6 +78,7 @@ def _planes(lib, **kw):
     (dict(ns=-1), ARG), (dict(n=-1), ARG), (dict(ns=0), ARG), (dict(cu=None), ARG), (dict(ids=None), ARG),
     (dict(planes=None), ARG), (dict(ps=999), ARG), (dict(n=1 << 31), ARG),
     (dict(ws=None), WS), (dict(ws=A + 64), WS), (dict(wsb=256 + 8 * 15), WS),
+    (dict(fl=64), ARG), (dict(fl=-1), ARG), (dict(fl=4097), ARG),
 ])
 def test_planes_validation(lib, kw, code):
     assert _planes(lib, **kw) == code
@@ -154,17 +155,18 @@ def test_apply_kv_nothing_to_do(lib):
 
 def _apply_ids_kv(lib, **kw):
     a = dict(q=A, qt=2048, qh=256, nq=8, k=A, kt=512, kh=256, nk=2, v=A, vt=512, vh=256, n=1000, hd=256, rot=64,
-             dt=BF16, theta=1e7, ids=A, cu=A, ns=4, marker=248078, ws=A, wsb=10 ** 6, **_CACHE)
+             dt=BF16, theta=1e7, ids=A, cu=A, ns=4, marker=248078, fl=0, ws=A, wsb=10 ** 6, **_CACHE)
     a["vc"] = A
     a.update(kw)
     return lib.mrope_apply_ids_kv(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["v"],
                                   a["vt"], a["vh"], a["n"], a["hd"], a["rot"], a["dt"], a["theta"], a["ids"], a["cu"],
-                                  a["ns"], a["marker"], None, None, None, 0, None, None, None, None, a["ws"],
+                                  a["ns"], a["marker"], a["fl"], None, None, None, 0, None, None, None, None, a["ws"],
                                   a["wsb"], 1, *_cache_args(a), None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(ids=None), ARG), (dict(cu=None), ARG), (dict(ws=None), WS), (dict(wsb=100), WS), (dict(dt=9), UNSUP),
+    (dict(fl=30), ARG),
 ] + [(kw, c) for kw, c in _PAGED_CASES if "v" not in kw and "vc" not in kw])
 def test_apply_ids_kv_validation(lib, kw, code):
     assert _apply_ids_kv(lib, **kw) == code

@@ -495,7 +495,7 @@ def test_device_epoch_mode_through_c_abi():
         st, am, og, fl = (torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(4))
         p = lambda t: ctypes.c_void_p(t.data_ptr())
         ws.ensure(L)
-        rc = lib.mrope_planes(p(ids), p(cu), n, L, MARKER, None, None, p(pl), L, p(st), p(am), p(og), p(fl), ws.ptr,
+        rc = lib.mrope_planes(p(ids), p(cu), n, L, MARKER, 0, None, None, p(pl), L, p(st), p(am), p(og), p(fl), ws.ptr,
                               ws.capacity, 0, stream)
         assert rc == 0
         _check_scan(b, pl, st, am, og, fl, f"device epoch call {i}")
@@ -649,3 +649,56 @@ def test_rounding_is_nearest_even(dtype):
     mr.apply(q, None, pl)
     info = compare_heads(host_heads(q), qn, epl, dtype, what=f"{dtype} rounding")
     assert info["frac_off_by_one"] < 1e-3, info
+
+
+@pytest.mark.parametrize("frame_len", [65, 66, 68, 75])
+def test_frame_len_planes_and_fused(frame_len):
+    """Frames of other lengths (marker runs after </image>; Qwen-VL's rule at 65): planes, scalars
+    and flags of mrope_planes and the fused call against the oracle's rule for that length."""
+    b = synth.random_batch(301 + frame_len, 40, max_len=600, dtype="bf16", empty_frac=0.05)
+    say(f"case: frame_len={frame_len} tokens={b.n_tokens}")
+    epl, est, eam, eog = oracle.planes_chunk(b.ids, b.cu_seqlens, MARKER, frame_len=frame_len)
+    assert (eam[eog >= 0] == frame_len - 9).all()
+    want_fl = expected_flags(b, eog) & 1
+    lens = np.diff(b.cu_seqlens)
+    want_fl |= np.where((eog >= 0) & (eog + frame_len > lens), 2, 0).astype(np.int32)
+    ids, cu = i32(b.ids), i32(b.cu_seqlens)
+    pl, st, am, og, fl = mr.planes(ids, cu, MARKER, frame_len=frame_len)
+    np.testing.assert_array_equal(pl.cpu().numpy(), epl)
+    np.testing.assert_array_equal(st.cpu().numpy(), est)
+    np.testing.assert_array_equal(am.cpu().numpy(), eam)
+    np.testing.assert_array_equal(og.cpu().numpy(), eog)
+    np.testing.assert_array_equal(fl.cpu().numpy(), want_fl)
+    qn, kn = b.qk()
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    pl2 = torch.full_like(pl, -7)
+    st2, am2, og2, fl2, _ = mr.apply_ids(q, k, ids, cu, MARKER, planes_out=pl2, frame_len=frame_len)
+    np.testing.assert_array_equal(pl2.cpu().numpy(), epl)
+    np.testing.assert_array_equal(fl2.cpu().numpy(), want_fl)
+    compare_heads(host_heads(q), qn, epl, "bf16", what=f"q frame_len={frame_len}")
+    compare_heads(host_heads(k), kn, epl, "bf16", what=f"k frame_len={frame_len}")
+
+
+def test_frame_len_pieces_cut_inside_the_tail():
+    """A 75-token frame fed in two pieces cut inside its marker run: the pieces equal the whole."""
+    frame_len = 75
+    b = synth.random_batch(331, 24, max_len=700, text_frac=0.0)
+    epl, est, eam, eog = oracle.planes_chunk(b.ids, b.cu_seqlens, MARKER, frame_len=frame_len)
+    lens = np.diff(b.cu_seqlens)
+    cut = np.clip(np.where(eog >= 0, eog + 70, lens // 2), 0, lens).astype(np.int64)
+    got = np.full_like(epl, -7)
+    prev = None
+    for part in range(2):
+        lo = np.zeros_like(cut) if part == 0 else cut
+        hi = cut if part == 0 else lens.astype(np.int64)
+        rows = np.concatenate([np.arange(b.cu_seqlens[s] + lo[s], b.cu_seqlens[s] + hi[s])
+                               for s in range(b.n_seqs)]).astype(np.int64)
+        cu = np.zeros(b.n_seqs + 1, np.int32)
+        cu[1:] = np.cumsum(hi - lo)
+        pl, st, am, og, fl = mr.planes(i32(b.ids[rows]), i32(cu), MARKER, pos_offset=i32(lo.astype(np.int32)),
+                                       origin_in=prev, frame_len=frame_len)
+        got[:, rows] = pl.cpu().numpy()
+        prev = og
+    np.testing.assert_array_equal(got, epl)
+    np.testing.assert_array_equal(st.cpu().numpy(), est)
+    np.testing.assert_array_equal(am.cpu().numpy(), eam)
