@@ -450,16 +450,27 @@ struct Raw8 {
     uint4 w[IO == kIoF32 ? 2 : 1];
 };
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Q, K and V chunks are read once: loads carry the non-temporal hint.  Measured on the 64 x 4096
+// workload: mrope_apply 119 -> 113 us, mrope_apply_ids 124 -> 117 us back to back, and no slower
+// from cold caches; marking the stores as well made both slower.
+__device__ __forceinline__ uint4 load16_nt(const void *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int IO>
 __device__ __forceinline__ Raw8<IO> load8(const void *base, int64_t elem)
 {
     Raw8<IO> r;
     if constexpr (IO != kIoF32) {
-        r.w[0] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + elem);
+        r.w[0] = load16_nt(static_cast<const uint16_t *>(base) + elem);
     } else {
-        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + elem);
-        r.w[0] = p[0];
-        r.w[1] = p[1];
+        const float *p = static_cast<const float *>(base) + elem;
+        r.w[0] = load16_nt(p);
+        r.w[1] = load16_nt(p + 4);
     }
     return r;
 }
