@@ -310,21 +310,29 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
     // id loads and the sequence search go out together
     int32_t idv[kSub];
     issue_ids(sc, c0, c_end, c0, lane, idv);
-    int32_t cnt_first, cnt_last;
-    wave_count_le2(sc.cu, n, c0, c_end - 1, lane, cnt_first, cnt_last);
-    ChunkMasks cm;
-    ballot_ids(sc, idv, cm);
-    const int32_t s_first = cnt_first - 1, s_last = cnt_last - 1;
-
-    // first window of 64 sequences (chunk 0 starts at sequence 0 so leading empty sequences get
-    // their scalars); it also holds the starts of the chunk's first and, usually, last sequence
-    int32_t win = c0 == 0 ? 0 : max(s_first, 0);
+    int32_t cnt_first, cnt_last, win;
     int64_t W, Wn;
-    {
+    if (n < 64) {
+        // every sequence start fits one window: it is loaded with the ids, and the chunk's first and
+        // last sequences are counted by ballot -- one round trip instead of a search, then a window
+        win = 0;
+        W = lane <= n ? (int64_t)sc.cu[lane] : INT64_MAX;
+        Wn = lane < n ? (int64_t)sc.cu[lane + 1] : INT64_MAX;
+        cnt_first = __builtin_popcountll(__ballot(W <= c0));
+        cnt_last = __builtin_popcountll(__ballot(W <= c_end - 1));
+    } else {
+        wave_count_le2(sc.cu, n, c0, c_end - 1, lane, cnt_first, cnt_last);
+        // first window of 64 sequences (chunk 0 starts at sequence 0 so leading empty sequences
+        // get their scalars); it also holds the starts of the chunk's first and, usually, last
+        // sequence
+        win = c0 == 0 ? 0 : max(cnt_first - 1, 0);
         const int32_t j = win + lane;
         W = j <= n ? (int64_t)sc.cu[min(j, n)] : INT64_MAX;
         Wn = j < n ? (int64_t)sc.cu[j + 1] : INT64_MAX;
     }
+    ChunkMasks cm;
+    ballot_ids(sc, idv, cm);
+    const int32_t s_first = cnt_first - 1, s_last = cnt_last - 1;
     const bool first_ok = s_first >= 0 && s_first < n;
     int64_t s0_begin = c0;
     if (first_ok) s0_begin = (s_first - win < 64) ? __shfl(W, s_first - win) : (int64_t)sc.cu[s_first];
