@@ -136,8 +136,18 @@ __device__ void wave_count_le2(const int32_t *cu, int32_t n, int64_t ka, int64_t
             stride[q] = (hi[q] - lo[q] + 127) / 128;
             p0[q] = lo[q] + (2 * lane) * stride[q];
             p1[q] = p0[q] + stride[q];
-            le0[q] = !done[q] && p0[q] < hi[q] && (int64_t)cu[p0[q]] <= key[q];
-            le1[q] = !done[q] && p1[q] < hi[q] && (int64_t)cu[p1[q]] <= key[q];
+        }
+        // the four loads of a level go out together (clamped to valid entries, masked after)
+        int32_t x0[2], x1[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            x0[q] = cu[min(p0[q], n)];
+            x1[q] = cu[min(p1[q], n)];
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            le0[q] = !done[q] && p0[q] < hi[q] && (int64_t)x0[q] <= key[q];
+            le1[q] = !done[q] && p1[q] < hi[q] && (int64_t)x1[q] <= key[q];
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -200,13 +210,21 @@ __device__ __forceinline__ void first_in(const ChunkMasks &cm, int64_t c0, int a
 }
 
 // Issue the chunk's id loads (tokens outside [from, c_end) read as a non-marker) ...
+// The 8 id loads of a chunk go out back to back: every lane loads (a clamped, valid address) and
+// out-of-range lanes are masked afterwards.  Loads under a per-lane condition were compiled into 8
+// round trips, each waited before the next was issued.  Needs from < c_end.
 __device__ __forceinline__ void issue_ids(const Scan &sc, int64_t c0, int64_t c_end, int64_t from, int lane,
                                           int32_t (&v)[kSub])
 {
 #pragma unroll
     for (int k = 0; k < kSub; ++k) {
         const int64_t g = c0 + 64 * k + lane;
-        v[k] = (g < c_end && g >= from) ? sc.ids[g] : ~sc.marker;
+        v[k] = sc.ids[min(max(g, from), c_end - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+        const int64_t g = c0 + 64 * k + lane;
+        if (!(g < c_end && g >= from)) v[k] = ~sc.marker;
     }
 }
 
@@ -300,8 +318,14 @@ __device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t
 // chunk's first sequence began earlier, writes the scalars of every sequence whose last token (for
 // an empty sequence: the token before it) lies in the chunk, and hands each token's planes to
 // sink(k, ok, t, h, w) for token chunk*kChunk + 64k + lane.
-template <class Sink>
-__device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint32_t ep, int lane, Sink sink)
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+// after_issue() runs once the chunk's id and sequence-start loads are in flight, before any wait.
+template <class Sink, class Hook = NoHook>
+__device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint32_t ep, int lane, Sink sink,
+                           Hook after_issue = Hook())
 {
     const int64_t c0 = chunk * kChunk;
     const int64_t c_end = min<int64_t>(c0 + kChunk, sc.n_tokens);
@@ -316,19 +340,23 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
         // every sequence start fits one window: it is loaded with the ids, and the chunk's first and
         // last sequences are counted by ballot -- one round trip instead of a search, then a window
         win = 0;
-        W = lane <= n ? (int64_t)sc.cu[lane] : INT64_MAX;
-        Wn = lane < n ? (int64_t)sc.cu[lane + 1] : INT64_MAX;
+        const int32_t w0 = sc.cu[min(lane, n)], w1 = sc.cu[min(lane + 1, n)];
+        after_issue();
+        W = lane <= n ? (int64_t)w0 : INT64_MAX;
+        Wn = lane < n ? (int64_t)w1 : INT64_MAX;
         cnt_first = __builtin_popcountll(__ballot(W <= c0));
         cnt_last = __builtin_popcountll(__ballot(W <= c_end - 1));
     } else {
+        after_issue();
         wave_count_le2(sc.cu, n, c0, c_end - 1, lane, cnt_first, cnt_last);
         // first window of 64 sequences (chunk 0 starts at sequence 0 so leading empty sequences
         // get their scalars); it also holds the starts of the chunk's first and, usually, last
         // sequence
         win = c0 == 0 ? 0 : max(cnt_first - 1, 0);
         const int32_t j = win + lane;
-        W = j <= n ? (int64_t)sc.cu[min(j, n)] : INT64_MAX;
-        Wn = j < n ? (int64_t)sc.cu[j + 1] : INT64_MAX;
+        const int32_t w0 = sc.cu[min(j, n)], w1 = sc.cu[min(j + 1, n)];
+        W = j <= n ? (int64_t)w0 : INT64_MAX;
+        Wn = j < n ? (int64_t)w1 : INT64_MAX;
     }
     ChunkMasks cm;
     ballot_ids(sc, idv, cm);
@@ -414,8 +442,9 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
         if (win + 64 >= n || (int64_t)sc.cu[win + 64] > c_end) break;
         win += 64;
         const int32_t jn = win + lane;
-        W = jn <= n ? (int64_t)sc.cu[min(jn, n)] : INT64_MAX;
-        Wn = jn < n ? (int64_t)sc.cu[jn + 1] : INT64_MAX;
+        const int32_t w0 = sc.cu[min(jn, n)], w1 = sc.cu[min(jn + 1, n)];
+        W = jn <= n ? (int64_t)w0 : INT64_MAX;
+        Wn = jn < n ? (int64_t)w1 : INT64_MAX;
     }
 }
 
@@ -918,13 +947,20 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     constexpr bool kFixed = NQ > 0 && NK > 0;
     constexpr int AQ = kFixed ? NQ : 1, AK = kFixed ? NK : 1;
 
+    // Wave 0 puts the scan's loads in flight first; only then (first barrier, without a fence: no
+    // wait) do the waves issue their first token's Q/K loads.  Issued the other way round, the scan's
+    // first round trip queued behind all Q/K loads of the chip (7 of the scan's 11.5 us).
     int64_t g = c0 + (tid >> 3);
     Raw8<IO> qv[AQ], kv[AK];
-    if constexpr (kFixed && !KV) {
-        if (g < c_end) load_token_fixed<IO, AQ, AK>(hd, g, e0, qv, kv);
-    }
-
-    if (tid < 64) {
+    auto prologue = [&]() {
+        if constexpr (kFixed && !KV) {
+            if (g < c_end) load_token_fixed<IO, AQ, AK>(hd, g, e0, qv, kv);
+        }
+    };
+    if (tid >= 64) {
+        __builtin_amdgcn_s_barrier();
+        prologue();
+    } else {
         if (lane < kSub) s_ok[lane] = 0;
         // a token is handed over once, in the sequence window that holds it
         scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane,
@@ -942,6 +978,10 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
                            sc.planes[sc.plane_stride + gg] = h;
                            sc.planes[2 * sc.plane_stride + gg] = w;
                        }
+                   },
+                   [&]() {
+                       __builtin_amdgcn_s_barrier();
+                       prologue();
                    });
     }
     __syncthreads();
