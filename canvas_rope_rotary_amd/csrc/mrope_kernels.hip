@@ -317,15 +317,18 @@ __device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t
 // Scan of one chunk by one full wave.  Publishes the chunk's status word, looks back when the
 // chunk's first sequence began earlier, writes the scalars of every sequence whose last token (for
 // an empty sequence: the token before it) lies in the chunk, and hands each token's planes to
-// sink(k, ok, t, h, w) for token chunk*kChunk + 64k + lane.
+// sink(k, ok, t, h, w) for token chunk*kChunk + 64k + lane.  When several workgroups scan the same
+// chunk, only the owner publishes and writes scalars: device-scope stores to one address from many
+// workgroups are serialized (16 writers of one status word took 3-8 us to be acknowledged, against
+// 0.6 us for one).
 struct NoHook {
     __device__ void operator()() const {}
 };
 
 // after_issue() runs once the chunk's id and sequence-start loads are in flight, before any wait.
 template <class Sink, class Hook = NoHook>
-__device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint32_t ep, int lane, Sink sink,
-                           Hook after_issue = Hook())
+__device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint32_t ep, int lane, bool owner,
+                           Sink sink, Hook after_issue = Hook())
 {
     const int64_t c0 = chunk * kChunk;
     const int64_t c_end = min<int64_t>(c0 + kChunk, sc.n_tokens);
@@ -374,13 +377,13 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
     int32_t f_last;
     bool m_last;
     first_in(cm, c0, (int)(max(sl_begin, c0) - c0), (int)(c_end - c0), f_last, m_last);
-    if (lane == 0) astore(status + chunk, status_word(ep, last_open ? kAgg : kIncl, m_last, last_ok ? f_last : kNone));
+    if (owner && lane == 0) astore(status + chunk, status_word(ep, last_open ? kAgg : kIncl, m_last, last_ok ? f_last : kNone));
 
     int32_t carry = kNone;
     bool carry_multi = false;
     if (need_carry) {
         lookback(sc, status, chunk, ep, lane, s0_begin, carry, carry_multi);
-        if (last_open && lane == 0) {
+        if (owner && last_open && lane == 0) {
             const bool mm = carry_multi || m_last || (carry != kNone && f_last != kNone);
             astore(status + chunk, status_word(ep, kIncl, mm, min(carry, f_last)));
         }
@@ -405,7 +408,7 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
         }
         if (j < n) {
             const int64_t fin = max<int64_t>(Wn - 1, 0);
-            if (fin >= c0 && fin < c_end) write_scalars(sc, j, oseq == kNone ? -1 : oseq, mm, poff + (Wn - W));
+            if (owner && fin >= c0 && fin < c_end) write_scalars(sc, j, oseq == kNone ? -1 : oseq, mm, poff + (Wn - W));
         }
         const int64_t w_lo = __shfl(W, 0), w_hi = __shfl(Wn, 63);
         if (s_first == s_last && s_first >= win && s_first - win < 64) {
@@ -917,7 +920,7 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
     const int64_t chunk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
     if (chunk >= n_chunks) return;
     const int64_t c0 = chunk * kChunk;
-    scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane,
+    scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane, true,
                [&](int k, bool ok, int32_t t, int32_t h, int32_t w) {
                    if (!ok) return;
                    const int64_t g = c0 + 64 * k + lane;
@@ -927,12 +930,14 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
                });
 }
 
-// Fused: one chunk per workgroup.  Every lane issues the Q/K loads of its first token, wave 0 scans
-// the chunk into LDS meanwhile, then the workgroup rotates the chunk 32 tokens at a time, each
-// 8-lane group prefetching its next token before rotating the current one.  KV as in apply_kernel
-// (fixed head counts); the generic path writes the cache when pc.k_cache is set.
+// Fused: one chunk per workgroup, or for small inputs one part of a chunk (2^part_log parts, each
+// workgroup repeating the chunk's scan, so more workgroups share the work and each has fewer
+// sequential steps).  Every lane issues the Q/K loads of its first token, wave 0 scans the chunk into
+// LDS meanwhile, then the workgroup rotates its part 32 tokens at a time, each 8-lane group
+// prefetching its next token before rotating the current one.  KV as in apply_kernel (fixed head
+// counts); the generic path writes the cache when pc.k_cache is set.
 template <int IO, int NQ, int NK, bool KV>
-__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, PagedKV pc)
+__global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, PagedKV pc, int part_log)
 {
     __shared__ int32_t s_pl[3][kChunk];
     __shared__ uint64_t s_ok[kSub];
@@ -941,20 +946,28 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     const int l = tid & 7, m = l >> 1, half = l & 1;
     const int e0 = 32 * half + 8 * m;
     const LaneFreq lf = lane_freq<true>(rot, m, half);
-    const int64_t chunk = blockIdx.x;
+    const int64_t chunk = (int64_t)(blockIdx.x >> part_log);
     const int64_t c0 = chunk * kChunk;
     const int64_t c_end = min<int64_t>(c0 + kChunk, hd.n_tokens);
+    const int plen = kChunk >> part_log;
+    const int64_t r0 = c0 + (int64_t)(blockIdx.x & ((1u << part_log) - 1)) * plen;  // this part: [r0, r_end)
+    if (r0 >= c_end) return;  // a part past the last token (the chunk's other parts scan it)
+    const int64_t r_end = min<int64_t>(r0 + plen, c_end);
     constexpr bool kFixed = NQ > 0 && NK > 0;
     constexpr int AQ = kFixed ? NQ : 1, AK = kFixed ? NK : 1;
 
     // Wave 0 puts the scan's loads in flight first; only then (first barrier, without a fence: no
     // wait) do the waves issue their first token's Q/K loads.  Issued the other way round, the scan's
-    // first round trip queued behind all Q/K loads of the chip (7 of the scan's 11.5 us).
-    int64_t g = c0 + (tid >> 3);
+    // first round trip queued behind all Q/K loads of the chip (7 of the scan's 11.5 us).  With a
+    // split chunk wave 0 issues its own first token only after the scan: the scan's later waits
+    // would otherwise include those loads (small inputs: 1 x 4096 tokens 17.8 -> 17.2 us, 4 x 4096
+    // 28.4 -> 25.7); on a full grid issuing them early is 1-2 us faster.
+    const bool w0_late = part_log > 0;
+    int64_t g = r0 + (tid >> 3);
     Raw8<IO> qv[AQ], kv[AK];
     auto prologue = [&]() {
         if constexpr (kFixed && !KV) {
-            if (g < c_end) load_token_fixed<IO, AQ, AK>(hd, g, e0, qv, kv);
+            if (g < r_end) load_token_fixed<IO, AQ, AK>(hd, g, e0, qv, kv);
         }
     };
     if (tid >= 64) {
@@ -963,7 +976,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     } else {
         if (lane < kSub) s_ok[lane] = 0;
         // a token is handed over once, in the sequence window that holds it
-        scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane,
+        scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane, r0 == c0,
                    [&](int k, bool ok, int32_t t, int32_t h, int32_t w) {
                        const int p = 64 * k + lane;
                        const uint64_t okm = __ballot(ok);
@@ -972,7 +985,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
                        s_pl[0][p] = t;
                        s_pl[1][p] = h;
                        s_pl[2][p] = w;
-                       if (sc.planes) {
+                       if (sc.planes && c0 + p >= r0 && c0 + p < r_end) {
                            const int64_t gg = c0 + p;
                            sc.planes[gg] = t;
                            sc.planes[sc.plane_stride + gg] = h;
@@ -981,13 +994,14 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
                    },
                    [&]() {
                        __builtin_amdgcn_s_barrier();
-                       prologue();
+                       if (!w0_late) prologue();
                    });
+        if (w0_late) prologue();
     }
     __syncthreads();
     wait_vm_all();  // the first token's loads: see apply_kernel
 
-    while (g < c_end) {  // the eight lanes of a token stay together
+    while (g < r_end) {  // the eight lanes of a token stay together
         const int p = (int)(g - c0);
         const bool ok = (s_ok[p >> 6] >> (p & 63)) & 1u;
         const int64_t gn = g + kTokPerBlock;
@@ -996,7 +1010,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
             if (ok) kv_token<IO, AQ, AK>(hd, pc, lf, g, e0, l, s_pl[0][p], s_pl[1][p], s_pl[2][p], pc.slots[g]);
         } else if constexpr (kFixed) {
             Raw8<IO> qn[AQ], kn[AK];
-            if (gn < c_end) load_token_fixed<IO, AQ, AK>(hd, gn, e0, qn, kn);
+            if (gn < r_end) load_token_fixed<IO, AQ, AK>(hd, gn, e0, qn, kn);
             if (ok) {
                 pair_sincos(lf, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
                 rotate_token_fixed<IO, AQ, AK, false>(hd, pc, -1, g, e0, l, c, ss, qv, kv);
@@ -1189,18 +1203,26 @@ hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, 
 template <int IO>
 static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, const PagedKV &pc, hipStream_t st)
 {
-    const unsigned n_chunks = (unsigned)((h.n_tokens + kChunk - 1) / kChunk);
+    const int64_t n_chunks = (h.n_tokens + kChunk - 1) / kChunk;
+    // Small inputs split each chunk over up to 16 workgroups (down to one 32-token step each) while
+    // that keeps the grid within two workgroups per CU; from 512 chunks on, one workgroup per chunk
+    // (splitting there measured slower: the repeated scans and the extra workgroups cost more than
+    // the balancing gains).
+    const int64_t target = (int64_t)compute_units() * 2;
+    int part_log = 0;
+    while (part_log < 4 && (n_chunks << (part_log + 1)) <= target) ++part_log;
+    const unsigned blocks = (unsigned)(n_chunks << part_log);
     if (fixed_heads(h, pc, IO)) {
         bool done = false;
         if constexpr (IO != kIoF32) {
             if (pc.k_cache) {
-                apply_ids_kernel<IO, 8, 2, true><<<n_chunks, kBlock, 0, st>>>(h, r, s, pc);
+                apply_ids_kernel<IO, 8, 2, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
                 done = true;
             }
         }
-        if (!done) apply_ids_kernel<IO, 8, 2, false><<<n_chunks, kBlock, 0, st>>>(h, r, s, pc);
+        if (!done) apply_ids_kernel<IO, 8, 2, false><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
     } else {
-        apply_ids_kernel<IO, 0, 0, false><<<n_chunks, kBlock, 0, st>>>(h, r, s, pc);
+        apply_ids_kernel<IO, 0, 0, false><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
     }
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : bump_if_device_epoch(s, st);

@@ -161,6 +161,35 @@ def test_chunk_boundaries(fused):
     compare_heads(host_heads(k), kn, epl, "bf16", what="edges k")
 
 
+@pytest.mark.parametrize("n_chunks", [1, 20, 40, 100, 200, 300])
+def test_fused_split_grid_levels(n_chunks):
+    """The fused call splits each 512-token chunk over up to 16 workgroups when the input is small
+    (1 and 20 chunks: 16 parts, 40: 8, 100: 4, 200: 2, 300: 1 on a 256-CU part); only the first
+    part of a chunk publishes its look-back word and writes scalars.  A long image sequence whose
+    look-back crosses many chunks, image and text sequences around it, a ragged tail."""
+    n = n_chunks * 512 - 37
+    tail = [300, 0, 70, 1] if n > 600 else []
+    lead = 5 if n > 600 else 0
+    lens = [lead] + [n - lead - sum(tail)] + tail
+    rng = np.random.default_rng(n_chunks)
+    placed = [None if lead == 0 else 0, int(rng.integers(0, max(1, lens[1] - 80))), 10, None, 0, None][:len(lens)]
+    g = synth.rng(17, n_chunks)
+    ids = np.concatenate([synth.prompt_ids(g, m, o) for m, o in zip(lens, placed) if m > 0])
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    b = synth.Prefill(f"split{n_chunks}", ids, cu, placed, "bf16", seed=17, head_dim=64)
+    say(f"case: {b.name}, {b.n_tokens} tokens")
+    qn, kn = b.qk()
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    pl = torch.full((3, b.n_tokens), -7, dtype=torch.int32, device="cuda")
+    st, am, og, fl, _ = mr.apply_ids(q, k, i32(ids), i32(cu), MARKER, planes_out=pl)
+    epl, est, eam, eog = _check_scan(b, pl, st, am, og, fl, b.name)
+    idx = np.arange(b.n_tokens) if b.n_tokens <= 25000 else _sample_tokens(b, eog, seed=n_chunks)
+    ti = torch.from_numpy(idx).cuda()
+    compare_heads(host_heads(q[ti]), qn[idx], epl[:, idx], "bf16", what=f"{b.name} q")
+    compare_heads(host_heads(k[ti]), kn[idx], epl[:, idx], "bf16", what=f"{b.name} k")
+
+
 def test_zero_tokens_text_scalars():
     cu = i32([0, 0, 0])
     ids = torch.zeros(0, dtype=torch.int32, device="cuda")
