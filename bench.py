@@ -130,6 +130,11 @@ def extras(args, dev, timed):
                          "fused_gbs": algorithmic_bytes_fused(cfg.n_tokens, elem=elem) / f_us / 1e3,
                          "apply_gbs": algorithmic_bytes_apply(cfg.n_tokens, elem=elem) / a_us / 1e3,
                          "tokens_per_s_fused": cfg.n_tokens / (f_us / 1e6)}
+        if small:  # out of place: full heads written to new buffers
+            qo, ko = torch.empty_like(q), torch.empty_like(k)
+            o_us = graph_timed(lambda: mr.apply(q, k, pl, q_out=qo, k_out=ko), args.steps) * 1e6
+            out[cfg.name]["apply_out_of_place_us"] = o_us
+            del qo, ko
         del q, k, pl
         torch.cuda.empty_cache()
     # fp16 I/O on the default batch shape (same bytes as bf16)
@@ -231,6 +236,65 @@ def cpu_baseline(b, qn, kn, min_seconds: float = 10.0, max_passes: int = 8):
                       f"{passes} pass(es), {el:.1f} s, one thread"}
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    """Worker threads for the all-cores oracle timing: the CPUs this process may run on, at most 16
+    (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline_threads(b, qn, kn, threads: int, min_seconds: float = 5.0, max_passes: int = 64):
+    """The same oracle calls as cpu_baseline, run by `threads` host threads over disjoint groups of
+    whole sequences (the oracle's C calls release the interpreter lock); tokens/s."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    from canvas_rope_rotary_amd import synth
+
+    cu = b.cu_seqlens.astype(np.int64)
+    # split the sequences into `threads` groups of about equal token counts
+    cuts = np.searchsorted(cu, np.linspace(0, cu[-1], threads + 1)[1:-1])
+    bounds = [0, *sorted(set(int(c) for c in cuts)), b.n_seqs]
+    groups = [(s0, s1) for s0, s1 in zip(bounds[:-1], bounds[1:]) if s1 > s0]
+
+    def work(g):
+        s0, s1 = g
+        t0, t1 = int(cu[s0]), int(cu[s1])
+        pl, *_ = oracle.planes(b.ids[t0:t1], (cu[s0:s1 + 1] - t0).astype(np.int32), synth.IMAGE_ID)
+        for x in (qn, kn):
+            oracle.round_bf16(oracle.rotate(synth.bf16_bits_to_f32(x[t0:t1]), pl))
+
+    passes = 0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(work, groups))
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or passes >= max_passes:
+                break
+    return {"value": passes * b.n_tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": host_cpu_model(),
+            "sample": f"the whole workload ({b.n_tokens} tokens in {len(groups)} sequence groups), {passes} "
+                      f"pass(es), {el:.1f} s, {threads} threads"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,14 +391,14 @@ def main():
         # to write back): the HBM-only figure, without hits in the 256 MB memory-side cache
         sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         ts, tf = [], []
-        for _ in range(10):
+        for _ in range(20):
             sweep.sum()
             torch.cuda.synchronize()
             ts.append(timed(lambda: mr.apply(q, k, planes), 1))
             sweep.sum()
             torch.cuda.synchronize()
             tf.append(timed(step, 1))
-        cold = (sorted(ts)[len(ts) // 2], sorted(tf)[len(tf) // 2])
+        cold = (sorted(ts), sorted(tf))
         del sweep
 
     # plain device-to-device copy of 1 GiB: the practical streaming ceiling on this machine (context)
@@ -381,14 +445,24 @@ def main():
         "copy_ceiling_gbs": copy_gbs,
     }
     if cold is not None:
-        out["cold"] = {"mrope_apply_us": cold[0] * 1e6, "mrope_apply_gbs": ab / cold[0] / 1e9,
-                       "mrope_apply_ids_us": cold[1] * 1e6, "mrope_apply_ids_gbs": fb / cold[1] / 1e9,
-                       "note": "median single launch after a 1 GiB read sweep (no memory-side cache hits)"}
+        pct = lambda v, q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+        ma, mf = pct(cold[0], 0.5), pct(cold[1], 0.5)
+        out["cold"] = {"mrope_apply_us": ma * 1e6, "mrope_apply_gbs": ab / ma / 1e9,
+                       "mrope_apply_ids_us": mf * 1e6, "mrope_apply_ids_gbs": fb / mf / 1e9,
+                       "mrope_apply_us_p10_p50_p90": [pct(cold[0], q) * 1e6 for q in (0.1, 0.5, 0.9)],
+                       "mrope_apply_ids_us_p10_p50_p90": [pct(cold[1], q) * 1e6 for q in (0.1, 0.5, 0.9)],
+                       "reps": len(cold[0]),
+                       "note": "single launches, each after a 1 GiB read sweep (no memory-side cache hits)"}
     if args.extras:
         out["extras"] = extras(args, dev, timed)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(b, qn, kn, min_seconds=args.cpu_seconds)
+        out["cpu_baseline"]["cpu"] = host_cpu_model()
+        nt = cpu_threads()
+        if nt > 1:
+            log(f"cpu baseline (oracle, {nt} threads)")
+            out["cpu_baseline_all_cores"] = cpu_baseline_threads(b, qn, kn, nt)
     print(json.dumps(out), flush=True)
 
 
