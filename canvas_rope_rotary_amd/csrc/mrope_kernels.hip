@@ -324,11 +324,17 @@ __device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t
 struct NoHook {
     __device__ void operator()() const {}
 };
+struct NoSingle {
+    __device__ bool operator()(int64_t, int32_t, int32_t) const { return false; }
+};
 
 // after_issue() runs once the chunk's id and sequence-start loads are in flight, before any wait.
-template <class Sink, class Hook = NoHook>
+// single(seq_begin, pos_offset, origin) is offered a chunk that lies in one sequence; returning true
+// takes the chunk's planes over in that form (every token of the chunk is handed over), and sink is
+// then not called.
+template <class Sink, class Hook = NoHook, class Single = NoSingle>
 __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint32_t ep, int lane, bool owner,
-                           Sink sink, Hook after_issue = Hook())
+                           Sink sink, Hook after_issue = Hook(), Single single = Single())
 {
     const int64_t c0 = chunk * kChunk;
     const int64_t c_end = min<int64_t>(c0 + kChunk, sc.n_tokens);
@@ -416,14 +422,16 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
             const int r = s_first - win;
             const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r);
             const int64_t sb = __shfl(W, r);
+            if (!single(sb, offr, orr)) {
 #pragma unroll
-            for (int k = 0; k < kSub; ++k) {
-                const int64_t g = c0 + 64 * k + lane;
-                const bool ok = g < c_end;
-                const int32_t p = offr + (int32_t)(g - sb);
-                int32_t t = 0, h = 0, w = 0;
-                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, sc.frame_len, t, h, w);
-                sink(k, ok, t, h, w);
+                for (int k = 0; k < kSub; ++k) {
+                    const int64_t g = c0 + 64 * k + lane;
+                    const bool ok = g < c_end;
+                    const int32_t p = offr + (int32_t)(g - sb);
+                    int32_t t = 0, h = 0, w = 0;
+                    if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, sc.frame_len, t, h, w);
+                    sink(k, ok, t, h, w);
+                }
             }
         } else {
 #pragma unroll
@@ -941,6 +949,8 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
 {
     __shared__ int32_t s_pl[3][kChunk];
     __shared__ uint64_t s_ok[kSub];
+    __shared__ int64_t s_seq[2];  // a chunk inside one sequence: [1] = its begin; [0] = its offset | origin << 32
+    __shared__ int32_t s_single;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int l = tid & 7, m = l >> 1, half = l & 1;
@@ -975,7 +985,11 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         prologue();
     } else {
         if (lane < kSub) s_ok[lane] = 0;
-        // a token is handed over once, in the sequence window that holds it
+        if (lane == 0) s_single = 0;
+        // A token is handed over once, in the sequence window that holds it.  A chunk inside one
+        // sequence (without planes_out) is handed over as that sequence's begin, offset and origin:
+        // every wave then derives its own tokens' planes, instead of wave 0 writing all 512 to LDS
+        // (measured: that handover was ~4 us of the launch on 64 x 4096 tokens).
         scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane, r0 == c0,
                    [&](int k, bool ok, int32_t t, int32_t h, int32_t w) {
                        const int p = 64 * k + lane;
@@ -995,24 +1009,64 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
                    [&]() {
                        __builtin_amdgcn_s_barrier();
                        if (!w0_late) prologue();
+                   },
+                   [&](int64_t sb, int32_t off, int32_t org) {
+                       if (sc.planes) return false;
+                       if (lane == 0) {
+                           s_seq[1] = sb;
+                           s_seq[0] = (int64_t)(uint32_t)off | ((int64_t)org << 32);
+                           s_single = 1;
+                       }
+                       return true;
                    });
         if (w0_late) prologue();
     }
     __syncthreads();
     wait_vm_all();  // the first token's loads: see apply_kernel
 
+    // Wave-uniform: the chunk's planes come from its sequence (single) or from LDS per token.  A
+    // single chunk wholly before the image (or in a text-only sequence) or wholly after the frame has
+    // t = h = w = p - shift for a uniform shift: one add per token.
+    const bool single = __builtin_amdgcn_readfirstlane(s_single) != 0;
+    const int64_t seq_begin = single ? s_seq[1] : 0;
+    const int64_t seq_word = single ? s_seq[0] : 0;
+    const int32_t seq_off = (int32_t)(uint32_t)seq_word, seq_org = (int32_t)(seq_word >> 32);
+    const int64_t p_c0 = single ? seq_off + (c0 - seq_begin) : 0;  // position of the chunk's first token
+    const int64_t p_last = p_c0 + (c_end - 1 - c0);
+    const bool before = seq_org == kNone || p_last < seq_org;
+    const bool after = !before && p_c0 - seq_org >= sc.frame_len;
+    const bool flat = single && (before || after);
+    const int32_t flat_c0 = (int32_t)(p_c0 - (after ? sc.frame_len - kExtent : 0));
+    auto planes_of = [&](int64_t gt, bool &ok, int32_t &t, int32_t &h, int32_t &w) {
+        if (flat) {
+            ok = true;
+            t = h = w = flat_c0 + (int32_t)(gt - c0);
+        } else if (single) {
+            const int32_t pp = seq_off + (int32_t)(gt - seq_begin);
+            ok = true;
+            canvas_planes(pp, (seq_org != kNone && seq_org <= pp) ? seq_org : kNone, sc.frame_len, t, h, w);
+        } else {
+            const int p = (int)(gt - c0);
+            ok = (s_ok[p >> 6] >> (p & 63)) & 1u;
+            t = s_pl[0][p];
+            h = s_pl[1][p];
+            w = s_pl[2][p];
+        }
+    };
+
     while (g < r_end) {  // the eight lanes of a token stay together
-        const int p = (int)(g - c0);
-        const bool ok = (s_ok[p >> 6] >> (p & 63)) & 1u;
+        bool ok;
+        int32_t pt, ph, pw;
+        planes_of(g, ok, pt, ph, pw);
         const int64_t gn = g + kTokPerBlock;
         double c[8], ss[8];
         if constexpr (kFixed && KV) {
-            if (ok) kv_token<IO, AQ, AK>(hd, pc, lf, g, e0, l, s_pl[0][p], s_pl[1][p], s_pl[2][p], pc.slots[g]);
+            if (ok) kv_token<IO, AQ, AK>(hd, pc, lf, g, e0, l, pt, ph, pw, pc.slots[g]);
         } else if constexpr (kFixed) {
             Raw8<IO> qn[AQ], kn[AK];
             if (gn < r_end) load_token_fixed<IO, AQ, AK>(hd, gn, e0, qn, kn);
             if (ok) {
-                pair_sincos(lf, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
+                pair_sincos(lf, pt, ph, pw, c, ss);
                 rotate_token_fixed<IO, AQ, AK, false>(hd, pc, -1, g, e0, l, c, ss, qv, kv);
             }
 #pragma unroll
@@ -1021,7 +1075,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
             for (int h = 0; h < AK; ++h) kv[h] = kn[h];
         } else {
             if (ok) {
-                pair_sincos(lf, s_pl[0][p], s_pl[1][p], s_pl[2][p], c, ss);
+                pair_sincos(lf, pt, ph, pw, c, ss);
                 rotate_token_any<IO>(hd, pc, pc.k_cache ? pc.slots[g] : -1, g, e0, l, c, ss);
             }
         }

@@ -83,11 +83,13 @@ def test_apply_kv_matches_oracle(dtype, with_v):
     assert n > 0.9 * b.n_tokens
 
 
+@pytest.mark.parametrize("planes_out", [True, False])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_apply_ids_kv_matches_oracle(dtype):
+def test_apply_ids_kv_matches_oracle(dtype, planes_out):
     """Planes from ids, rotation and the cache write in one launch; scalars and planes out as in
-    mrope_apply_ids."""
-    b = synth.random_batch(211, 48, max_len=900, dtype=dtype, empty_frac=0.05)
+    mrope_apply_ids.  Without planes_out a chunk inside one sequence takes the kernel's per-chunk
+    handover instead of per-token planes."""
+    b = synth.random_batch(211, 48, max_len=900 if planes_out else 3000, dtype=dtype, empty_frac=0.05)
     say(f"case: apply_ids_kv dtype={dtype} tokens={b.n_tokens}")
     qn, kn = b.qk()
     vn = v_heads(b)
@@ -96,10 +98,11 @@ def test_apply_ids_kv_matches_oracle(dtype):
     q, k, v = dev_heads(qn, dtype), dev_heads(kn, dtype), dev_heads(vn, dtype)
     kc = new_cache(nb, 32, 2, 256, dtype, 3.0)
     vc = new_cache(nb, 32, 2, 256, dtype, 3.0)
-    pl = torch.full((3, b.n_tokens), -9, dtype=torch.int32, device="cuda")
+    pl = torch.full((3, b.n_tokens), -9, dtype=torch.int32, device="cuda") if planes_out else None
     st, am, og, fl, _ = mr.apply_ids_kv(q, k, v, i32(b.ids), i32(b.cu_seqlens), kc, vc, torch.from_numpy(slots).cuda(),
                                         MARKER, planes_out=pl)
-    np.testing.assert_array_equal(pl.cpu().numpy(), epl)
+    if planes_out:
+        np.testing.assert_array_equal(pl.cpu().numpy(), epl)
     np.testing.assert_array_equal(st.cpu().numpy(), est)
     np.testing.assert_array_equal(am.cpu().numpy(), eam)
     np.testing.assert_array_equal(og.cpu().numpy(), eog)

@@ -112,6 +112,12 @@ def test_fuzz_small_batches(seed, dtype, n_seqs, max_len, empty):
     st2, am2, og2, fl2, _ = mr.apply_ids(q2, k2, ids, cu, MARKER, planes_out=pl2)
     _check_scan(b, pl2, st2, am2, og2, fl2, f"fuzz {seed} fused")
     assert torch.equal(q2, q) and torch.equal(k2, k)
+    # fused without planes_out (chunks inside one sequence are handed over per chunk): same bits
+    q3, k3 = dev_heads(qn, dtype), dev_heads(kn, dtype)
+    st3, am3, og3, fl3, _ = mr.apply_ids(q3, k3, ids, cu, MARKER)
+    for a, c in ((st3, st), (am3, am), (og3, og), (fl3, fl)):
+        assert torch.equal(a, c)
+    assert torch.equal(q3, q) and torch.equal(k3, k)
 
 
 def test_many_tiny_sequences_and_empties():
@@ -161,8 +167,9 @@ def test_chunk_boundaries(fused):
     compare_heads(host_heads(k), kn, epl, "bf16", what="edges k")
 
 
+@pytest.mark.parametrize("planes_out", [True, False])
 @pytest.mark.parametrize("n_chunks", [1, 20, 40, 100, 200, 300])
-def test_fused_split_grid_levels(n_chunks):
+def test_fused_split_grid_levels(n_chunks, planes_out):
     """The fused call splits each 512-token chunk over up to 16 workgroups when the input is small
     (1 and 20 chunks: 16 parts, 40: 8, 100: 4, 200: 2, 300: 1 on a 256-CU part); only the first
     part of a chunk publishes its look-back word and writes scalars.  A long image sequence whose
@@ -181,13 +188,43 @@ def test_fused_split_grid_levels(n_chunks):
     say(f"case: {b.name}, {b.n_tokens} tokens")
     qn, kn = b.qk()
     q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
-    pl = torch.full((3, b.n_tokens), -7, dtype=torch.int32, device="cuda")
-    st, am, og, fl, _ = mr.apply_ids(q, k, i32(ids), i32(cu), MARKER, planes_out=pl)
-    epl, est, eam, eog = _check_scan(b, pl, st, am, og, fl, b.name)
+    if planes_out:
+        pl = torch.full((3, b.n_tokens), -7, dtype=torch.int32, device="cuda")
+        st, am, og, fl, _ = mr.apply_ids(q, k, i32(ids), i32(cu), MARKER, planes_out=pl)
+        epl, est, eam, eog = _check_scan(b, pl, st, am, og, fl, b.name)
+    else:
+        st, am, og, fl, _ = mr.apply_ids(q, k, i32(ids), i32(cu), MARKER)
+        epl, est, eam, eog = _oracle_planes(b)
+        for got, want in ((st, est), (am, eam), (og, eog)):
+            np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=b.name)
     idx = np.arange(b.n_tokens) if b.n_tokens <= 25000 else _sample_tokens(b, eog, seed=n_chunks)
     ti = torch.from_numpy(idx).cuda()
     compare_heads(host_heads(q[ti]), qn[idx], epl[:, idx], "bf16", what=f"{b.name} q")
     compare_heads(host_heads(k[ti]), kn[idx], epl[:, idx], "bf16", what=f"{b.name} k")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_chunk_classes_without_planes_out(dtype):
+    """Without planes_out a chunk inside one sequence is handed over as (sequence begin, offset,
+    origin): chunks wholly before the image, wholly after the frame, cutting the frame, inside
+    text-only sequences, and chunks shared by several sequences (per-token path).  Frames at and
+    around chunk edges; every token compared with the oracle."""
+    lens = [3000, 2600, 1536, 700, 5, 1, 0, 1800, 2048, 40, 513]
+    placed = [1200, 0, None, 511, 0, None, None, 1022, 2000, None, 446]
+    g = synth.rng(23, 4)
+    ids = np.concatenate([synth.prompt_ids(g, n, o) for n, o in zip(lens, placed) if n > 0])
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    b = synth.Prefill("classes", ids, cu, placed, dtype, seed=23, head_dim=128)
+    qn, kn = b.qk()
+    q, k = dev_heads(qn, dtype), dev_heads(kn, dtype)
+    st, am, og, fl, _ = mr.apply_ids(q, k, i32(ids), i32(cu), MARKER)
+    epl, est, eam, eog = _oracle_planes(b)
+    for got, want, what in ((st, est, "start"), (am, eam, "amount"), (og, eog, "origin")):
+        np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=what)
+    np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg="flags")
+    compare_heads(host_heads(q), qn, epl, dtype, what=f"classes {dtype} q")
+    compare_heads(host_heads(k), kn, epl, dtype, what=f"classes {dtype} k")
 
 
 def test_zero_tokens_text_scalars():
@@ -402,19 +439,25 @@ def test_red_arms_fail_on_gpu_output():
 # ------------------------------------------------------------------ full-size workloads --------
 
 def _full_prefill(b, fused: bool):
+    """The fused call runs as benchmarked, without planes_out: planes never leave the kernel, so the
+    scalars are compared bit for bit and the planes through the rotation."""
     say(f"case: {b.name} tokens={b.n_tokens} seqs={b.n_seqs} fused={fused}")
     qn, kn = b.qk()
     ids, cu = i32(b.ids), i32(b.cu_seqlens)
     q, k = dev_heads(qn, b.dtype), dev_heads(kn, b.dtype)
     q_tail, k_tail = q[..., 64:].clone(), k[..., 64:].clone()
     if fused:
-        pl = torch.empty((3, b.n_tokens), dtype=torch.int32, device="cuda")
-        st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER, planes_out=pl)
+        st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER)
+        torch.cuda.synchronize()
+        epl, est, eam, eog = _oracle_planes(b)
+        for got, want, what in ((st, est, "start"), (am, eam, "amount"), (og, eog, "origin")):
+            np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"{b.name} {what}")
+        np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg=f"{b.name} flags")
     else:
         pl, st, am, og, fl = mr.planes(ids, cu, MARKER)
         mr.apply(q, k, pl)
-    torch.cuda.synchronize()
-    epl, est, eam, eog = _check_scan(b, pl, st, am, og, fl, b.name)
+        torch.cuda.synchronize()
+        epl, est, eam, eog = _check_scan(b, pl, st, am, og, fl, b.name)
     assert torch.equal(q[..., 64:], q_tail) and torch.equal(k[..., 64:], k_tail)
     idx = _sample_tokens(b, eog)
     ti = torch.from_numpy(idx).cuda()
