@@ -1140,10 +1140,14 @@ __global__ __launch_bounds__(IPL == 1 ? 1024 : 256) void decode_kernel(DecodeArg
     const int n_rot = nrq + nrk, n_k = n_rot + d.nk * kpass;
     const int total = n_k + (pc.v ? d.nk * vch : 0);
     const int li = threadIdx.x % per;
+    // Every rotation item of this lane sits at the same place in its group of eight (items
+    // li + j * per with per a multiple of 64, groups starting at multiples of 8), so they share
+    // one set of frequencies and one sincos evaluation.
+    const int l8 = li & 7;
+    const LaneFreq lf = lane_freq<false>(rot, l8 >> 1, l8 & 1);
     for (int base = 0; base < total; base += per * IPL) {
         DecodeItem item[IPL];
         bool live[IPL];
-        LaneFreq lf[IPL];
         Raw8<IO> x[IPL];
 #pragma unroll
         for (int j = 0; j < IPL; ++j) {
@@ -1152,19 +1156,19 @@ __global__ __launch_bounds__(IPL == 1 ? 1024 : 256) void decode_kernel(DecodeArg
             const int it = base + li + j * per;
             live[j] = it < total;
             item[j] = decode_item(d, s, live[j] ? it : 0, nrq, n_rot, n_k, kpass, vch);
-            lf[j] = lane_freq<false>(rot, item[j].m, item[j].half);
             x[j] = load8<IO>(item[j].src, item[j].soff);
         }
         const int32_t plane = d.pos[s] - d.amount[s];
         const int64_t slot = pc.slots ? pc.slots[s] : -1;  // no slots without K heads
+        bool any_rot = false;
+#pragma unroll
+        for (int j = 0; j < IPL; ++j) any_rot = any_rot || item[j].kind <= 1;
+        double c[8], ss[8];
+        if (any_rot) pair_sincos(lf, plane, plane, plane, c, ss);
 #pragma unroll
         for (int j = 0; j < IPL; ++j) {
             const DecodeItem &r = item[j];
-            if (r.kind <= 1) {
-                double c[8], ss[8];
-                pair_sincos(lf[j], plane, plane, plane, c, ss);
-                x[j] = rotate_chunk<IO>(x[j], c, ss);
-            }
+            if (r.kind <= 1) x[j] = rotate_chunk<IO>(x[j], c, ss);
             if (!live[j]) continue;
             if (r.kind == 0)
                 store8<IO>(d.q, r.soff, x[j]);
