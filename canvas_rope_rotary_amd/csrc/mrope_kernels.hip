@@ -11,8 +11,11 @@
 //   planes_kernel     ids -> first marker per sequence (ballot + decoupled look-back over 512-token
 //                     chunks) -> planes, start, amount
 //   apply_kernel      planes -> cos/sin on the fly -> rotate-half of Q and K (the HBM stream)
-//   apply_ids_kernel  the two above in one launch; a chunk's planes stay in LDS
-//   decode_kernel     one token per sequence: Q in place, K rotated and scattered to a paged cache
+//   apply_kv_kernel   the same, with K rotated into and V copied to paged K/V caches
+//   apply_any_kernel  other head counts and head dims (one workgroup per 32 tokens)
+//   apply_ids_kernel  planes from ids and the rotation in one launch; a chunk's planes stay on chip
+//                     (per token in LDS, or as one sequence's begin/offset/origin)
+//   decode_kernel     one token per sequence: Q in place, K rotated and V copied to a paged cache
 //
 // Thread layout of the rotary kernels: eight lanes per token; lane pair m holds frequencies
 // 8m .. 8m+7, one lane the x_j dims and its neighbour the x_{j+32} dims of every head, so the eight
