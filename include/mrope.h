@@ -59,7 +59,8 @@ typedef enum {
 
 /* seq_flags bits (optional per-sequence output of the plane-deriving calls). */
 #define MROPE_SEQ_MULTI_MARKER 1u /* more than one <image> marker; planes follow the first frame */
-#define MROPE_SEQ_FRAME_OVERRUN 2u /* the frame (67 tokens from the marker) runs past the end     */
+#define MROPE_SEQ_FRAME_OVERRUN 2u /* the frame (frame_len tokens from the marker, 67 by default)
+                                     runs past the end of the sequence */
 
 /* Text-only sequences get start = 2^30 and amount = 0 (card, start/amount paragraph). */
 #define MROPE_TEXT_ONLY_START (1 << 30)
@@ -77,8 +78,9 @@ const char *mrope_last_error(void);
  *
  * Returns the bytes needed for n_tokens packed tokens.  The workspace must be 256-byte aligned
  * device memory, zero-filled (or passed once through mrope_workspace_init) before its first use;
- * it needs no clearing between calls.  It holds a device epoch counter and one 64-bit status word
- * per 64-token tile, through which a tile hands the first marker of a sequence to the next tiles.
+ * it needs no clearing between calls.  It holds a device epoch counter and room for one 64-bit
+ * status word per 64 tokens; the scan uses one word per 512-token chunk, through which a chunk
+ * hands the first marker of a sequence to the chunks after it.
  *
  * Epochs.  The plane-deriving calls take an `epoch` that tags the status words they write, so a
  * call never mistakes words left by an earlier call for its own:
@@ -134,10 +136,10 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  *
  * epoch      see mrope_workspace_bytes.
  *
- * One launch (plus a one-thread kernel when epoch == 0): each 64-token tile finds its markers with a
- * wavefront ballot and takes the first marker of a sequence that began in an earlier tile from its
- * predecessors by a wait-free decoupled look-back (a predecessor that has not published yet is
- * evaluated from its ids), so no tile ever waits on another.
+ * One launch (plus a one-thread kernel when epoch == 0): each 512-token chunk finds its markers with
+ * wavefront ballots over 64-id loads and takes the first marker of a sequence that began in an
+ * earlier chunk from its predecessors by a decoupled look-back with bounded polls (a predecessor
+ * that has not published after them is evaluated from its ids), so no chunk waits without bound.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
                           int32_t marker_id, int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
@@ -174,10 +176,10 @@ mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, i
 
 /* ---------------------------------------------------------------------------------------------
  * mrope_apply_ids -- planes derivation and rotation fused in ONE launch (plus a one-thread kernel
- * when epoch == 0): ids -> first marker per sequence -> planes (kept in LDS) -> rotate Q and K.
+ * when epoch == 0): ids -> first marker per sequence -> planes (kept on chip) -> rotate Q and K.
  * Arguments as in mrope_planes and mrope_apply; planes_out (nullable) additionally receives the
- * planes ([3][plane_stride]).  n_tokens must equal cu_seqlens[n_seqs].  The Q/K loads of a tile are
- * issued before its look-back, which hides behind them.
+ * planes ([3][plane_stride]).  n_tokens must equal cu_seqlens[n_seqs].  The Q/K loads of a chunk
+ * are issued while its scan runs.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
