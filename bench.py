@@ -152,6 +152,59 @@ def extras(args, dev, timed):
     del q, k, pl
     torch.cuda.empty_cache()
 
+    # chunked prefill: the 8 x 32,768 prompts fed as 4 pieces of 8,192 tokens per sequence, each piece
+    # one fused call carrying pos_offset and the previous piece's origin (all pieces resident)
+    cfg = synth.config3()
+    log("extras: 8x32768 bf16 in 4 pieces")
+    qn, kn = cfg.qk()
+    q, k = heads(qn, "bf16"), heads(kn, "bf16")
+    n_pc, L = 4, 32768
+    piece = L // n_pc
+    cu_p = torch.arange(0, 8 * piece + 1, piece, dtype=torch.int32, device=dev)
+    rows = [torch.from_numpy(np.concatenate([np.arange(s * L + i * piece, s * L + (i + 1) * piece)
+                                             for s in range(8)])).to(dev) for i in range(n_pc)]
+    ids_all = torch.from_numpy(cfg.ids).to(dev)
+    ids_p = [ids_all[r].contiguous() for r in rows]
+    q_p = [q[r].contiguous() for r in rows]
+    k_p = [k[r].contiguous() for r in rows]
+    offs = [torch.full((8,), i * piece, dtype=torch.int32, device=dev) for i in range(n_pc)]
+    origins = [torch.full((8,), -1, dtype=torch.int32, device=dev) for _ in range(n_pc + 1)]
+    ws = mr.Workspace(8 * piece, dev)
+
+    def pieces():
+        for i in range(n_pc):
+            mr.apply_ids(q_p[i], k_p[i], ids_p[i], cu_p, synth.IMAGE_ID, pos_offset=offs[i], origin_in=origins[i],
+                         origin=origins[i + 1], workspace=ws)
+
+    # GPU time from a replayed graph: a 65,536-token call is shorter than the binding's host time
+    c_us = graph_timed(pieces, max(1, args.steps // n_pc)) * 1e6
+    out["8x32768-image-bf16-in-4-pieces"] = {
+        "tokens": cfg.n_tokens, "pieces": n_pc, "fused_us_all_pieces": c_us, "fused_us_per_piece": c_us / n_pc,
+        "tokens_per_s": cfg.n_tokens / (c_us / 1e6),
+        "gbs": algorithmic_bytes_fused(cfg.n_tokens) / c_us / 1e3, "timing": "hip graph replay",
+        "note": "mrope_apply_ids per piece of 65,536 tokens with pos_offset and origin_in (chunked prefill)"}
+    del q, k, q_p, k_p
+    torch.cuda.empty_cache()
+
+    # a longer frame (frame_len 75: a run of 9 marker tokens after </image>) on the default workload
+    cfg = synth.config2()
+    log("extras: 64x4096 bf16, frame_len 75")
+    qn, kn = cfg.qk()
+    q, k = heads(qn, "bf16"), heads(kn, "bf16")
+    ids = torch.from_numpy(cfg.ids).to(dev)
+    cu = torch.from_numpy(cfg.cu_seqlens).to(dev)
+    ws = mr.Workspace(cfg.n_tokens, dev)
+    f75, f67 = [], []
+    for _ in range(3):  # interleaved, median of three
+        f67.append(timed(lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, workspace=ws), args.steps) * 1e6)
+        f75.append(timed(lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, frame_len=75, workspace=ws),
+                         args.steps) * 1e6)
+    f75, f67 = sorted(f75)[1], sorted(f67)[1]
+    out["64x4096-image-bf16-frame-len-75"] = {"tokens": cfg.n_tokens, "fused_us": f75, "fused_us_frame_len_67": f67,
+                                              "gbs": algorithmic_bytes_fused(cfg.n_tokens) / f75 / 1e3}
+    del q, k
+    torch.cuda.empty_cache()
+
     # prefill with the paged K/V cache write fused in (64 x 4096 bf16, V from the same seed stream)
     cfg = synth.config2()
     log("extras: 64x4096 bf16 with the K/V cache write")
