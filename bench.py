@@ -351,8 +351,9 @@ def cpu_baseline_threads(b, qn, kn, threads: int, min_seconds: float = 5.0, max_
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: the step time settles only after ~100 back-to-back launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cold", action="store_true", help="also time mrope_apply after a cache-clearing read sweep")
