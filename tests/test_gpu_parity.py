@@ -255,12 +255,14 @@ def _piece_cuts(b, n_pieces, seed):
     return np.array(cuts, np.int64)  # [n_seqs, n_pieces + 1]
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_chunked_pieces_match_whole_sequences(fused):
+@pytest.mark.parametrize("mode", ["planes", "fused", "fused_no_planes_out"])
+def test_chunked_pieces_match_whole_sequences(mode):
     """Prefill in pieces (chunked prefill, a second turn): each piece passes the position of its
     first token and the origin the earlier pieces found; planes and rotated Q/K of every piece equal
     the one-call result on the whole sequences, and the last piece's scalars equal the whole
-    sequences' scalars."""
+    sequences' scalars.  Without planes_out the fused call hands a single-sequence chunk over per
+    chunk, with the piece's offset and carried origin; its planes are then judged by the rotation."""
+    fused = mode != "planes"
     b = synth.random_batch(71, 36, max_len=2600, dtype="bf16", empty_frac=0.05)
     n_pieces = 5
     cuts = _piece_cuts(b, n_pieces, 72)
@@ -282,19 +284,19 @@ def test_chunked_pieces_match_whole_sequences(fused):
         ids_k = b.ids[rows].astype(np.int32)
         off = cuts[:, k].astype(np.int32)
         oin = None if origin_prev is None else origin_prev
+        # the piece alone against the oracle's piece rule
+        cpl, cst, cam, cog = oracle.planes_chunk(ids_k, cu, MARKER, off,
+                                                 None if oin is None else oin.cpu().numpy())
         if fused:
             q, kk = dev_heads(qn[rows], "bf16"), dev_heads(kn[rows], "bf16")
-            pl = torch.full((3, rows.size), -7, dtype=torch.int32, device="cuda")
+            pl = torch.full((3, rows.size), -7, dtype=torch.int32, device="cuda") if mode == "fused" else None
             st, am, og, fl, _ = mr.apply_ids(q, kk, i32(ids_k), i32(cu), MARKER, planes_out=pl,
                                              pos_offset=i32(off), origin_in=oin)
             got_q[rows], got_k[rows] = host_heads(q), host_heads(kk)
         else:
             pl, st, am, og, fl = mr.planes(i32(ids_k), i32(cu), MARKER, pos_offset=i32(off), origin_in=oin)
-        pl_h = pl.cpu().numpy()
+        pl_h = pl.cpu().numpy() if pl is not None else cpl
         got_pl[:, rows] = pl_h[:, :rows.size]
-        # the piece alone against the oracle's piece rule
-        cpl, cst, cam, cog = oracle.planes_chunk(ids_k, cu, MARKER, off,
-                                                 None if oin is None else oin.cpu().numpy())
         np.testing.assert_array_equal(pl_h[:, :rows.size], cpl, err_msg=f"piece {k} planes")
         np.testing.assert_array_equal(st.cpu().numpy(), cst, err_msg=f"piece {k} start")
         np.testing.assert_array_equal(am.cpu().numpy(), cam, err_msg=f"piece {k} amount")
@@ -329,7 +331,11 @@ def test_second_turn_long_pieces():
     seen = np.zeros(b.n_tokens, bool)
     turns = [[(0, 30000), (int(cu[1]), int(cu[1]) + 50000)],
              [(30000, 100000), (int(cu[1]) + 50000, int(cu[2]))]]
-    og_prev = None
+    # the fused call without planes_out on the same pieces (head_dim 64 keeps the inputs small):
+    # single-sequence chunks are handed over with the piece's offset and the carried origin
+    bq = synth.Prefill("turns-q", ids, cu, placed, "bf16", seed=19, head_dim=64)
+    qn, kn = bq.qk()
+    og_prev, og_prev_f = None, None
     for k, segs in enumerate(turns):
         rows = np.concatenate([np.arange(a, e) for a, e in segs]).astype(np.int64)
         ccu = np.array([0, segs[0][1] - segs[0][0], rows.size], np.int32)
@@ -338,6 +344,17 @@ def test_second_turn_long_pieces():
                                        origin_in=og_prev)
         np.testing.assert_array_equal(pl.cpu().numpy(), epl[:, rows], err_msg=f"turn {k} planes")
         og_prev = og
+        q, kk = dev_heads(qn[rows], "bf16"), dev_heads(kn[rows], "bf16")
+        st_f, am_f, og_f, fl_f, _ = mr.apply_ids(q, kk, i32(b.ids[rows]), i32(ccu), MARKER, pos_offset=i32(off),
+                                                 origin_in=og_prev_f)
+        for a_, c_ in ((st_f, st), (am_f, am), (og_f, og), (fl_f, fl)):
+            assert torch.equal(a_, c_), f"turn {k} fused scalars"
+        og_prev_f = og_f
+        pick = np.unique(np.concatenate([np.random.default_rng(k).integers(0, rows.size, 3000),
+                                         np.flatnonzero((epl[0, rows] != epl[1, rows]) | (epl[0, rows] != epl[2, rows]))]))
+        compare_heads(host_heads(q)[pick], qn[rows][pick], epl[:, rows][:, pick], "bf16", what=f"turn {k} fused q")
+        compare_heads(host_heads(kk)[pick], kn[rows][pick], epl[:, rows][:, pick], "bf16", what=f"turn {k} fused k")
+        del q, kk
         seen[rows] = True
     assert seen.all()
     np.testing.assert_array_equal(st.cpu().numpy(), est)
