@@ -225,6 +225,17 @@ def extras(args, dev, timed):
         "gbs": algorithmic_bytes_fused_kv(cfg.n_tokens) / kv_us / 1e3,
         "note": "mrope_apply_ids_kv: Q in place, K rotated and V copied into 16-token paged caches at a random "
                 "slot permutation"}
+    # the same with a serving engine's layout: each 16-token block of a sequence in a random cache block,
+    # the tokens in order inside it (so a block's rows are written together)
+    blocks = torch.randperm(nb, device=dev).to(torch.int64)
+    t = torch.arange(cfg.n_tokens, device=dev, dtype=torch.int64)
+    slots_b = blocks[t // 16] * 16 + t % 16
+    kvb_us = timed(lambda: mr.apply_ids_kv(q, k, v, ids, cu, kc, vc, slots_b, synth.IMAGE_ID, workspace=ws),
+                   args.steps) * 1e6
+    out["64x4096-image-bf16-kv-cache-block-order"] = {
+        "tokens": cfg.n_tokens, "fused_kv_us": kvb_us, "tokens_per_s": cfg.n_tokens / (kvb_us / 1e6),
+        "gbs": algorithmic_bytes_fused_kv(cfg.n_tokens) / kvb_us / 1e3,
+        "note": "as above, slots filling randomly placed 16-token blocks in token order"}
     del q, k, v, kc, vc
     torch.cuda.empty_cache()
 
