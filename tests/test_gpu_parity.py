@@ -766,6 +766,22 @@ def test_frame_len_planes_and_fused(frame_len):
     np.testing.assert_array_equal(fl2.cpu().numpy(), want_fl)
     compare_heads(host_heads(q), qn, epl, "bf16", what=f"q frame_len={frame_len}")
     compare_heads(host_heads(k), kn, epl, "bf16", what=f"k frame_len={frame_len}")
+    # long sequences without planes_out: chunks wholly before the image, cutting the frame, and
+    # wholly after it take the per-chunk handover, whose shift depends on the frame length
+    lens, placed = [3000, 2000, 1300], [1000, 470, 500]
+    g = synth.rng(341 + frame_len, 4)
+    ids3 = np.concatenate([synth.prompt_ids(g, n, o) for n, o in zip(lens, placed)])
+    cu3 = np.zeros(4, np.int32)
+    cu3[1:] = np.cumsum(lens)
+    b3 = synth.Prefill(f"long-frame{frame_len}", ids3, cu3, placed, "bf16", seed=341, head_dim=64)
+    epl3, est3, eam3, eog3 = oracle.planes_chunk(ids3, cu3, MARKER, frame_len=frame_len)
+    qn3, kn3 = b3.qk()
+    q3, k3 = dev_heads(qn3, "bf16"), dev_heads(kn3, "bf16")
+    st3, am3, og3, _, _ = mr.apply_ids(q3, k3, i32(ids3), i32(cu3), MARKER, frame_len=frame_len)
+    np.testing.assert_array_equal(st3.cpu().numpy(), est3)
+    np.testing.assert_array_equal(am3.cpu().numpy(), eam3)
+    compare_heads(host_heads(q3), qn3, epl3, "bf16", what=f"long q frame_len={frame_len}")
+    compare_heads(host_heads(k3), kn3, epl3, "bf16", what=f"long k frame_len={frame_len}")
 
 
 def test_frame_len_pieces_cut_inside_the_tail():
