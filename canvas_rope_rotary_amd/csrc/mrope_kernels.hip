@@ -675,7 +675,16 @@ template <int IO>
 __device__ __forceinline__ void copy_span(const void *src, int64_t soff, void *dst, int64_t doff, int from,
                                           int head_dim, int l)
 {
-    for (int d = from + 8 * l; d < head_dim; d += 64) store8<IO>(dst, doff + d, load8<IO>(src, soff + d));
+    // up to four chunks per round trip: every load of a batch goes out before its stores (a lane
+    // past the head's end reads the head's last chunk and stores nothing)
+    for (int d0 = from + 8 * l; d0 - 8 * l < head_dim; d0 += 256) {
+        Raw8<IO> r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = load8<IO>(src, soff + min(d0 + 64 * i, head_dim - 8));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (d0 + 64 * i < head_dim) store8<IO>(dst, doff + d0 + 64 * i, r[i]);
+    }
 }
 
 __device__ __forceinline__ int64_t q_off(const Heads &hd, int64_t g, int h) { return g * hd.q_tok + h * hd.q_head; }
