@@ -364,6 +364,40 @@ def test_second_turn_long_pieces():
     assert fl.tolist() == [0, 0]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_positions_near_the_limit(dtype):
+    """Pieces whose positions run up to the supported limit (|plane| < 2^24): a text piece ending
+    at 2^24 - 1, an image piece whose frame sits just below it, and a piece after a carried origin
+    near it.  Angles reach ~1.7e7 rad; planes, scalars and rotation against the oracle, through
+    the two-launch and the fused (no planes_out) calls."""
+    top = (1 << 24) - 1
+    lens = [1200, 900, 700]
+    off = np.array([top + 1 - 1200, top + 1 - 900 - 300, top + 1 - 700], np.int32)
+    placed = [None, 500, None]
+    g = synth.rng(51, 4)
+    ids = np.concatenate([synth.prompt_ids(g, n, o) for n, o in zip(lens, placed)])
+    cu = np.zeros(4, np.int32)
+    cu[1:] = np.cumsum(lens)
+    oin = np.array([-1, -1, top - 5000], np.int32)
+    b = synth.Prefill("near-limit", ids, cu, placed, dtype, seed=51, head_dim=128)
+    epl, est, eam, eog = oracle.planes_chunk(ids, cu, MARKER, off, oin)
+    assert np.abs(epl).max() <= top
+    say(f"case: positions near 2^24 dtype={dtype} max plane={int(np.abs(epl).max())}")
+    qn, kn = b.qk()
+    pl, st, am, og, fl = mr.planes(i32(ids), i32(cu), MARKER, pos_offset=i32(off), origin_in=i32(oin))
+    np.testing.assert_array_equal(pl.cpu().numpy(), epl)
+    np.testing.assert_array_equal(st.cpu().numpy(), est)
+    np.testing.assert_array_equal(am.cpu().numpy(), eam)
+    np.testing.assert_array_equal(og.cpu().numpy(), eog)
+    q, k = dev_heads(qn, dtype), dev_heads(kn, dtype)
+    mr.apply(q, k, pl)
+    compare_heads(host_heads(q), qn, epl, dtype, what=f"near-limit q {dtype}")
+    compare_heads(host_heads(k), kn, epl, dtype, what=f"near-limit k {dtype}")
+    q2, k2 = dev_heads(qn, dtype), dev_heads(kn, dtype)
+    mr.apply_ids(q2, k2, i32(ids), i32(cu), MARKER, pos_offset=i32(off), origin_in=i32(oin))
+    assert torch.equal(q2, q) and torch.equal(k2, k)
+
+
 def test_origin_zero_negative_planes():
     ids = synth.prompt_ids(synth.rng(3, 9), 200, 0)
     b = synth.Prefill("o0", ids, np.array([0, 200], np.int32), [0], "bf16", seed=3)
