@@ -683,6 +683,93 @@ def test_graph_replays_with_new_inputs():
         _ = torch.randn(1000, device="cuda").sum().item()   # unrelated eager work between replays
 
 
+def test_graph_replays_fused_and_decode():
+    """The fused call (no planes_out, so chunks inside one sequence take the per-chunk handover; the
+    device epoch counter and its one-thread kernel under capture) and a decode step with V, captured
+    in one HIP graph.  New prompts, Q/K and decode inputs are copied into the captured buffers
+    between replays, with unrelated eager work in between; every replay matches the oracle."""
+    L, n = 6000, 6
+    batches = []
+    for seed in (81, 82, 83):
+        g = np.random.default_rng(seed)
+        cuts = np.sort(g.choice(np.arange(600, L - 600), size=n - 1, replace=False))
+        lens = np.diff(np.concatenate([[0], cuts, [L]]))
+        placed = [int(g.integers(0, max(1, m - 67))) if g.uniform() < 0.7 else None for m in lens]
+        gi = synth.rng(seed, 4)
+        ids = np.concatenate([synth.prompt_ids(gi, int(m), o) for m, o in zip(lens, placed)])
+        cu = np.zeros(n + 1, np.int32)
+        cu[1:] = np.cumsum(lens)
+        b = synth.Prefill(f"graphf{seed}", ids, cu, placed, "bf16", seed=seed)
+        gd = np.random.default_rng(seed + 100)
+        S = 96
+        pos = gd.integers(100, 30000, S).astype(np.int32)
+        amount = np.where(gd.uniform(size=S) < 0.5, 58, 0).astype(np.int32)
+        slots = gd.permutation(128 * 16)[:S].astype(np.int64)
+        dq = synth.to_dtype(gd.standard_normal((S, 8, 256)).astype(np.float32), "bf16")
+        dk = synth.to_dtype(gd.standard_normal((S, 2, 256)).astype(np.float32), "bf16")
+        dv = synth.to_dtype(gd.standard_normal((S, 2, 256)).astype(np.float32), "bf16")
+        batches.append((b,) + b.qk() + (pos, amount, slots, dq, dk, dv))
+    S = 96
+    ids_d = torch.zeros(L, dtype=torch.int32, device="cuda")
+    cu_d = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    q_d = torch.zeros((L, 8, 256), dtype=torch.bfloat16, device="cuda")
+    k_d = torch.zeros((L, 2, 256), dtype=torch.bfloat16, device="cuda")
+    st_d, am_d, og_d, fl_d = (torch.zeros(n, dtype=torch.int32, device="cuda") for _ in range(4))
+    pos_d, amt_d = (torch.zeros(S, dtype=torch.int32, device="cuda") for _ in range(2))
+    slots_d = torch.zeros(S, dtype=torch.int64, device="cuda")
+    dq_d = torch.zeros((S, 8, 256), dtype=torch.bfloat16, device="cuda")
+    dk_d, dv_d = (torch.zeros((S, 2, 256), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    kc = torch.zeros((128, 16, 2, 256), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    ws = mr.Workspace(L)
+
+    def load(bt):
+        b, qn, kn, pos, amount, slots, dq, dk, dv = bt
+        ids_d.copy_(i32(b.ids))
+        cu_d.copy_(i32(b.cu_seqlens))
+        q_d.copy_(dev_heads(qn, "bf16"))
+        k_d.copy_(dev_heads(kn, "bf16"))
+        pos_d.copy_(i32(pos))
+        amt_d.copy_(i32(amount))
+        slots_d.copy_(torch.from_numpy(slots).cuda())
+        dq_d.copy_(dev_heads(dq, "bf16"))
+        dk_d.copy_(dev_heads(dk, "bf16"))
+        dv_d.copy_(dev_heads(dv, "bf16"))
+
+    def body():
+        mr.apply_ids(q_d, k_d, ids_d, cu_d, MARKER, start=st_d, amount=am_d, origin=og_d, seq_flags=fl_d,
+                     workspace=ws)
+        mr.decode(dq_d, dk_d, pos_d, amt_d, kc, slots_d, v=dv_d, v_cache=vc)
+
+    load(batches[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()                     # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    for rep in range(6):
+        bt = batches[rep % 3]
+        b, qn, kn, pos, amount, slots, dq, dk, dv = bt
+        load(bt)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        epl, est, eam, eog = _oracle_planes(b)
+        for got, want, what in ((st_d, est, "start"), (am_d, eam, "amount"), (og_d, eog, "origin")):
+            np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"replay {rep} {what}")
+        compare_heads(host_heads(q_d), qn, epl, "bf16", what=f"replay {rep} q")
+        compare_heads(host_heads(k_d), kn, epl, "bf16", what=f"replay {rep} k")
+        plane = np.stack([pos - amount] * 3)
+        compare_heads(host_heads(dq_d), dq, plane, "bf16", what=f"replay {rep} decode q")
+        rows = torch.from_numpy(slots).cuda()
+        compare_heads(host_heads(kc.view(-1, 2, 256)[rows]), dk, plane, "bf16", what=f"replay {rep} decode k cache")
+        assert np.array_equal(host_heads(vc.view(-1, 2, 256)[rows]), dv), f"replay {rep} decode v cache"
+        _ = torch.randn(1000, device="cuda").sum().item()   # unrelated eager work between replays
+
+
 def test_bf16_out_of_place_and_wide_plane_stride():
     """bf16 out of place == in place (full heads written, inputs untouched); planes written into a
     wider [3, L + 37] buffer leave the extra columns alone."""
