@@ -374,7 +374,7 @@ def main():
                     help="copy: only a plain 1 GiB device copy, repeated (calibrates rocprofv3 HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the method shards by "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the method shards by "
               "sequence or head with no communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
