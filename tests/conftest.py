@@ -17,7 +17,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) where no GPU is visible, so `-m "not gpu"` and a plain run on
-    # a CPU-only host both stay green; on the GPU machine they run.
+    # a CPU-only host both stay green; where a GPU is visible they run.
     try:
         import torch
 
