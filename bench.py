@@ -152,6 +152,25 @@ def extras(args, dev, timed):
     del q, k, pl
     torch.cuda.empty_cache()
 
+    # out of place on the default batch: full heads read and written (the rotated dims by the
+    # rotation kernel, the rest by the copy launch)
+    log("extras: 64x4096 bf16 out of place")
+    qn, kn = cfg.qk()
+    q, k = heads(qn, "bf16"), heads(kn, "bf16")
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    pl, *_ = mr.planes(ids, cu, synth.IMAGE_ID)
+    ws = mr.Workspace(cfg.n_tokens, dev)
+    oa_us = timed(lambda: mr.apply(q, k, pl, q_out=qo, k_out=ko), args.steps) * 1e6
+    of_us = timed(lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, q_out=qo, k_out=ko, workspace=ws),
+                  args.steps) * 1e6
+    oop_bytes = cfg.n_tokens * (10 * 256 * 2 * 2 + 12)
+    out["64x4096-image-bf16-out-of-place"] = {
+        "tokens": cfg.n_tokens, "apply_us": oa_us, "fused_us": of_us, "apply_gbs": oop_bytes / oa_us / 1e3,
+        "note": "10,252 B/token for apply (full Q/K heads read and written, planes read); the fused call "
+                "reads 4 B of ids instead of 12 B of planes"}
+    del q, k, qo, ko, pl
+    torch.cuda.empty_cache()
+
     # chunked prefill: the 8 x 32,768 prompts fed as 4 pieces of 8,192 tokens per sequence, each piece
     # one fused call carrying pos_offset and the previous piece's origin (all pieces resident)
     cfg = synth.config3()

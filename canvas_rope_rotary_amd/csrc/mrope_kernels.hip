@@ -783,7 +783,8 @@ __device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int
 }
 
 // Rotate one token's chunks and store them: Q in place (or into q_out); K in place (or into k_out),
-// or with KV into the cache slot (nothing when the slot is outside the cache).
+// or with KV into the cache slot (nothing when the slot is outside the cache).  The other dims of
+// out-of-place heads are copied by their own launch (copy_rest_kernel).
 template <int IO, int NQ, int NK, bool KV>
 __device__ __forceinline__ void rotate_token_fixed(const Heads &hd, const PagedKV &pc, int64_t slot, int64_t g, int e0,
                                                    int l, const double (&c)[8], const double (&ss)[8],
@@ -801,15 +802,12 @@ __device__ __forceinline__ void rotate_token_fixed(const Heads &hd, const PagedK
         void *ko = hd.k_out ? hd.k_out : hd.k;
 #pragma unroll
         for (int h = 0; h < NK; ++h) store8_to<IO>(ko, k_off(hd, g, h) + e0, rotate_chunk<IO>(kv[h], c, ss), hd.k_out);
-        if (hd.q_out) {
-            for (int h = 0; h < NQ; ++h) copy_span<IO>(hd.q, q_off(hd, g, h), hd.q_out, q_off(hd, g, h), 64, hd.head_dim, l);
-            for (int h = 0; h < NK; ++h) copy_span<IO>(hd.k, k_off(hd, g, h), hd.k_out, k_off(hd, g, h), 64, hd.head_dim, l);
-        }
     }
 }
 
 // Any head counts and head_dim: one head at a time.  With a cache (pc.k_cache), K heads go whole
-// into the slot and V heads are copied there; slot is the token's (ignored without a cache).
+// into the slot and V heads are copied there; slot is the token's (ignored without a cache).  Out
+// of place, only the rotated dims are written here (copy_rest_kernel copies the others).
 template <int IO>
 __device__ __forceinline__ void rotate_token_any(const Heads &hd, const PagedKV &pc, int64_t slot, int64_t g, int e0,
                                                  int l, const double (&c)[8], const double (&ss)[8])
@@ -830,7 +828,6 @@ __device__ __forceinline__ void rotate_token_any(const Heads &hd, const PagedKV 
         }
         void *dst = isq ? (hd.q_out ? hd.q_out : hd.q) : (hd.k_out ? hd.k_out : hd.k);
         store8_to<IO>(dst, base + e0, rotate_chunk<IO>(load8<IO>(src, base + e0), c, ss), dst != src);
-        if (hd.q_out) copy_span<IO>(src, base, dst, base, 64, hd.head_dim, l);
     }
     if (cache_ok && pc.v) {
         for (int h = 0; h < hd.nk; ++h) copy_span<IO>(pc.v, v_off(pc, g, h), pc.v_cache, cache_off(pc, slot, h), 0, hd.head_dim, l);
@@ -955,6 +952,63 @@ __global__ __launch_bounds__(kBlock) void apply_any_kernel(Heads hd, Rotary rot,
     double c[8], ss[8];
     pair_sincos(lane_freq<false>(rot, m, half), planes[g], planes[ps + g], planes[2 * ps + g], c, ss);
     rotate_token_any<IO>(hd, pc, slot, g, e0, l, c, ss);
+}
+
+// Out of place: the dims a rotation leaves unchanged (64..head_dim of every head) are copied by a
+// launch of their own, shaped for a streaming copy.  Eight lanes take a head row, each every eighth
+// 16-byte chunk, so an instruction of eight lanes covers 128 contiguous bytes; a 256-dim row is one
+// batch of 3 chunks per lane (bf16, fp16; two batches for fp32).  Loads are unconditional (clamped
+// to the last row and chunk) and go out before any store; the grid covers the rows in one pass, so
+// the dispatcher balances the CUs.  Inside one token step of the rotation kernels this copy was a
+// load-to-store round trip per head: 64 x 4096 bf16 tokens out of place took 542 us (4.96 TB/s),
+// now 465 us (5.78 TB/s).  Two or four rows per lane took 474 and 508 us; persistent grids of 8 or
+// 32 workgroups per CU, 486 and 498 us.
+constexpr int kRestRows = 1;  // rows per lane and step
+constexpr int kRestBatch = 3; // chunks per lane and row per batch
+
+__global__ __launch_bounds__(kBlock) void copy_rest_kernel(const char *__restrict__ src, char *__restrict__ dst,
+                                                           int64_t tok_bytes, int64_t head_bytes, int nh, int nh_shift,
+                                                           int64_t n_rows, int64_t row_from, int n_chunks)
+{
+    const int l8 = threadIdx.x & 7;
+    constexpr int kRowsPerStep = kBlock / 8 * kRestRows;
+    const int64_t stride = (int64_t)gridDim.x * kRowsPerStep;
+    auto row_base = [&](int64_t row) {  // byte offset of the row's first copied chunk
+        int64_t t, h;
+        if (nh_shift >= 0) {
+            t = row >> nh_shift;
+            h = row & ((1 << nh_shift) - 1);
+        } else {
+            t = row / nh;
+            h = row - t * nh;
+        }
+        return t * tok_bytes + h * head_bytes + row_from;
+    };
+    for (int64_t r0 = (int64_t)blockIdx.x * kRowsPerStep + (threadIdx.x >> 3); r0 < n_rows; r0 += stride) {
+        int64_t base[kRestRows];
+        bool row_ok[kRestRows];
+#pragma unroll
+        for (int j = 0; j < kRestRows; ++j) {
+            const int64_t row = r0 + (int64_t)j * (kBlock / 8);
+            row_ok[j] = row < n_rows;
+            base[j] = row_base(row_ok[j] ? row : n_rows - 1);
+        }
+        for (int c0 = l8; c0 - l8 < n_chunks; c0 += 8 * kRestBatch) {
+            u32x4_t v[kRestRows][kRestBatch];
+#pragma unroll
+            for (int j = 0; j < kRestRows; ++j)
+#pragma unroll
+                for (int b = 0; b < kRestBatch; ++b)
+                    v[j][b] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4_t *>(src + base[j] + 16 * (int64_t)min(c0 + 8 * b, n_chunks - 1)));
+#pragma unroll
+            for (int j = 0; j < kRestRows; ++j)
+#pragma unroll
+                for (int b = 0; b < kRestBatch; ++b)
+                    if (row_ok[j] && c0 + 8 * b < n_chunks)
+                        __builtin_nontemporal_store(v[j][b], reinterpret_cast<u32x4_t *>(dst + base[j] + 16 * (int64_t)(c0 + 8 * b)));
+        }
+    }
 }
 
 // One wave per chunk, four chunks per workgroup.
@@ -1299,10 +1353,34 @@ static bool fixed_heads(const Heads &h, const PagedKV &pc, int io)
     return !pc.k_cache || (h.head_dim == 256 && io != kIoF32);
 }
 
+// Out of place: copy dims 64..head_dim of every Q and K head (see copy_rest_kernel).  Nothing to
+// do in place or when the heads hold only rotated dims.
+template <int IO>
+static hipError_t copy_rest(const Heads &h, hipStream_t st)
+{
+    constexpr int64_t es = IO == kIoF32 ? 4 : 2;
+    const int n_chunks = (int)((h.head_dim - 64) * es / 16);
+    if (!h.q_out || n_chunks <= 0 || h.n_tokens <= 0) return hipSuccess;
+    auto one = [&](const void *src, void *dst, int64_t tok, int64_t head, int nh) {
+        if (nh <= 0 || !dst) return;
+        const int64_t n_rows = h.n_tokens * nh;
+        const int shift = (nh & (nh - 1)) == 0 ? __builtin_ctz((unsigned)nh) : -1;
+        constexpr int64_t kRowsPerBlock = kBlock / 8 * kRestRows;
+        const int64_t need = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+        const unsigned blocks = (unsigned)(need < (1 << 20) ? need : (1 << 20));
+        copy_rest_kernel<<<blocks, kBlock, 0, st>>>(static_cast<const char *>(src), static_cast<char *>(dst), tok * es,
+                                                    head * es, nh, shift, n_rows, 64 * es, n_chunks);
+    };
+    one(h.q, h.q_out, h.q_tok, h.q_head, h.nq);
+    one(h.k, h.k_out, h.k_tok, h.k_head, h.nk);
+    return hipGetLastError();
+}
+
 template <int IO>
 static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t *planes, int64_t ps,
                                  const PagedKV &pc, hipStream_t st)
 {
+    if (const hipError_t ce = copy_rest<IO>(h, st); ce != hipSuccess) return ce;
     const int64_t groups = (h.n_tokens + kTokPerBlock - 1) / kTokPerBlock;
     if (fixed_heads(h, pc, IO)) {
         // Up to 16 grid-stride steps per workgroup the grid is persistent (two workgroups per CU).
@@ -1338,6 +1416,7 @@ hipError_t launch_apply(const Heads &h, const Rotary &r, const int32_t *planes, 
 template <int IO>
 static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, const PagedKV &pc, hipStream_t st)
 {
+    if (const hipError_t ce = copy_rest<IO>(h, st); ce != hipSuccess) return ce;
     const int64_t n_chunks = (h.n_tokens + kChunk - 1) / kChunk;
     // Small inputs split each chunk over up to 16 workgroups (down to one 32-token step each) while
     // that keeps the grid within two workgroups per CU; from 512 chunks on, one workgroup per chunk

@@ -798,6 +798,57 @@ def test_bf16_out_of_place_and_wide_plane_stride():
     np.testing.assert_array_equal(host_heads(q3), qn)
 
 
+def test_out_of_place_generic_shapes_and_padded_strides():
+    """Out of place with head counts that are not powers of two, other head dims and padded
+    strides: the outputs hold the rotated dims and the rest of every head bit for bit, the inputs
+    are untouched, and the padding between the heads and tokens of the outputs is never written."""
+    b = synth.random_batch(83, 24, max_len=240)
+    T = b.n_tokens
+    pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    sentinel = -3.0
+
+    def padded(nh, D, pad_h, pad_t, tdt):
+        """A [T, nh, D] view into a sentinel-filled buffer with padding after every head and token."""
+        buf = torch.full((T * (nh * (D + pad_h) + pad_t),), sentinel, dtype=tdt, device="cuda")
+        view = buf.as_strided((T, nh, D), (nh * (D + pad_h) + pad_t, D + pad_h, 1))
+        outside = torch.ones(buf.shape, dtype=torch.bool, device="cuda")
+        outside.as_strided((T, nh, D), view.stride()).fill_(False)
+        return buf, view, outside
+
+    for case, (dt, nq, nk, D, pad_h, pad_t) in enumerate((("f16", 3, 1, 136, 8, 16), ("f32", 3, 3, 1024, 4, 0),
+                                                          ("bf16", 8, 2, 256, 8, 64), ("bf16", 5, 0, 64, 0, 8),
+                                                          ("f32", 8, 2, 256, 0, 4))):
+        say(f"case: out of place {dt} {nq}+{nk} heads of {D}, head pad {pad_h}, token pad {pad_t}")
+        tdt = TORCH_DT[dt]
+        xq = synth.to_dtype(synth.normal(83, 70 + case, T * nq * D), dt).reshape(T, nq, D)
+        xk = synth.to_dtype(synth.normal(83, 80 + case, T * nk * D), dt).reshape(T, nk, D) if nk else None
+        _, q_in, _ = padded(nq, D, pad_h, pad_t, tdt)
+        q_in.copy_(dev_heads(xq, dt))
+        qo_buf, q_out, q_pad = padded(nq, D, pad_h, pad_t, tdt)
+        k_in = k_out = None
+        if nk:
+            _, k_in, _ = padded(nk, D, pad_h, pad_t, tdt)
+            k_in.copy_(dev_heads(xk, dt))
+            ko_buf, k_out, k_pad = padded(nk, D, pad_h, pad_t, tdt)
+        for fused in (False, True):
+            qo_buf.fill_(sentinel)
+            if nk:
+                ko_buf.fill_(sentinel)
+            if fused:
+                mr.apply_ids(q_in, k_in, i32(b.ids), i32(b.cu_seqlens), MARKER, q_out=q_out, k_out=k_out)
+            else:
+                mr.apply(q_in, k_in, pl, q_out=q_out, k_out=k_out)
+            what = f"{dt} {nq}+{nk}x{D} {'fused' if fused else 'apply'}"
+            np.testing.assert_array_equal(host_heads(q_in), xq, err_msg=f"{what}: q input changed")
+            compare_heads(host_heads(q_out), xq, epl, dt, what=f"{what} q_out")
+            assert bool((qo_buf[q_pad] == sentinel).all()), f"{what}: q_out padding written"
+            if nk:
+                np.testing.assert_array_equal(host_heads(k_in), xk, err_msg=f"{what}: k input changed")
+                compare_heads(host_heads(k_out), xk, epl, dt, what=f"{what} k_out")
+                assert bool((ko_buf[k_pad] == sentinel).all()), f"{what}: k_out padding written"
+
+
 def test_decode_fp32_and_generic_shapes():
     d = synth.config4(n_seqs=300, num_blocks=512)
     g = synth.rng(91, 5)
