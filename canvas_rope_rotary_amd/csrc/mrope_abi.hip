@@ -86,7 +86,7 @@ mrope_status check_heads(void *q, int64_t q_tok, int64_t q_head, int32_t nq, voi
 Heads make_heads(void *q, int64_t q_tok, int64_t q_head, int32_t nq, void *k, int64_t k_tok, int64_t k_head, int32_t nk,
                  int64_t n_tokens, int32_t head_dim, void *q_out, void *k_out)
 {
-    Heads h;
+    Heads h{};
     h.q = q;
     h.k = k;
     h.q_out = q_out;

@@ -542,7 +542,8 @@ __device__ __forceinline__ void store8(void *base, int64_t elem, const Raw8<IO> 
 // back by the launch: it carries the non-temporal hint.  Measured on 64 x 4096 bf16 tokens: the
 // fused K/V cache write 335 -> 281 us, mrope_apply_kv 328 -> 272 us, out of place 550 -> 542 us
 // (apply) and 559 -> 532 us (fused); a 4,096-sequence decode step 7.4 -> 6.7 us.  In-place stores
-// stay plain (with the hint they were slower, see load16_nt).
+// take the hint only when the launch writes more in place than the memory-side cache absorbs
+// (the fixed-head kernels' NTS argument, chosen by the host).
 template <int IO>
 __device__ __forceinline__ void store8_nt(void *base, int64_t elem, const Raw8<IO> &r)
 {
@@ -554,11 +555,12 @@ __device__ __forceinline__ void store8_nt(void *base, int64_t elem, const Raw8<I
         __builtin_nontemporal_store((u32x4_t){r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w}, p + i);
 }
 
-// Plain store in place, non-temporal store into another buffer.
-template <int IO>
-__device__ __forceinline__ void store8_to(void *base, int64_t elem, const Raw8<IO> &r, bool other)
+// Non-temporal or plain store, chosen at compile time: with a run-time choice the compiler merges
+// the two stores of the branches into one plain store (the hint is lost).
+template <int IO, bool NT>
+__device__ __forceinline__ void store8_as(void *base, int64_t elem, const Raw8<IO> &r)
 {
-    if (other) store8_nt<IO>(base, elem, r);
+    if constexpr (NT) store8_nt<IO>(base, elem, r);
     else store8<IO>(base, elem, r);
 }
 
@@ -784,15 +786,16 @@ __device__ __forceinline__ void load_token_fixed(const Heads &hd, int64_t g, int
 
 // Rotate one token's chunks and store them: Q in place (or into q_out); K in place (or into k_out),
 // or with KV into the cache slot (nothing when the slot is outside the cache).  The other dims of
-// out-of-place heads are copied by their own launch (copy_rest_kernel).
-template <int IO, int NQ, int NK, bool KV>
+// out-of-place heads are copied by their own launch (copy_rest_kernel).  NTS: Q and K stores (in
+// place or out of place) carry the non-temporal hint; cache rows always do.
+template <int IO, int NQ, int NK, bool KV, bool NTS>
 __device__ __forceinline__ void rotate_token_fixed(const Heads &hd, const PagedKV &pc, int64_t slot, int64_t g, int e0,
                                                    int l, const double (&c)[8], const double (&ss)[8],
                                                    const Raw8<IO> (&qv)[NQ], const Raw8<IO> (&kv)[NK])
 {
     void *qo = hd.q_out ? hd.q_out : hd.q;
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) store8_to<IO>(qo, q_off(hd, g, h) + e0, rotate_chunk<IO>(qv[h], c, ss), hd.q_out);
+    for (int h = 0; h < NQ; ++h) store8_as<IO, NTS>(qo, q_off(hd, g, h) + e0, rotate_chunk<IO>(qv[h], c, ss));
     if constexpr (KV) {
         if (slot_ok(pc, slot)) {
 #pragma unroll
@@ -801,7 +804,7 @@ __device__ __forceinline__ void rotate_token_fixed(const Heads &hd, const PagedK
     } else {
         void *ko = hd.k_out ? hd.k_out : hd.k;
 #pragma unroll
-        for (int h = 0; h < NK; ++h) store8_to<IO>(ko, k_off(hd, g, h) + e0, rotate_chunk<IO>(kv[h], c, ss), hd.k_out);
+        for (int h = 0; h < NK; ++h) store8_as<IO, NTS>(ko, k_off(hd, g, h) + e0, rotate_chunk<IO>(kv[h], c, ss));
     }
 }
 
@@ -827,7 +830,7 @@ __device__ __forceinline__ void rotate_token_any(const Heads &hd, const PagedKV 
             continue;
         }
         void *dst = isq ? (hd.q_out ? hd.q_out : hd.q) : (hd.k_out ? hd.k_out : hd.k);
-        store8_to<IO>(dst, base + e0, rotate_chunk<IO>(load8<IO>(src, base + e0), c, ss), dst != src);
+        store8<IO>(dst, base + e0, rotate_chunk<IO>(load8<IO>(src, base + e0), c, ss));
     }
     if (cache_ok && pc.v) {
         for (int h = 0; h < hd.nk; ++h) copy_span<IO>(pc.v, v_off(pc, g, h), pc.v_cache, cache_off(pc, slot, h), 0, hd.head_dim, l);
@@ -846,7 +849,7 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f7
 // is sized to the chip by the host).  Each 8-lane group prefetches its next token's planes and head
 // chunks before it rotates and stores the current one, so loads stay in flight while the sincos
 // and rotation math runs.  Control flow is wave-uniform.
-template <int IO, int NQ, int NK>
+template <int IO, int NQ, int NK, bool NTS>
 __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
                                                        int64_t ps)
 {
@@ -886,7 +889,7 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
         if (ok) {
             double c[8], ss[8];
             pair_sincos(lf, pt, ph, pw, c, ss);
-            rotate_token_fixed<IO, NQ, NK, false>(hd, PagedKV{}, -1, g, e0, l, c, ss, qv, kv);
+            rotate_token_fixed<IO, NQ, NK, false, NTS>(hd, PagedKV{}, -1, g, e0, l, c, ss, qv, kv);
         }
         G = Gn;
         g = gn;
@@ -906,7 +909,7 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
 // the stores (Q in place, K and V into the cache slot, nothing for a slot outside the cache).  No
 // prefetch of the next token: 24 chunks a lane already keep enough bytes in flight per wave, and
 // the registers of a second set would halve the waves per SIMD.
-template <int IO, int NQ, int NK>
+template <int IO, int NQ, int NK, bool NTS>
 __device__ __forceinline__ void kv_token(const Heads &hd, const PagedKV &pc, const LaneFreq &lf, int64_t g, int e0,
                                          int l, int32_t pt, int32_t ph, int32_t pw, int64_t slot)
 {
@@ -916,12 +919,12 @@ __device__ __forceinline__ void kv_token(const Heads &hd, const PagedKV &pc, con
     load_copy_chunks<IO, NK>(hd, pc, g, l, cc);
     double c[8], ss[8];
     pair_sincos(lf, pt, ph, pw, c, ss);
-    rotate_token_fixed<IO, NQ, NK, true>(hd, pc, slot, g, e0, l, c, ss, qv, kv);
+    rotate_token_fixed<IO, NQ, NK, true, NTS>(hd, pc, slot, g, e0, l, c, ss, qv, kv);
     if (slot_ok(pc, slot)) store_copy_chunks<IO, NK>(pc, slot, l, cc);
 }
 
 // mrope_apply_kv, fixed head counts: a grid-stride loop over 8-token groups like apply_kernel.
-template <int IO, int NQ, int NK>
+template <int IO, int NQ, int NK, bool NTS>
 __global__ __launch_bounds__(kBlock) void apply_kv_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
                                                           int64_t ps, PagedKV pc)
 {
@@ -934,7 +937,7 @@ __global__ __launch_bounds__(kBlock) void apply_kv_kernel(Heads hd, Rotary rot, 
     for (int64_t G = (int64_t)blockIdx.x * kTokPerBlock + (tid >> 6) * 8; G < hd.n_tokens; G += stride) {
         const int64_t g = G + sub;
         if (g < hd.n_tokens)
-            kv_token<IO, NQ, NK>(hd, pc, lf, g, e0, l, planes[g], planes[ps + g], planes[2 * ps + g], pc.slots[g]);
+            kv_token<IO, NQ, NK, NTS>(hd, pc, lf, g, e0, l, planes[g], planes[ps + g], planes[2 * ps + g], pc.slots[g]);
     }
 }
 
@@ -1034,7 +1037,7 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
 // LDS meanwhile, then the workgroup rotates its part 32 tokens at a time, each 8-lane group
 // prefetching its next token before rotating the current one.  KV as in apply_kernel (fixed head
 // counts); the generic path writes the cache when pc.k_cache is set.
-template <int IO, int NQ, int NK, bool KV>
+template <int IO, int NQ, int NK, bool KV, bool NTS>
 __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, PagedKV pc, int part_log)
 {
     __shared__ int32_t s_pl[3][kChunk];
@@ -1151,13 +1154,13 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         const int64_t gn = g + kTokPerBlock;
         double c[8], ss[8];
         if constexpr (kFixed && KV) {
-            if (ok) kv_token<IO, AQ, AK>(hd, pc, lf, g, e0, l, pt, ph, pw, pc.slots[g]);
+            if (ok) kv_token<IO, AQ, AK, NTS>(hd, pc, lf, g, e0, l, pt, ph, pw, pc.slots[g]);
         } else if constexpr (kFixed) {
             Raw8<IO> qn[AQ], kn[AK];
             if (gn < r_end) load_token_fixed<IO, AQ, AK>(hd, gn, e0, qn, kn);
             if (ok) {
                 pair_sincos(lf, pt, ph, pw, c, ss);
-                rotate_token_fixed<IO, AQ, AK, false>(hd, pc, -1, g, e0, l, c, ss, qv, kv);
+                rotate_token_fixed<IO, AQ, AK, false, NTS>(hd, pc, -1, g, e0, l, c, ss, qv, kv);
             }
 #pragma unroll
             for (int h = 0; h < AQ; ++h) qv[h] = qn[h];
@@ -1353,6 +1356,25 @@ static bool fixed_heads(const Heads &h, const PagedKV &pc, int io)
     return !pc.k_cache || (h.head_dim == 256 && io != kIoF32);
 }
 
+// The fixed-head kernels' Q/K stores take the non-temporal hint (the NTS template argument) out of
+// place, and in place when the launch writes more than this in place: up to about there the 256 MB
+// memory-side cache absorbs the written lines and plain stores are faster, beyond it the hint is.
+// Measured (bf16, 8 + 2 heads; plain vs hinted): mrope_apply 109 vs 131 us at 262,144 tokens
+// (335 MB written in place), 164 vs 159 us at 327,680 (419 MB), 202 vs 190 us at 393,216, 527 vs
+// 498 us at 1,048,576 (fused: 531 vs 505); the fused K/V cache write (Q in place) 281 vs 323 us at
+// 262,144 (268 MB), 495 vs 480 us at 393,216 (403 MB), 1,318 vs 1,281 us at 1,048,576.  fp32 at
+// 262,144 tokens (671 MB): equal.  Out of place (64 x 4096 bf16) 464 vs 459 us.
+constexpr int64_t kNtInplaceBytes = 352ll << 20;
+
+template <int IO>
+static bool nt_stores(const Heads &h, const PagedKV &pc)
+{
+    constexpr int64_t es = IO == kIoF32 ? 4 : 2;
+    if (h.q_out) return true;
+    const int64_t heads = h.nq + (pc.k_cache ? 0 : h.nk);
+    return h.n_tokens * heads * 64 * es > kNtInplaceBytes;
+}
+
 // Out of place: copy dims 64..head_dim of every Q and K head (see copy_rest_kernel).  Nothing to
 // do in place or when the heads hold only rotated dims.
 template <int IO>
@@ -1381,6 +1403,7 @@ static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t 
                                  const PagedKV &pc, hipStream_t st)
 {
     if (const hipError_t ce = copy_rest<IO>(h, st); ce != hipSuccess) return ce;
+    const bool nts = nt_stores<IO>(h, pc);
     const int64_t groups = (h.n_tokens + kTokPerBlock - 1) / kTokPerBlock;
     if (fixed_heads(h, pc, IO)) {
         // Up to 16 grid-stride steps per workgroup the grid is persistent (two workgroups per CU).
@@ -1392,11 +1415,13 @@ static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t 
         const unsigned blocks = (unsigned)(groups < cap ? groups : cap);
         if constexpr (IO != kIoF32) {
             if (pc.k_cache) {
-                apply_kv_kernel<IO, 8, 2><<<blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
+                if (nts) apply_kv_kernel<IO, 8, 2, true><<<blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
+                else apply_kv_kernel<IO, 8, 2, false><<<blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
                 return hipGetLastError();
             }
         }
-        apply_kernel<IO, 8, 2><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
+        if (nts) apply_kernel<IO, 8, 2, true><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
+        else apply_kernel<IO, 8, 2, false><<<blocks, kBlock, 0, st>>>(h, r, planes, ps);
     } else {
         apply_any_kernel<IO><<<(unsigned)groups, kBlock, 0, st>>>(h, r, planes, ps, pc);
     }
@@ -1417,6 +1442,7 @@ template <int IO>
 static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan &s, const PagedKV &pc, hipStream_t st)
 {
     if (const hipError_t ce = copy_rest<IO>(h, st); ce != hipSuccess) return ce;
+    const bool nts = nt_stores<IO>(h, pc);
     const int64_t n_chunks = (h.n_tokens + kChunk - 1) / kChunk;
     // Small inputs split each chunk over up to 16 workgroups (down to one 32-token step each) while
     // that keeps the grid within two workgroups per CU; from 512 chunks on, one workgroup per chunk
@@ -1430,13 +1456,15 @@ static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan
         bool done = false;
         if constexpr (IO != kIoF32) {
             if (pc.k_cache) {
-                apply_ids_kernel<IO, 8, 2, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+                if (nts) apply_ids_kernel<IO, 8, 2, true, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+                else apply_ids_kernel<IO, 8, 2, true, false><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
                 done = true;
             }
         }
-        if (!done) apply_ids_kernel<IO, 8, 2, false><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+        if (!done && nts) apply_ids_kernel<IO, 8, 2, false, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+        if (!done && !nts) apply_ids_kernel<IO, 8, 2, false, false><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
     } else {
-        apply_ids_kernel<IO, 0, 0, false><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+        apply_ids_kernel<IO, 0, 0, false, false><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
     }
     const hipError_t e = hipGetLastError();
     return e != hipSuccess ? e : bump_if_device_epoch(s, st);

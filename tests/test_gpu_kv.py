@@ -208,3 +208,40 @@ def test_apply_ids_kv_full_size_sampled():
     all_ok = (slots >= 0) & (slots < S)
     written = kc.view(S, 2 * 256)[torch.from_numpy(slots[all_ok]).cuda()].abs().amax(dim=1)
     assert int((written == 0).sum()) == 0
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_kv_past_the_store_hint_size(fused):
+    """96 x 4096 bf16 tokens write 403 MB of Q in place, past the size from which the cache-writing
+    kernels' Q stores take the non-temporal hint: Q and the cache rows on sampled tokens."""
+    origins = [int(o) for o in np.random.default_rng(251).integers(0, 513, size=96)]
+    b = synth._batch("96x4096-image-bf16", 251, [4096] * 96, origins, "bf16")
+    T = b.n_tokens
+    say(f"case: kv past the store hint size tokens={T} fused={fused}")
+    qn, kn = b.qk()
+    vn = v_heads(b)
+    slots, nb = make_slots(252, T, room=1.1, neg=0.001, past=0.001)
+    q, k, v = dev_heads(qn, "bf16"), dev_heads(kn, "bf16"), dev_heads(vn, "bf16")
+    kc = new_cache(nb, 16, 2, 256, "bf16", 0.0)
+    vc = new_cache(nb, 16, 2, 256, "bf16", 0.0)
+    epl, est, eam, eog = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    sl_dev = torch.from_numpy(slots).cuda()
+    if fused:
+        st, am, og, _, _ = mr.apply_ids_kv(q, k, v, i32(b.ids), i32(b.cu_seqlens), kc, vc, sl_dev, MARKER)
+        np.testing.assert_array_equal(st.cpu().numpy(), est)
+        np.testing.assert_array_equal(og.cpu().numpy(), eog)
+    else:
+        mr.apply_kv(q, k, v, i32(epl), kc, vc, sl_dev)
+    idx = set(np.random.default_rng(253).integers(0, T, size=4000).tolist())
+    for s in range(b.n_seqs):
+        lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
+        idx.update((lo, hi - 1))
+        idx.update(range(lo + int(eog[s]), min(lo + int(eog[s]) + 70, hi)))
+    idx = np.array(sorted(idx), np.int64)
+    compare_heads(host_heads(q[torch.from_numpy(idx).cuda()]), qn[idx], epl[:, idx], "bf16", what="q sampled")
+    S = nb * 16
+    sl = slots[idx]
+    ok = (sl >= 0) & (sl < S)
+    rows = torch.from_numpy(sl[ok]).cuda()
+    compare_heads(host_heads(kc.view(S, 2, 256)[rows]), kn[idx[ok]], epl[:, idx[ok]], "bf16", what="k cache sampled")
+    np.testing.assert_array_equal(host_heads(vc.view(S, 2, 256)[rows]), vn[idx[ok]])

@@ -542,6 +542,18 @@ def test_config5_full_ragged_fused():
     _full_prefill(synth.config5(), fused=True)
 
 
+def _image_batch(name, seed, n_seqs, length, dtype):
+    origins = [int(o) for o in np.random.default_rng(seed).integers(0, 513, size=n_seqs)]
+    return synth._batch(name, seed, [length] * n_seqs, origins, dtype)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_fp32_past_the_store_hint_size(fused):
+    """40 x 4096 fp32 tokens write 419 MB in place, past the size from which the rotation kernels'
+    stores take the non-temporal hint: the hinted kernels against the oracle on sampled tokens."""
+    _full_prefill(_image_batch("40x4096-image-f32", 12, 40, 4096, "f32"), fused=fused)
+
+
 def test_config4_decode_paged():
     d = synth.config4()
     say(f"case: {d.name}")
