@@ -166,7 +166,8 @@ mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t
  *            more to the 16-bit type.
  * q_out, k_out  NULL: rotate in place (dims >= rot_dim are never read or written).  Otherwise the
  *            full heads are written there, with the same strides as q / k (no aliasing with the
- *            inputs).  Both NULL or both non-NULL (k_out may be NULL when n_k_heads == 0).
+ *            inputs): a first launch copies dims >= rot_dim, the rotation launch writes the rest.
+ *            Both NULL or both non-NULL (k_out may be NULL when n_k_heads == 0).
  * Alignment: q, k, q_out, k_out 16-byte aligned; strides multiples of 8 (bf16, fp16) or 4 (fp32).
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,
@@ -176,7 +177,8 @@ mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, i
 
 /* ---------------------------------------------------------------------------------------------
  * mrope_apply_ids -- planes derivation and rotation fused in ONE launch (plus a one-thread kernel
- * when epoch == 0): ids -> first marker per sequence -> planes (kept on chip) -> rotate Q and K.
+ * when epoch == 0, and out of place the copy launch described under mrope_apply): ids -> first
+ * marker per sequence -> planes (kept on chip) -> rotate Q and K.
  * Arguments as in mrope_planes and mrope_apply; planes_out (nullable) additionally receives the
  * planes ([3][plane_stride]).  n_tokens must equal cu_seqlens[n_seqs].  The Q/K loads of a chunk
  * are issued while its scan runs.
