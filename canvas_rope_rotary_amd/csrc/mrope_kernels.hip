@@ -540,8 +540,8 @@ __device__ __forceinline__ void store8(void *base, int64_t elem, const Raw8<IO> 
 
 // A store into another buffer than the one read (a cache row, an out-of-place head) is not read
 // back by the launch: it carries the non-temporal hint.  Measured on 64 x 4096 bf16 tokens: the
-// fused K/V cache write 335 -> 281 us, mrope_apply_kv 328 -> 272 us, out of place 550 -> 542 us
-// (apply) and 559 -> 532 us (fused); a 4,096-sequence decode step 7.4 -> 6.7 us.  In-place stores
+// fused K/V cache write 335 -> 281 us, mrope_apply_kv 328 -> 272 us; a 4,096-sequence decode step
+// 7.4 -> 6.7 us (out of place: see copy_rest_kernel).  In-place stores
 // take the hint only when the launch writes more in place than the memory-side cache absorbs
 // (the fixed-head kernels' NTS argument, chosen by the host).
 template <int IO>
@@ -696,7 +696,7 @@ __device__ __forceinline__ Raw8<IO> rotate_chunk(const Raw8<IO> &own, const doub
 }
 
 // Copy this lane's share of the 8-element chunks of one head from dim `from` on: src at soff, dst
-// at doff (element offsets of the head's dim 0).  Out-of-place calls and cache writes.
+// at doff (element offsets of the head's dim 0).  The generic kernels' cache writes.
 template <int IO>
 __device__ __forceinline__ void copy_span(const void *src, int64_t soff, void *dst, int64_t doff, int from,
                                           int head_dim, int l)
