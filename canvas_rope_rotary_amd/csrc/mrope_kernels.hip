@@ -1407,11 +1407,13 @@ static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t 
     const int64_t groups = (h.n_tokens + kTokPerBlock - 1) / kTokPerBlock;
     if (fixed_heads(h, pc, IO)) {
         // Up to 16 grid-stride steps per workgroup the grid is persistent (two workgroups per CU).
-        // Beyond that, workgroups of two steps each, many more than fit at once: the dispatcher hands
-        // a freed slot the next workgroup, which balances the unequal rates of the CUs (1,048,576
-        // tokens: 540 -> 524 us; at 262,144 tokens the persistent grid is 3 % faster).
+        // Beyond that, one step per workgroup, many more workgroups than fit at once: the
+        // dispatcher hands a freed slot the next workgroup, which balances the unequal rates of the
+        // CUs.  Measured (bf16): 1,048,576 tokens 498 us with two-step workgroups, 470 us with one
+        // step, 524 us persistent; 393,216 tokens 189 -> 175 us.  At 262,144 tokens (16 steps) the
+        // persistent grid is 3 % faster than one-step workgroups.
         const int64_t persistent = (int64_t)compute_units() * kApplyBlocksPerCU;
-        const int64_t cap = groups > 16 * persistent ? (groups + 1) / 2 : persistent;
+        const int64_t cap = groups > 16 * persistent ? groups : persistent;
         const unsigned blocks = (unsigned)(groups < cap ? groups : cap);
         if constexpr (IO != kIoF32) {
             if (pc.k_cache) {
