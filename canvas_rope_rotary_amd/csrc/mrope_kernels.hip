@@ -1417,8 +1417,11 @@ static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t 
         const unsigned blocks = (unsigned)(groups < cap ? groups : cap);
         if constexpr (IO != kIoF32) {
             if (pc.k_cache) {
-                if (nts) apply_kv_kernel<IO, 8, 2, true><<<blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
-                else apply_kv_kernel<IO, 8, 2, false><<<blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
+                // the cache-writing loop has no prefetch: one step per workgroup at every size
+                // (64 x 4096 tokens: 271 -> 266 us against the persistent grid)
+                const unsigned kv_blocks = (unsigned)groups;
+                if (nts) apply_kv_kernel<IO, 8, 2, true><<<kv_blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
+                else apply_kv_kernel<IO, 8, 2, false><<<kv_blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
                 return hipGetLastError();
             }
         }
