@@ -697,9 +697,11 @@ def test_graph_replays_with_new_inputs():
 
 def test_graph_replays_fused_and_decode():
     """The fused call (no planes_out, so chunks inside one sequence take the per-chunk handover; the
-    device epoch counter and its one-thread kernel under capture) and a decode step with V, captured
-    in one HIP graph.  New prompts, Q/K and decode inputs are copied into the captured buffers
-    between replays, with unrelated eager work in between; every replay matches the oracle."""
+    device epoch counter and its one-thread kernel under capture), the same call out of place first
+    (its copy launch and its rotation launch) and a decode step with V, captured in one HIP graph.
+    New prompts, Q/K and decode inputs are copied into the captured buffers between replays, with
+    unrelated eager work in between; every replay matches the oracle, and the out-of-place heads
+    equal the in-place result."""
     L, n = 6000, 6
     batches = []
     for seed in (81, 82, 83):
@@ -733,6 +735,7 @@ def test_graph_replays_fused_and_decode():
     dk_d, dv_d = (torch.zeros((S, 2, 256), dtype=torch.bfloat16, device="cuda") for _ in range(2))
     kc = torch.zeros((128, 16, 2, 256), dtype=torch.bfloat16, device="cuda")
     vc = torch.zeros_like(kc)
+    qo_d, ko_d = torch.zeros_like(q_d), torch.zeros_like(k_d)
     ws = mr.Workspace(L)
 
     def load(bt):
@@ -749,6 +752,7 @@ def test_graph_replays_fused_and_decode():
         dv_d.copy_(dev_heads(dv, "bf16"))
 
     def body():
+        mr.apply_ids(q_d, k_d, ids_d, cu_d, MARKER, q_out=qo_d, k_out=ko_d, workspace=ws)
         mr.apply_ids(q_d, k_d, ids_d, cu_d, MARKER, start=st_d, amount=am_d, origin=og_d, seq_flags=fl_d,
                      workspace=ws)
         mr.decode(dq_d, dk_d, pos_d, amt_d, kc, slots_d, v=dv_d, v_cache=vc)
@@ -774,6 +778,7 @@ def test_graph_replays_fused_and_decode():
             np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"replay {rep} {what}")
         compare_heads(host_heads(q_d), qn, epl, "bf16", what=f"replay {rep} q")
         compare_heads(host_heads(k_d), kn, epl, "bf16", what=f"replay {rep} k")
+        assert torch.equal(qo_d, q_d) and torch.equal(ko_d, k_d), f"replay {rep}: out of place differs from in place"
         plane = np.stack([pos - amount] * 3)
         compare_heads(host_heads(dq_d), dq, plane, "bf16", what=f"replay {rep} decode q")
         rows = torch.from_numpy(slots).cuda()
