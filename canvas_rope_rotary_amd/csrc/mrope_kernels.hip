@@ -1031,9 +1031,9 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
                });
 }
 
-// Fused: one chunk per workgroup, or for small inputs one part of a chunk (2^part_log parts, each
-// workgroup repeating the chunk's scan, so more workgroups share the work and each has fewer
-// sequential steps).  Every lane issues the Q/K loads of its first token, wave 0 scans the chunk into
+// Fused: one part of a 512-token chunk per workgroup (2^part_log parts: halves for large inputs,
+// down to 32-token parts for small ones; each workgroup repeats the chunk's scan, so more
+// workgroups share the work and each has fewer sequential steps).  Every lane issues the Q/K loads of its first token, wave 0 scans the chunk into
 // LDS meanwhile, then the workgroup rotates its part 32 tokens at a time, each 8-lane group
 // prefetching its next token before rotating the current one.  KV as in apply_kernel (fixed head
 // counts); the generic path writes the cache when pc.k_cache is set.
@@ -1061,10 +1061,11 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
 
     // Wave 0 puts the scan's loads in flight first; only then (first barrier, without a fence: no
     // wait) do the waves issue their first token's Q/K loads.  Issued the other way round, the scan's
-    // first round trip queued behind all Q/K loads of the chip (7 of the scan's 11.5 us).  With a
-    // split chunk wave 0 issues its own first token only after the scan: the scan's later waits
-    // would otherwise include those loads (small inputs: 1 x 4096 tokens 17.8 -> 17.2 us, 4 x 4096
-    // 28.4 -> 25.7); on a full grid issuing them early is 1-2 us faster.
+    // first round trip queued behind all Q/K loads of the chip (7 of the scan's 11.5 us).  Wave 0
+    // issues its own first token only after the scan: the scan's later waits would otherwise
+    // include those loads (1 x 4096 tokens 17.8 -> 17.2 us, 4 x 4096 28.4 -> 25.7).  Issued early,
+    // 8 x 32768 tokens took 122 us instead of 118: with long sequences a chunk's look-back waits on
+    // its predecessors' look-backs, and each waited behind its wave 0's loads.
     const bool w0_late = part_log > 0;
     int64_t g = r0 + (tid >> 3);
     Raw8<IO> qv[AQ], kv[AK];
@@ -1450,12 +1451,16 @@ static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan
     const bool nts = nt_stores<IO>(h, pc);
     const int64_t n_chunks = (h.n_tokens + kChunk - 1) / kChunk;
     // Small inputs split each chunk over up to 16 workgroups (down to one 32-token step each) while
-    // that keeps the grid within two workgroups per CU; from 512 chunks on, one workgroup per chunk
-    // (splitting there measured slower: the repeated scans and the extra workgroups cost more than
-    // the balancing gains).
+    // that keeps the grid within two workgroups per CU.  Larger ones split each chunk in two: with
+    // one workgroup per chunk, a chunk count between one and two grids of resident workgroups left
+    // slots idle or ran a partial second round, and halves let the dispatcher even the rounds out.
+    // Measured (bf16, back to back): the 64 x 4096 step 116.2 -> 113.0 us (200 warm-up launches),
+    // 163,840 tokens (64 sequences) 92 -> 81 us, 196,608 104 -> 99, 1,048,576 ragged 509 -> 501,
+    // 8 x 32768 unchanged (118 us).  Four parts cost more than they balance (262,144 tokens: 130).
     const int64_t target = (int64_t)compute_units() * 2;
     int part_log = 0;
     while (part_log < 4 && (n_chunks << (part_log + 1)) <= target) ++part_log;
+    if (part_log == 0) part_log = 1;
     const unsigned blocks = (unsigned)(n_chunks << part_log);
     if (fixed_heads(h, pc, IO)) {
         bool done = false;
@@ -1478,6 +1483,15 @@ static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan
 hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, const PagedKV &pc, int io,
                             hipStream_t stream)
 {
+    // With the planes wanted in memory anyway (planes_out) and past the size where mrope_apply
+    // takes one step per workgroup, the scan writes planes_out and the rotation reads it back: one
+    // workgroup per chunk cannot use that grid.  Measured (bf16): 1,048,576 ragged tokens 17.5 +
+    // 465 us against 508 us fused; 524,288 tokens ~243 against 261 us.
+    const int64_t one_step_from = (int64_t)compute_units() * kApplyBlocksPerCU * 16 * kTokPerBlock;
+    if (s.planes && fixed_heads(h, pc, io) && h.n_tokens > one_step_from) {
+        const hipError_t e = launch_planes(s, stream);
+        return e != hipSuccess ? e : launch_apply(h, r, s.planes, s.plane_stride, pc, io, stream);
+    }
     switch (io) {
     case kIoBF16: return apply_ids_dispatch<kIoBF16>(h, r, s, pc, stream);
     case kIoF16: return apply_ids_dispatch<kIoF16>(h, r, s, pc, stream);
