@@ -198,6 +198,15 @@ int main(void)
     oracle_round_bf16(eq, eqb, nq);
     oracle_round_bf16(ek, ekb, nk);
     void *d_qb = dev_copy(qb, 2 * nq), *d_kb = dev_copy(kb, 2 * nk);
+    /* out of place first (a copy launch for dims 64..255, then the rotation launch); the in-place
+       call below then starts from the same, untouched inputs */
+    void *d_qo, *d_ko;
+    HIP_OK(hipMalloc(&d_qo, 2 * nq));
+    HIP_OK(hipMalloc(&d_ko, 2 * nk));
+    st = mrope_apply_ids(d_qb, NQ * HD, HD, NQ, d_kb, NK * HD, HD, NK, T, HD, ROT, MROPE_BF16, THETA, d_qo, d_ko,
+                         d_ids, d_cu, n_seqs, MARKER, 0, NULL, NULL, NULL, T, NULL, NULL, NULL, NULL, d_ws, ws_bytes,
+                         3u, stream);
+    report("mrope_apply_ids out of place status", st == MROPE_OK, st == MROPE_OK ? "" : mrope_last_error());
     st = mrope_apply_ids(d_qb, NQ * HD, HD, NQ, d_kb, NK * HD, HD, NK, T, HD, ROT, MROPE_BF16, THETA, NULL, NULL,
                          d_ids, d_cu, n_seqs, MARKER, 0, NULL, NULL, NULL, T, d_st, d_am, d_og, NULL, d_ws, ws_bytes,
                          2u, stream);
@@ -220,6 +229,10 @@ int main(void)
     }
     snprintf(detail, sizeof detail, "max %d ulp, %lld elements off by one", worst_ulp, (long long)off_by_one);
     report("bf16 fused rotation within 1 ulp", worst_ulp <= 1, detail);
+    uint16_t *qo = malloc(2 * nq), *ko = malloc(2 * nk);
+    HIP_OK(hipMemcpy(qo, d_qo, 2 * nq, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(ko, d_ko, 2 * nk, hipMemcpyDeviceToHost));
+    report("bf16 out of place equals in place, bit for bit", !memcmp(qo, qb, 2 * nq) && !memcmp(ko, kb, 2 * nk), "");
 
     /* 3. a host-detected error */
     st = mrope_apply(NULL, NQ * HD, HD, NQ, d_k, NK * HD, HD, NK, T, HD, ROT, MROPE_F32, d_pl, T, THETA, NULL, NULL,

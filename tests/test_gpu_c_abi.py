@@ -21,4 +21,4 @@ def test_plain_c_caller():
     assert r.returncode == 0, r.stdout + r.stderr
     lines = r.stdout.strip().splitlines()
     assert lines[-1] == "ALL PASSED" and not any(l.startswith("FAIL") for l in lines)
-    assert sum(l.startswith("PASS") for l in lines) == 11, lines
+    assert sum(l.startswith("PASS") for l in lines) == 13, lines
