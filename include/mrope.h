@@ -180,8 +180,11 @@ mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, i
  * when epoch == 0, and out of place the copy launch described under mrope_apply): ids -> first
  * marker per sequence -> planes (kept on chip) -> rotate Q and K.
  * Arguments as in mrope_planes and mrope_apply; planes_out (nullable) additionally receives the
- * planes ([3][plane_stride]).  n_tokens must equal cu_seqlens[n_seqs].  The Q/K loads of a chunk
- * are issued while its scan runs.
+ * planes ([3][plane_stride]).  With planes_out, an input of more than 512 tokens per resident
+ * rotation workgroup (262,144 on a 256-CU MI355X; the model's head shape) runs as mrope_planes into
+ * planes_out followed by mrope_apply from it: the same results, and faster at that size.
+ * n_tokens must equal cu_seqlens[n_seqs].  The Q/K loads of a chunk are issued while its scan
+ * runs.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,

@@ -210,10 +210,11 @@ def test_apply_ids_kv_full_size_sampled():
     assert int((written == 0).sum()) == 0
 
 
-@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("fused", [False, True, "planes_out"])
 def test_kv_past_the_store_hint_size(fused):
     """96 x 4096 bf16 tokens write 403 MB of Q in place, past the size from which the cache-writing
-    kernels' Q stores take the non-temporal hint: Q and the cache rows on sampled tokens."""
+    kernels' Q stores take the non-temporal hint: Q and the cache rows on sampled tokens.  With
+    planes_out the fused call runs as the scan launch and then mrope_apply_kv's launch."""
     origins = [int(o) for o in np.random.default_rng(251).integers(0, 513, size=96)]
     b = synth._batch("96x4096-image-bf16", 251, [4096] * 96, origins, "bf16")
     T = b.n_tokens
@@ -227,9 +228,13 @@ def test_kv_past_the_store_hint_size(fused):
     epl, est, eam, eog = oracle.planes(b.ids, b.cu_seqlens, MARKER)
     sl_dev = torch.from_numpy(slots).cuda()
     if fused:
-        st, am, og, _, _ = mr.apply_ids_kv(q, k, v, i32(b.ids), i32(b.cu_seqlens), kc, vc, sl_dev, MARKER)
+        pl = torch.full((3, T), -9, dtype=torch.int32, device="cuda") if fused == "planes_out" else None
+        st, am, og, _, _ = mr.apply_ids_kv(q, k, v, i32(b.ids), i32(b.cu_seqlens), kc, vc, sl_dev, MARKER,
+                                           planes_out=pl)
         np.testing.assert_array_equal(st.cpu().numpy(), est)
         np.testing.assert_array_equal(og.cpu().numpy(), eog)
+        if pl is not None:
+            np.testing.assert_array_equal(pl.cpu().numpy(), epl)
     else:
         mr.apply_kv(q, k, v, i32(epl), kc, vc, sl_dev)
     idx = set(np.random.default_rng(253).integers(0, T, size=4000).tolist())

@@ -489,18 +489,22 @@ def test_red_arms_fail_on_gpu_output():
 
 # ------------------------------------------------------------------ full-size workloads --------
 
-def _full_prefill(b, fused: bool):
+def _full_prefill(b, fused: bool, planes_out: bool = False):
     """The fused call runs as benchmarked, without planes_out: planes never leave the kernel, so the
-    scalars are compared bit for bit and the planes through the rotation."""
-    say(f"case: {b.name} tokens={b.n_tokens} seqs={b.n_seqs} fused={fused}")
+    scalars are compared bit for bit and the planes through the rotation.  With planes_out (large
+    inputs then take the scan launch and the rotation launch) the planes are compared in full too."""
+    say(f"case: {b.name} tokens={b.n_tokens} seqs={b.n_seqs} fused={fused} planes_out={planes_out}")
     qn, kn = b.qk()
     ids, cu = i32(b.ids), i32(b.cu_seqlens)
     q, k = dev_heads(qn, b.dtype), dev_heads(kn, b.dtype)
     q_tail, k_tail = q[..., 64:].clone(), k[..., 64:].clone()
     if fused:
-        st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER)
+        pl = torch.full((3, b.n_tokens), -9, dtype=torch.int32, device="cuda") if planes_out else None
+        st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER, planes_out=pl)
         torch.cuda.synchronize()
         epl, est, eam, eog = _oracle_planes(b)
+        if planes_out:
+            np.testing.assert_array_equal(pl.cpu().numpy(), epl, err_msg=f"{b.name} planes_out")
         for got, want, what in ((st, est, "start"), (am, eam, "amount"), (og, eog, "origin")):
             np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"{b.name} {what}")
         np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg=f"{b.name} flags")
@@ -540,6 +544,12 @@ def test_config5_full_ragged():
 
 def test_config5_full_ragged_fused():
     _full_prefill(synth.config5(), fused=True)
+
+
+def test_config5_full_ragged_fused_planes_out():
+    """Past 262,144 tokens with planes_out, mrope_apply_ids runs the scan launch and then the
+    rotation launch from planes_out."""
+    _full_prefill(synth.config5(), fused=True, planes_out=True)
 
 
 def _image_batch(name, seed, n_seqs, length, dtype):
