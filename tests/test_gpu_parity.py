@@ -564,6 +564,45 @@ def test_fp32_past_the_store_hint_size(fused):
     _full_prefill(_image_batch("40x4096-image-f32", 12, 40, 4096, "f32"), fused=fused)
 
 
+@pytest.mark.parametrize("seed,total,hi", [(12, 333333, 3000), (15, 1 << 19, 300)])
+def test_ragged_past_the_size_thresholds(seed, total, hi):
+    """Ragged batches past the sizes where the fused kernel splits every chunk in two, where
+    planes_out makes mrope_apply_ids two launches and where stores take the non-temporal hint: a
+    total that leaves the last chunk partial (333,333 tokens, 408 sequences) and 3,426 short
+    sequences (more than one 64-sequence window per chunk).  Scalars and planes in full, rotation
+    on sampled tokens (every frame, every sequence end, random), for the fused call with and
+    without planes_out and for planes + apply."""
+    lengths, kinds = synth.ragged_lengths(seed, total, hi=hi)
+    g = np.random.default_rng(seed)
+    placed = [int(g.integers(0, max(1, n - 67))) if k else None for n, k in zip(lengths, kinds)]
+    b = synth._batch(f"ragged{seed}", seed, lengths, placed, "bf16")
+    say(f"case: {b.name} tokens={b.n_tokens} seqs={b.n_seqs}")
+    qn, kn = b.qk()
+    ids, cu = i32(b.ids), i32(b.cu_seqlens)
+    epl, est, eam, eog = _oracle_planes(b)
+    idx = _sample_tokens(b, eog, n_random=2000, seed=seed)
+    ti = torch.from_numpy(idx).cuda()
+    for mode in ("fused", "fused_planes_out", "planes_apply"):
+        q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+        pl = torch.full((3, b.n_tokens), -9, dtype=torch.int32, device="cuda")
+        if mode == "fused":
+            st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER)
+        elif mode == "fused_planes_out":
+            st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER, planes_out=pl)
+        else:
+            _, st, am, og, fl = mr.planes(ids, cu, MARKER, out=pl)
+            mr.apply(q, k, pl)
+        for got, want, what in ((st, est, "start"), (am, eam, "amount"), (og, eog, "origin")):
+            np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"{mode} {what}")
+        np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg=f"{mode} flags")
+        if mode != "fused":
+            np.testing.assert_array_equal(pl.cpu().numpy(), epl, err_msg=f"{mode} planes")
+        compare_heads(host_heads(q[ti]), qn[idx], epl[:, idx], "bf16", what=f"{mode} q")
+        compare_heads(host_heads(k[ti]), kn[idx], epl[:, idx], "bf16", what=f"{mode} k")
+        del q, k, pl
+        torch.cuda.empty_cache()
+
+
 def test_config4_decode_paged():
     d = synth.config4()
     say(f"case: {d.name}")
