@@ -571,7 +571,7 @@ def test_ragged_past_the_size_thresholds(seed, total, hi):
     total that leaves the last chunk partial (333,333 tokens, 408 sequences) and 3,426 short
     sequences (more than one 64-sequence window per chunk).  Scalars and planes in full, rotation
     on sampled tokens (every frame, every sequence end, random), for the fused call with and
-    without planes_out and for planes + apply."""
+    without planes_out, out of place (inputs untouched), and for planes + apply."""
     lengths, kinds = synth.ragged_lengths(seed, total, hi=hi)
     g = np.random.default_rng(seed)
     placed = [int(g.integers(0, max(1, n - 67))) if k else None for n, k in zip(lengths, kinds)]
@@ -582,11 +582,17 @@ def test_ragged_past_the_size_thresholds(seed, total, hi):
     epl, est, eam, eog = _oracle_planes(b)
     idx = _sample_tokens(b, eog, n_random=2000, seed=seed)
     ti = torch.from_numpy(idx).cuda()
-    for mode in ("fused", "fused_planes_out", "planes_apply"):
+    for mode in ("fused", "fused_planes_out", "fused_out_of_place", "planes_apply"):
         q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
         pl = torch.full((3, b.n_tokens), -9, dtype=torch.int32, device="cuda")
         if mode == "fused":
             st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER)
+        elif mode == "fused_out_of_place":
+            qo, ko = torch.empty_like(q), torch.empty_like(k)
+            st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER, q_out=qo, k_out=ko)
+            np.testing.assert_array_equal(host_heads(q[ti]), qn[idx], err_msg="q input changed")
+            np.testing.assert_array_equal(host_heads(k[ti]), kn[idx], err_msg="k input changed")
+            q, k = qo, ko
         elif mode == "fused_planes_out":
             st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER, planes_out=pl)
         else:
@@ -595,7 +601,7 @@ def test_ragged_past_the_size_thresholds(seed, total, hi):
         for got, want, what in ((st, est, "start"), (am, eam, "amount"), (og, eog, "origin")):
             np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"{mode} {what}")
         np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg=f"{mode} flags")
-        if mode != "fused":
+        if mode in ("fused_planes_out", "planes_apply"):
             np.testing.assert_array_equal(pl.cpu().numpy(), epl, err_msg=f"{mode} planes")
         compare_heads(host_heads(q[ti]), qn[idx], epl[:, idx], "bf16", what=f"{mode} q")
         compare_heads(host_heads(k[ti]), kn[idx], epl[:, idx], "bf16", what=f"{mode} k")
