@@ -28,6 +28,8 @@
 // products of each output are double (the same per-lane rate as fp32 on this chip with packed fp32
 // off); each output is rounded once to fp32 and, for bf16/fp16 I/O, once more to the 16-bit type
 // (nearest even).
+#include <atomic>
+
 #include "mrope_internal.h"
 #include "mrope_math.h"
 
@@ -1341,12 +1343,24 @@ hipError_t launch_planes(const Scan &s, hipStream_t stream)
 #endif
 constexpr int kApplyBlocksPerCU = MROPE_APPLY_BLOCKS_PER_CU;
 
+// Compute units of the current device, queried once per device and kept (the grid shapes depend on
+// it; the attribute query costs more host time than a launch).  Racing first calls store the same
+// value.
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_compute_units[kMaxDevices];
+
 static int compute_units()
 {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 256;
-    return cus > 0 ? cus : 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int known = g_compute_units[dev].load(std::memory_order_relaxed);
+        if (known > 0) return known;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    if (dev >= 0 && dev < kMaxDevices) g_compute_units[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 // The fixed-head kernels cover the model's shape (8 Q heads, 2 KV heads); with a cache they also
@@ -1371,19 +1385,20 @@ template <int IO>
 static bool nt_stores(const Heads &h, const PagedKV &pc)
 {
     constexpr int64_t es = IO == kIoF32 ? 4 : 2;
-    if (h.q_out) return true;
+    if (h.q_out || h.k_out) return true;
     const int64_t heads = h.nq + (pc.k_cache ? 0 : h.nk);
     return h.n_tokens * heads * 64 * es > kNtInplaceBytes;
 }
 
-// Out of place: copy dims 64..head_dim of every Q and K head (see copy_rest_kernel).  Nothing to
-// do in place or when the heads hold only rotated dims.
+// Out of place: copy dims 64..head_dim of every Q and K head (see copy_rest_kernel), for each head
+// set that has an output buffer (a call with no Q heads may pass only k_out, and one with no K heads
+// only q_out).  Nothing to do in place or when the heads hold only rotated dims.
 template <int IO>
 static hipError_t copy_rest(const Heads &h, hipStream_t st)
 {
     constexpr int64_t es = IO == kIoF32 ? 4 : 2;
     const int n_chunks = (int)((h.head_dim - 64) * es / 16);
-    if (!h.q_out || n_chunks <= 0 || h.n_tokens <= 0) return hipSuccess;
+    if ((!h.q_out && !h.k_out) || n_chunks <= 0 || h.n_tokens <= 0) return hipSuccess;
     auto one = [&](const void *src, void *dst, int64_t tok, int64_t head, int nh) {
         if (nh <= 0 || !dst) return;
         const int64_t n_rows = h.n_tokens * nh;

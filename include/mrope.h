@@ -15,8 +15,10 @@
  *
  * Conventions for every entry point
  *   - Pointers to tensors are DEVICE pointers owned by the caller.  The library allocates no
- *     device memory and keeps no mutable global state; the only state that crosses calls lives in
- *     the caller's workspace (see mrope_workspace_bytes).
+ *     device memory.  State that crosses calls lives in the caller's workspace (see
+ *     mrope_workspace_bytes); the library itself keeps only a per-thread copy of the last error
+ *     text (mrope_last_error) and, per device, the compute-unit count it sizes its grids by (read
+ *     once).
  *   - Every call enqueues its work on `stream` (a hipStream_t; NULL = the null stream) and returns
  *     without synchronising.  Calls issue no memset and no allocation, so they can be captured in a
  *     HIP graph.
@@ -167,7 +169,8 @@ mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t
  * q_out, k_out  NULL: rotate in place (dims >= rot_dim are never read or written).  Otherwise the
  *            full heads are written there, with the same strides as q / k (no aliasing with the
  *            inputs): a first launch copies dims >= rot_dim, the rotation launch writes the rest.
- *            Both NULL or both non-NULL (k_out may be NULL when n_k_heads == 0).
+ *            Both NULL or both non-NULL when both head sets are present; a call with no K heads
+ *            may pass q_out alone, one with no Q heads k_out alone.
  * Alignment: q, k, q_out, k_out 16-byte aligned; strides multiples of 8 (bf16, fp16) or 4 (fp32).
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_apply(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads, void *k,

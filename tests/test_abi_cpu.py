@@ -53,7 +53,7 @@ def _apply(lib, **kw):
     (dict(dt=7), UNSUP), (dict(nq=65), UNSUP), (dict(nk=-1), UNSUP),
     (dict(n=-1), ARG), (dict(q=None), ARG), (dict(k=None), ARG), (dict(planes=None), ARG), (dict(ps=99), ARG),
     (dict(theta=0.0), ARG), (dict(theta=float("nan")), ARG), (dict(theta=float("inf")), ARG),
-    (dict(qo=A), ARG), (dict(qt=-8), ARG),
+    (dict(qo=A), ARG), (dict(ko=A), ARG), (dict(qt=-8), ARG),
     (dict(q=A + 8), ALIGN), (dict(k=A + 4), ALIGN), (dict(qt=2044), ALIGN), (dict(kh=252), ALIGN),
     (dict(dt=F32, qt=2050), ALIGN),
 ])

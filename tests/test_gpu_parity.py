@@ -921,6 +921,34 @@ def test_out_of_place_generic_shapes_and_padded_strides():
                 assert bool((ko_buf[k_pad] == sentinel).all()), f"{what}: k_out padding written"
 
 
+def test_out_of_place_one_head_set_only():
+    """Out of place with only K heads (no Q heads, k_out alone) and with only Q heads (q_out alone):
+    the one output holds every dim of every head -- the rotated dims and, from the copy launch, the
+    rest -- and the input is untouched."""
+    b = synth.random_batch(84, 16, max_len=200)
+    T = b.n_tokens
+    pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    for case, (dt, nh, D, k_side) in enumerate((("bf16", 2, 256, True), ("f32", 3, 128, True),
+                                                ("bf16", 8, 256, False), ("f16", 1, 72, False))):
+        say(f"case: out of place, {'K' if k_side else 'Q'} heads only: {dt} {nh}x{D}")
+        x = synth.to_dtype(synth.normal(84, 90 + case, T * nh * D), dt).reshape(T, nh, D)
+        src = dev_heads(x, dt)
+        out = torch.full_like(src, -3.0)
+        none = torch.empty((T, 0, D), dtype=TORCH_DT[dt], device="cuda")
+        for fused in (False, True):
+            out.fill_(-3.0)
+            q_in, k_in = (none, src) if k_side else (src, None)
+            kw = dict(k_out=out) if k_side else dict(q_out=out)
+            if fused:
+                mr.apply_ids(q_in, k_in, i32(b.ids), i32(b.cu_seqlens), MARKER, **kw)
+            else:
+                mr.apply(q_in, k_in, pl, **kw)
+            what = f"{dt} {nh}x{D} {'K' if k_side else 'Q'} only {'fused' if fused else 'apply'}"
+            np.testing.assert_array_equal(host_heads(src), x, err_msg=f"{what}: input changed")
+            compare_heads(host_heads(out), x, epl, dt, what=what)
+
+
 def test_decode_fp32_and_generic_shapes():
     d = synth.config4(n_seqs=300, num_blocks=512)
     g = synth.rng(91, 5)
