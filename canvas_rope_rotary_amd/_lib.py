@@ -18,9 +18,20 @@ TEXT_ONLY_START = 1 << 30
 ROT_DIM = 64
 
 # every symbol include/mrope.h declares
-EXPORTS = ("mrope_abi_version", "mrope_status_string", "mrope_last_error", "mrope_workspace_bytes",
+EXPORTS = ("mrope_abi_version", "mrope_status_string", "mrope_last_error", "mrope_set_test_hooks",
+           "mrope_workspace_bytes",
            "mrope_workspace_init", "mrope_planes", "mrope_apply", "mrope_apply_ids", "mrope_apply_kv",
            "mrope_apply_ids_kv", "mrope_decode")
+
+
+HOOK_FUSED_CHUNKED = 1
+HOOK_FUSED_SCAN_FIRST = 2
+HOOK_SCAN_FALLBACK = 4
+
+
+def set_test_hooks(flags: int) -> int:
+    """Test and tuning hooks of the library (see mrope_set_test_hooks); returns the previous value."""
+    return int(load().mrope_set_test_hooks(int(flags)))
 
 
 class MarkerFlags(enum.IntFlag):
@@ -54,6 +65,8 @@ def load():
     lib.mrope_status_string.restype = ctypes.c_char_p
     lib.mrope_last_error.argtypes = []
     lib.mrope_last_error.restype = ctypes.c_char_p
+    lib.mrope_set_test_hooks.argtypes = [ctypes.c_int]
+    lib.mrope_set_test_hooks.restype = ctypes.c_int
     lib.mrope_workspace_bytes.argtypes = [I64]
     lib.mrope_workspace_bytes.restype = U64
     lib.mrope_workspace_init.argtypes = [P, U64, P]

@@ -1,5 +1,6 @@
 // C ABI of libmrope: argument checks, rotary constants, launches.  The entry points are declared
 // and documented in include/mrope.h.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -9,6 +10,12 @@
 #include "mrope_internal.h"
 
 using namespace mrope;
+
+namespace mrope {
+// Test and tuning hooks (mrope_set_test_hooks); 0 in normal use.
+static std::atomic<int> g_test_hooks{0};
+int test_hooks() { return g_test_hooks.load(std::memory_order_relaxed); }
+}  // namespace mrope
 
 namespace {
 
@@ -142,6 +149,9 @@ Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_
     s.origin_in = origin_in;
     s.frame_len = frame_len == 0 ? kDefaultFrameLen : frame_len;
     s.workspace = ws;
+    const WsLayout lay = ws_layout(n_tokens);
+    s.parts = ws ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + lay.parts) : nullptr;
+    s.tagged = ws ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + lay.tagged) : nullptr;
     s.epoch = epoch;
     return s;
 }
@@ -220,12 +230,14 @@ const char *mrope_status_string(int status)
 
 const char *mrope_last_error(void) { return g_last_error; }
 
-size_t mrope_workspace_bytes(int64_t n_tokens)
+int mrope_set_test_hooks(int flags)
 {
-    if (n_tokens < 0) n_tokens = 0;
-    const int64_t tiles = (n_tokens + kTile - 1) / kTile;
-    return kWsHeaderBytes + (size_t)tiles * sizeof(uint64_t);
+    const int prev = g_test_hooks.load(std::memory_order_relaxed);
+    g_test_hooks.store(flags & (kHookFusedChunked | kHookFusedScanFirst | kHookScanFallback), std::memory_order_relaxed);
+    return prev;
 }
+
+size_t mrope_workspace_bytes(int64_t n_tokens) { return ws_layout(n_tokens).total; }
 
 mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream)
 {

@@ -9,8 +9,33 @@ namespace mrope {
 constexpr int kMaxHeads = 64;
 constexpr int kDefaultFrameLen = 67;    // <image>, 64 rows, </image>, "\n"
 constexpr int kMaxFrameLen = 4096;
-constexpr int kTile = 64;               // tokens per scan tile: one wavefront, one lane per token
+constexpr int kChunkTokens = 512;       // tokens per scan chunk: one wave, eight 64-id ballots
+constexpr int kPartTokens = 32;         // tokens per rotation workgroup of the scan-first fused kernel
 constexpr size_t kWsHeaderBytes = 256;  // device epoch counter (+ padding)
+
+// Workspace of the plane-deriving calls (byte offsets; every region 256-byte aligned):
+//   header   the device epoch counter
+//   status   one 64-bit look-back word per 512-token chunk
+//   parts    two 64-bit words per 32-token part: the planes handover of the scan-first fused kernel
+//   tagged   three 64-bit words per token: planes of parts that hold more than one sequence
+struct WsLayout {
+    size_t status, parts, tagged, total;
+};
+
+inline size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
+
+inline WsLayout ws_layout(int64_t n_tokens)
+{
+    if (n_tokens < 0) n_tokens = 0;
+    const size_t chunks = (size_t)((n_tokens + kChunkTokens - 1) / kChunkTokens);
+    const size_t parts = (size_t)((n_tokens + kPartTokens - 1) / kPartTokens);
+    WsLayout w;
+    w.status = kWsHeaderBytes;
+    w.parts = w.status + ws_round(chunks * 8);
+    w.tagged = w.parts + ws_round(parts * 16);
+    w.total = w.tagged + ws_round((size_t)n_tokens * 24);
+    return w;
+}
 
 // Rotary constants: 32 fp32 inverse frequencies and the plane each frequency reads, 2 bits per
 // frequency (0 = T, 1 = H, 2 = W).
@@ -48,8 +73,17 @@ struct Scan {
     const int32_t *origin_in;   // nullable: origin found in earlier pieces, -1 = none
     int32_t frame_len;          // tokens from <image> to start (65 .. kMaxFrameLen)
     void *workspace;
+    uint64_t *parts;     // workspace regions (see WsLayout); set by the host from n_tokens
+    uint64_t *tagged;
     uint32_t epoch;      // tags this launch's status words; 0 = use (and advance) the device counter
 };
+
+// Test and tuning hooks (mrope_set_test_hooks): which fused kernel serves mrope_apply_ids, and a
+// mode that makes the scan-first kernel's rotation workgroups derive their planes themselves.
+constexpr int kHookFusedChunked = 1;   // always the chunk-per-workgroup fused kernel
+constexpr int kHookFusedScanFirst = 2; // always the scan-first fused kernel (8 Q + 2 K heads)
+constexpr int kHookScanFallback = 4;   // scan-first: rotation workgroups first, no waiting
+int test_hooks();
 
 // Paged K/V cache destination.  Element (block, row, head, d) of either cache is at
 // block*c_block + row*c_tok + head*c_head + d; slot -> (slot / block_size, slot % block_size).

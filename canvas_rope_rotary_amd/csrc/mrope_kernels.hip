@@ -28,6 +28,7 @@
 // products of each output are double (the same per-lane rate as fp32 on this chip with packed fp32
 // off); each output is rounded once to fp32 and, for bf16/fp16 I/O, once more to the 16-bit type
 // (nearest even).
+#include <algorithm>
 #include <atomic>
 
 #include "mrope_internal.h"
@@ -322,12 +323,23 @@ __device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t
 // Scan of one chunk by one full wave.  Publishes the chunk's status word, looks back when the
 // chunk's first sequence began earlier, writes the scalars of every sequence whose last token (for
 // an empty sequence: the token before it) lies in the chunk, and hands each token's planes to
-// sink(k, ok, t, h, w) for token chunk*kChunk + 64k + lane.  When several workgroups scan the same
+// sink(k, ok, t, h, w, seq) for token chunk*kChunk + 64k + lane, where seq describes the token's
+// sequence (its begin, position offset and origin; see SeqInfo).  When several workgroups scan the same
 // chunk, only the owner publishes and writes scalars: device-scope stores to one address from many
 // workgroups are serialized (16 writers of one status word took 3-8 us to be acknowledged, against
 // 0.6 us for one).
 struct NoHook {
     __device__ void operator()() const {}
+};
+
+// The sequence a token belongs to, as the scan hands it to a sink: the sequence's first token
+// (global index), the position of that token in the whole sequence (pos_offset), and the sequence's
+// canvas origin in positions (kNone when it has no marker so far).  Position of token g:
+// off + (g - begin).
+struct SeqInfo {
+    int64_t begin;
+    int32_t off;
+    int32_t org;
 };
 struct NoSingle {
     __device__ bool operator()(int64_t, int32_t, int32_t) const { return false; }
@@ -435,7 +447,7 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
                     const int32_t p = offr + (int32_t)(g - sb);
                     int32_t t = 0, h = 0, w = 0;
                     if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, sc.frame_len, t, h, w);
-                    sink(k, ok, t, h, w);
+                    sink(k, ok, t, h, w, SeqInfo{sb, offr, orr});
                 }
             }
         } else {
@@ -452,7 +464,7 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
                 const int32_t p = offr + (int32_t)(g - sb);
                 int32_t t = 0, h = 0, w = 0;
                 if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, sc.frame_len, t, h, w);
-                sink(k, ok, t, h, w);
+                sink(k, ok, t, h, w, SeqInfo{sb, offr, orr});
             }
         }
         if (win + 64 >= n || (int64_t)sc.cu[win + 64] > c_end) break;
@@ -1024,7 +1036,7 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
     if (chunk >= n_chunks) return;
     const int64_t c0 = chunk * kChunk;
     scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane, true,
-               [&](int k, bool ok, int32_t t, int32_t h, int32_t w) {
+               [&](int k, bool ok, int32_t t, int32_t h, int32_t w, const SeqInfo &) {
                    if (!ok) return;
                    const int64_t g = c0 + 64 * k + lane;
                    sc.planes[g] = t;
@@ -1087,7 +1099,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         // every wave then derives its own tokens' planes, instead of wave 0 writing all 512 to LDS
         // (measured: that handover was ~4 us of the launch on 64 x 4096 tokens).
         scan_chunk(sc, status_array(sc.workspace), chunk, launch_epoch(sc), lane, r0 == c0,
-                   [&](int k, bool ok, int32_t t, int32_t h, int32_t w) {
+                   [&](int k, bool ok, int32_t t, int32_t h, int32_t w, const SeqInfo &) {
                        const int p = 64 * k + lane;
                        const uint64_t okm = __ballot(ok);
                        if (lane == 0) s_ok[k] |= okm;
@@ -1176,6 +1188,221 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
             }
         }
         g = gn;
+    }
+}
+
+// ------------------------------------------------------------------ scan-first fused kernel ----
+// mrope_apply_ids for large inputs with the model's heads (8 Q, 2 K).  The grid holds two kinds of
+// workgroups, dispatched in index order:
+//   scan workgroups [0, S): one wave per 512-token chunk runs the chunk scan (ballots, look-back,
+//     scalars, planes_out) and hands the planes of each 32-token part of the chunk over through the
+//     workspace -- a part inside one sequence as two words (the position base, p = g + base, and the
+//     sequence's canvas origin), any other part as its tokens' planes, three words a token -- every
+//     word tagged with the launch's epoch;
+//   rotation workgroups [S, S + R): one 32-token part each, shaped like mrope_apply's one-step
+//     workgroups: every lane issues its token's Q/K loads, then reads the part's handover words,
+//     derives its token's planes, rotates and stores.
+// The scans of all chunks run first, on an otherwise idle memory system, so the rotation sees no
+// scan latency beyond the first chunks'; the rotation workgroups then run on the dispatcher-balanced
+// one-step grid that serves mrope_apply at this size.  A wave whose handover words are not tagged
+// with this launch after a bounded number of polls scans its chunk itself (as the chunk-per-workgroup
+// kernel does), so no wait depends on which workgroups the hardware has scheduled.
+constexpr uint64_t kPartSingle = 1, kPartMulti = 2;
+constexpr int kScanWaves = kBlock / 64;  // chunks per scan workgroup
+
+__device__ __forceinline__ uint64_t tag_word(uint32_t ep, uint64_t kind, uint32_t v)
+{
+    return ((uint64_t)ep << 34) | (kind << 32) | (uint64_t)v;
+}
+__device__ __forceinline__ bool tagged_with(uint64_t w, uint32_t ep) { return (uint32_t)(w >> 34) == ep; }
+
+// One wave's chunk scan with the part handover.
+__device__ void sf_scan_chunk(const Scan &sc, int64_t chunk, uint32_t ep, int lane)
+{
+    const int64_t c0 = chunk * kChunk;
+    const int64_t c_end = min<int64_t>(c0 + kChunk, sc.n_tokens);
+    scan_chunk(
+        sc, status_array(sc.workspace), chunk, ep, lane, true,
+        [&](int k, bool ok, int32_t t, int32_t h, int32_t w, const SeqInfo &si) {
+            const int64_t g = c0 + 64 * k + lane;
+            if (ok && sc.planes) {
+                sc.planes[g] = t;
+                sc.planes[sc.plane_stride + g] = h;
+                sc.planes[2 * sc.plane_stride + g] = w;
+            }
+            // the two 32-token parts of this 64-token block: lanes [0, 32) and [32, 64).  A part is
+            // handed over as one sequence when every token of it (before the end) is delivered in
+            // this call with the same sequence; otherwise its delivered tokens' planes go over one by
+            // one (a part whose tokens come in several calls is written so by each).
+            const int leader = lane & 32;
+            const int64_t lb = __shfl(si.begin, leader);
+            const int32_t lo = __shfl(si.off, leader), lg = __shfl(si.org, leader);
+            const bool valid = g < c_end;
+            const bool same = !valid || (ok && si.begin == lb && si.off == lo && si.org == lg);
+            const uint64_t half = leader ? 0xffffffff00000000ull : 0x00000000ffffffffull;
+            const bool single = (__ballot(same) & half) == half;
+            if ((__ballot(ok) & half) == 0) return;
+            const int64_t part = (c0 + 64 * k + leader) / kPartTokens;
+            if (single) {
+                if (lane == leader) {
+                    astore(sc.parts + 2 * part, tag_word(ep, kPartSingle, (uint32_t)(int32_t)((int64_t)lo - lb)));
+                    astore(sc.parts + 2 * part + 1, tag_word(ep, 0, (uint32_t)lg));
+                }
+            } else {
+                if (ok) {
+                    astore(sc.tagged + 3 * g, tag_word(ep, 0, (uint32_t)t));
+                    astore(sc.tagged + 3 * g + 1, tag_word(ep, 0, (uint32_t)h));
+                    astore(sc.tagged + 3 * g + 2, tag_word(ep, 0, (uint32_t)w));
+                }
+                if (lane == leader) {
+                    astore(sc.parts + 2 * part, tag_word(ep, kPartMulti, 0u));
+                    astore(sc.parts + 2 * part + 1, tag_word(ep, 0, 0u));
+                }
+            }
+        },
+        NoHook(),
+        [&](int64_t sb, int32_t off, int32_t org) {
+            if (sc.planes) return false;  // planes_out is written token by token (sink)
+            const int64_t p0 = c0 / kPartTokens, np = (c_end - c0 + kPartTokens - 1) / kPartTokens;
+            if (lane < np) {
+                astore(sc.parts + 2 * (p0 + lane), tag_word(ep, kPartSingle, (uint32_t)(int32_t)((int64_t)off - sb)));
+                astore(sc.parts + 2 * (p0 + lane) + 1, tag_word(ep, 0, (uint32_t)org));
+            }
+            return true;
+        });
+}
+
+// The planes of this lane's token g (< n_tokens when ok) in wave's group [G, G + 8), taken from the
+// part handover, or -- when it is missing after the polls, or wait is false -- from a scan of the
+// chunk by this wave.
+__device__ void sf_planes(const Scan &sc, uint32_t ep, int lane, int64_t G, int64_t g, bool ok, bool wait,
+                          int32_t &pt, int32_t &ph, int32_t &pw)
+{
+    const int64_t part = G / kPartTokens;
+    bool have = false;
+    pt = ph = pw = 0;
+    if (wait) {
+        uint64_t w0 = 0, w1 = 0;
+        bool ready = false;
+        for (int poll = 0;; ++poll) {
+            w0 = aload(sc.parts + 2 * part);
+            w1 = aload(sc.parts + 2 * part + 1);
+            ready = tagged_with(w0, ep) && tagged_with(w1, ep);
+            if (ready || poll == kPolls) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (ready && ((w0 >> 32) & 3u) == kPartSingle) {
+            const int32_t base = (int32_t)(uint32_t)w0, org = (int32_t)(uint32_t)w1;
+            const int32_t p = (int32_t)g + base;
+            if (ok) canvas_planes(p, (org != kNone && org <= p) ? org : kNone, sc.frame_len, pt, ph, pw);
+            have = true;
+        } else if (ready) {
+            for (int poll = 0;; ++poll) {
+                if (ok && !have) {
+                    const uint64_t a = aload(sc.tagged + 3 * g), b = aload(sc.tagged + 3 * g + 1),
+                                   c = aload(sc.tagged + 3 * g + 2);
+                    if (tagged_with(a, ep) && tagged_with(b, ep) && tagged_with(c, ep)) {
+                        pt = (int32_t)(uint32_t)a;
+                        ph = (int32_t)(uint32_t)b;
+                        pw = (int32_t)(uint32_t)c;
+                        have = true;
+                    }
+                }
+                if (__ballot(ok && !have) == 0 || poll == kPolls) break;
+                __builtin_amdgcn_s_sleep(8);
+            }
+            have = have || !ok;
+        }
+    }
+    if (__ballot(!have) == 0) return;
+    // fallback: this wave scans the chunk (not as its owner: the scan workgroup publishes it)
+    const int64_t chunk = G / kChunk, c0 = chunk * kChunk;
+    const int kk = (int)((G - c0) >> 6);     // the 64-token block holding the wave's tokens
+    const int src = (int)((g - c0) & 63);    // the lane that carries this lane's token there
+    scan_chunk(
+        sc, status_array(sc.workspace), chunk, ep, lane, false,
+        [&](int k, bool tok, int32_t t, int32_t h, int32_t w, const SeqInfo &) {
+            const int okv = __shfl((int)tok, src);
+            const int32_t tt = __shfl(t, src), hh = __shfl(h, src), ww = __shfl(w, src);
+            if (k == kk && okv) {
+                pt = tt;
+                ph = hh;
+                pw = ww;
+            }
+        },
+        NoHook(),
+        [&](int64_t sb, int32_t off, int32_t org) {
+            const int32_t p = off + (int32_t)(g - sb);
+            if (ok) canvas_planes(p, (org != kNone && org <= p) ? org : kNone, sc.frame_len, pt, ph, pw);
+            return true;
+        });
+}
+
+// Block order of the scan-first grid.  The first `lead` scan workgroups come first; then each
+// further scan workgroup follows the rotation workgroups of the 4 chunks (64 parts) that lie `lead`
+// scan workgroups behind it, so a chunk's scan runs well before its rotation while the scans of
+// later chunks overlap the rotation stream; the rotation workgroups of the last chunks close the
+// grid.  The grid has n_scan + max(n_parts, 64 (n_scan - lead)) workgroups; parts past the last
+// token exit at once.  With the fallback hook every rotation workgroup comes first.
+constexpr int kPartsPerScanBlock = kScanWaves * (kChunk / kPartTokens);
+
+__device__ __forceinline__ void sf_block_role(int64_t b, int64_t n_scan, int64_t lead, int64_t n_parts, bool rot_first,
+                                              bool &is_scan, int64_t &idx)
+{
+    if (rot_first) {
+        is_scan = b >= n_parts;
+        idx = is_scan ? b - n_parts : b;
+        return;
+    }
+    if (b < lead) {
+        is_scan = true;
+        idx = b;
+        return;
+    }
+    const int64_t u = b - lead, ng = n_scan - lead, span = kPartsPerScanBlock + 1;
+    if (u < ng * span) {
+        const int64_t grp = u / span, r = u - grp * span;
+        is_scan = r == kPartsPerScanBlock;
+        idx = is_scan ? lead + grp : grp * kPartsPerScanBlock + r;
+        return;
+    }
+    is_scan = false;
+    idx = ng * kPartsPerScanBlock + (u - ng * span);
+}
+
+template <int IO, bool NTS>
+__global__ __launch_bounds__(kBlock) void apply_ids_sf_kernel(Heads hd, Rotary rot, Scan sc, int64_t n_scan_blocks,
+                                                              int64_t lead, int hooks)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const uint32_t ep = launch_epoch(sc);
+    const int64_t n_parts = (hd.n_tokens + kPartTokens - 1) / kPartTokens;
+    const bool rot_first = (hooks & kHookScanFallback) != 0;
+    bool is_scan;
+    int64_t idx;
+    sf_block_role(blockIdx.x, n_scan_blocks, lead, n_parts, rot_first, is_scan, idx);
+    if (is_scan) {
+        const int64_t chunk = idx * kScanWaves + (tid >> 6);
+        if (chunk * kChunk < hd.n_tokens) sf_scan_chunk(sc, chunk, ep, lane);
+        return;
+    }
+    const int64_t part = idx;
+    const int l = tid & 7, m = l >> 1, half = l & 1;
+    const int e0 = 32 * half + 8 * m;
+    const int64_t G = part * kPartTokens + (tid >> 6) * 8;  // the wave's first token
+    if (G >= hd.n_tokens) return;
+    const int64_t g = G + ((tid & 63) >> 3);
+    const bool ok = g < hd.n_tokens;
+    Raw8<IO> qv[8], kv[2];
+    if (ok) load_token_fixed<IO, 8, 2>(hd, g, e0, qv, kv);
+    int32_t pt, ph, pw;
+    sf_planes(sc, ep, lane, G, g, ok, !rot_first, pt, ph, pw);
+    if (ok) {
+        const LaneFreq lf = lane_freq<true>(rot, m, half);
+        double c[8], ss[8];
+        pair_sincos(lf, pt, ph, pw, c, ss);
+        rotate_token_fixed<IO, 8, 2, false, NTS>(hd, PagedKV{}, -1, g, e0, l, c, ss, qv, kv);
     }
 }
 
@@ -1495,9 +1722,60 @@ static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan
     return e != hipSuccess ? e : bump_if_device_epoch(s, st);
 }
 
+// Scan-first fused kernel (fixed heads, no cache write).  kScanLead: scan workgroups (4 chunks,
+// 64 rotation workgroups each) that run ahead of the rotation.  Measured on 1,048,576 ragged tokens
+// (four workgroups per CU): every scan first 485.8 us, a lead of 128 scan workgroups 484.7, 32
+// 479.9, 8 479.5; the scan itself then costs nothing measurable (the same grid with no scan and
+// constant planes: 478.4 us).
+constexpr int64_t kScanLead = 32;
+
+template <int IO>
+static hipError_t apply_ids_sf_dispatch(const Heads &h, const Rotary &r, const Scan &s, hipStream_t st)
+{
+    if (const hipError_t ce = copy_rest<IO>(h, st); ce != hipSuccess) return ce;
+    const int64_t n_chunks = (h.n_tokens + kChunk - 1) / kChunk;
+    const int64_t n_scan = (n_chunks + kScanWaves - 1) / kScanWaves;
+    const int64_t n_parts = (h.n_tokens + kPartTokens - 1) / kPartTokens;
+    const int hooks = test_hooks();
+    const int64_t lead = n_scan < kScanLead ? n_scan : kScanLead;
+    const int64_t rot_blocks = (hooks & kHookScanFallback) ? n_parts
+                                                           : std::max(n_parts, (n_scan - lead) * kPartsPerScanBlock);
+    const unsigned blocks = (unsigned)(n_scan + rot_blocks);
+    // Two workgroups per CU: the kernel needs 127 VGPRs (four could be resident), but more
+    // concurrent 32-token parts make the HBM stream slower.  Measured on 1,048,576 ragged tokens:
+    // 480 us at four workgroups per CU, 476 at three, 468 at two (mrope_apply, two by its registers:
+    // 467), 680 at one.  The unused dynamic LDS holds the occupancy there.
+    constexpr unsigned kOccupancyLds = 64 << 10;
+    if (nt_stores<IO>(h, PagedKV{}))
+        apply_ids_sf_kernel<IO, true><<<blocks, kBlock, kOccupancyLds, st>>>(h, r, s, n_scan, lead, hooks);
+    else
+        apply_ids_sf_kernel<IO, false><<<blocks, kBlock, kOccupancyLds, st>>>(h, r, s, n_scan, lead, hooks);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : bump_if_device_epoch(s, st);
+}
+
+// Which fused kernel serves a call: the scan-first kernel for the model's heads from this many
+// tokens on (where mrope_apply takes one-step workgroups), the chunk-per-workgroup kernel below it
+// and for other shapes.
+static bool use_scan_first(const Heads &h, const PagedKV &pc, int io)
+{
+    const int hooks = test_hooks();
+    if (pc.k_cache || h.nq != 8 || h.nk != 2 || (hooks & kHookFusedChunked)) return false;
+    if (hooks & (kHookFusedScanFirst | kHookScanFallback)) return true;
+    const int64_t one_step_from = (int64_t)compute_units() * kApplyBlocksPerCU * 16 * kTokPerBlock;
+    return h.n_tokens > one_step_from && io >= 0;
+}
+
 hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, const PagedKV &pc, int io,
                             hipStream_t stream)
 {
+    if (use_scan_first(h, pc, io)) {
+        switch (io) {
+        case kIoBF16: return apply_ids_sf_dispatch<kIoBF16>(h, r, s, stream);
+        case kIoF16: return apply_ids_sf_dispatch<kIoF16>(h, r, s, stream);
+        default: return apply_ids_sf_dispatch<kIoF32>(h, r, s, stream);
+        }
+    }
     // With the planes wanted in memory anyway (planes_out) and past the size where mrope_apply
     // takes one step per workgroup, the scan writes planes_out and the rotation reads it back: one
     // workgroup per chunk cannot use that grid.  Measured (bf16): 1,048,576 ragged tokens 17.5 +

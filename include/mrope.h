@@ -75,14 +75,28 @@ const char *mrope_status_string(int status);
 /* Description of the last non-OK status returned on the calling thread ("" if none). */
 const char *mrope_last_error(void);
 
+/* Test and tuning hooks: not for production use.  They choose among the library's own kernels for
+ * mrope_apply_ids and never change results, so the test suite can run every kernel on every input.
+ * Process-wide; returns the previous value.  0 (the default) lets the library choose.
+ *   MROPE_HOOK_FUSED_CHUNKED     always the chunk-per-workgroup fused kernel
+ *   MROPE_HOOK_FUSED_SCAN_FIRST  always the scan-first fused kernel (8 Q + 2 K heads, no cache write)
+ *   MROPE_HOOK_SCAN_FALLBACK     scan-first kernel whose rotation workgroups derive their planes
+ *                                themselves instead of waiting for the scan's handover */
+#define MROPE_HOOK_FUSED_CHUNKED 1
+#define MROPE_HOOK_FUSED_SCAN_FIRST 2
+#define MROPE_HOOK_SCAN_FALLBACK 4
+int mrope_set_test_hooks(int flags);
+
 /* ---------------------------------------------------------------------------------------------
  * Workspace for the calls that derive planes from ids (mrope_planes, mrope_apply_ids).
  *
  * Returns the bytes needed for n_tokens packed tokens.  The workspace must be 256-byte aligned
  * device memory, zero-filled (or passed once through mrope_workspace_init) before its first use;
  * it needs no clearing between calls.  It holds a device epoch counter and room for one 64-bit
- * status word per 64 tokens; the scan uses one word per 512-token chunk, through which a chunk
- * hands the first marker of a sequence to the chunks after it.
+ * status word per 512-token chunk, through which a chunk hands the first marker of a sequence to
+ * the chunks after it, then the planes handover of the scan-first fused kernel (16 bytes per 32
+ * tokens, and 24 bytes per token for parts that hold more than one sequence): about 24.5 bytes per
+ * token in all.
  *
  * Epochs.  The plane-deriving calls take an `epoch` that tags the status words they write, so a
  * call never mistakes words left by an earlier call for its own:

@@ -36,8 +36,21 @@ def test_version_and_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    for n, tiles in ((0, 0), (1, 1), (64, 1), (65, 2), (1 << 20, 1 << 14)):
-        assert lib.mrope_workspace_bytes(n) == 256 + 8 * tiles
+    """Header, one status word per 512-token chunk, two words per 32-token part, three words per
+    token; every region rounded up to 256 bytes."""
+    r = lambda b: (b + 255) // 256 * 256
+    for n in (0, 1, 31, 32, 64, 65, 511, 512, 513, 1 << 20, 3_000_001):
+        chunks, parts = -(-n // 512), -(-n // 32)
+        assert lib.mrope_workspace_bytes(n) == 256 + r(8 * chunks) + r(16 * parts) + r(24 * n), n
+
+
+def test_test_hooks_round_trip(lib):
+    prev = lib.mrope_set_test_hooks(_lib.HOOK_FUSED_SCAN_FIRST)
+    try:
+        assert lib.mrope_set_test_hooks(_lib.HOOK_SCAN_FALLBACK | 64) == _lib.HOOK_FUSED_SCAN_FIRST
+        assert lib.mrope_set_test_hooks(0) == _lib.HOOK_SCAN_FALLBACK  # unknown bits are dropped
+    finally:
+        lib.mrope_set_test_hooks(prev)
 
 
 def _apply(lib, **kw):
@@ -77,7 +90,7 @@ def _planes(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(ns=-1), ARG), (dict(n=-1), ARG), (dict(ns=0), ARG), (dict(cu=None), ARG), (dict(ids=None), ARG),
     (dict(planes=None), ARG), (dict(ps=999), ARG), (dict(n=1 << 31), ARG),
-    (dict(ws=None), WS), (dict(ws=A + 64), WS), (dict(wsb=256 + 8 * 15), WS),
+    (dict(ws=None), WS), (dict(ws=A + 64), WS), (dict(wsb=256 + 8 * 15), WS), (dict(wsb=24 * 1000), WS),
     (dict(fl=64), ARG), (dict(fl=-1), ARG), (dict(fl=4097), ARG),
 ])
 def test_planes_validation(lib, kw, code):

@@ -155,3 +155,61 @@ def test_copy_rest_map_copies_each_byte_once():
                     s = (t * tok_el + h * head_el) * es
                     want[s + 64 * es:s + D * es] = 1
             assert np.array_equal(written, want), (T, nh, D, es, tok_el, head_el, cap)
+
+
+# ------------------------------------------------------------------ apply_ids_sf_kernel ---------
+# Block roles of the scan-first fused kernel (sf_block_role and apply_ids_sf_dispatch): scan
+# workgroups of 4 chunks, rotation workgroups of 32 tokens; the first `lead` scan workgroups first,
+# then each further one after the 64 rotation workgroups of the chunks `lead` scan workgroups
+# behind it; with the fallback hook the rotation workgroups come first.
+
+def _sf_roles(n_tokens, lead_max=32, rot_first=False):
+    n_chunks = -(-n_tokens // 512)
+    n_scan = -(-n_chunks // 4)
+    n_parts = -(-n_tokens // 32)
+    lead = min(n_scan, lead_max)
+    per = 64
+    rot_blocks = n_parts if rot_first else max(n_parts, (n_scan - lead) * per)
+    roles = []
+    for b in range(n_scan + rot_blocks):
+        if rot_first:
+            is_scan = b >= n_parts
+            idx = b - n_parts if is_scan else b
+        elif b < lead:
+            is_scan, idx = True, b
+        else:
+            u, ng, span = b - lead, n_scan - lead, per + 1
+            if u < ng * span:
+                grp, r = divmod(u, span)
+                is_scan = r == per
+                idx = lead + grp if is_scan else grp * per + r
+            else:
+                is_scan, idx = False, ng * per + (u - ng * span)
+        roles.append((is_scan, idx))
+    return roles, n_scan, n_parts
+
+
+def test_scan_first_grid_covers_every_chunk_and_part_once():
+    for n in (1, 31, 32, 33, 511, 512, 513, 2047, 2048, 2049, 65535, 65536, 65537, 262143, 262144, 300001,
+              1 << 20, (1 << 20) + 17):
+        for rot_first in (False, True):
+            for lead in (1, 32):
+                roles, n_scan, n_parts = _sf_roles(n, lead, rot_first)
+                scans = sorted(i for s, i in roles if s)
+                parts = [i for s, i in roles if not s]
+                assert scans == list(range(n_scan)), (n, rot_first, lead)
+                assert sorted(p for p in parts if p < n_parts) == list(range(n_parts)), (n, rot_first, lead)
+                assert all(p * 32 >= n for p in parts if p >= n_parts), (n, rot_first, lead)
+
+
+def test_scan_first_scans_run_ahead_of_their_parts():
+    """Outside the fallback order, the scan workgroup of a chunk comes before every rotation
+    workgroup of that chunk, by at least `lead` scan workgroups' worth of parts when it can."""
+    for n in (70000, 300001, 1 << 20):
+        roles, n_scan, n_parts = _sf_roles(n)
+        pos_scan = {i: b for b, (s, i) in enumerate(roles) if s}
+        for b, (s, i) in enumerate(roles):
+            if s or i >= n_parts:
+                continue
+            chunk = i * 32 // 512
+            assert pos_scan[chunk // 4] < b, (n, i)
