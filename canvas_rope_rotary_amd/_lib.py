@@ -20,7 +20,8 @@ ROT_DIM = 64
 # every symbol include/mrope.h declares
 EXPORTS = ("mrope_abi_version", "mrope_status_string", "mrope_last_error", "mrope_set_test_hooks",
            "mrope_workspace_bytes",
-           "mrope_workspace_init", "mrope_planes", "mrope_apply", "mrope_apply_ids", "mrope_apply_kv",
+           "mrope_workspace_init", "mrope_planes", "mrope_apply", "mrope_apply_ids", "mrope_apply_ids_noalloc",
+           "mrope_apply_kv",
            "mrope_apply_ids_kv", "mrope_decode")
 
 
@@ -79,6 +80,9 @@ def load():
     lib.mrope_apply_ids.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
                                     P, P, I32, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_apply_ids.restype = ctypes.c_int
+    lib.mrope_apply_ids_noalloc.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
+                                            P, P, I32, I32, I32, P, P, P, I64, P, P, P, P, P]
+    lib.mrope_apply_ids_noalloc.restype = ctypes.c_int
     cache = [P, P, P, I32, I64, I64, I64, I64]  # k_cache, v_cache, slot_mapping, block_size, num_blocks, strides
     lib.mrope_apply_kv.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I64, I32, I32, I32, P, I64, F64,
                                    *cache, P]
@@ -327,6 +331,44 @@ def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seq
                                       _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
                                       int(frame_len), _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
                                       _ptr(seq_flags), ws.ptr, ws.capacity, ws.next_epoch(), _stream(dev)))
+    return start, amount, origin, seq_flags, planes_out
+
+
+NOALLOC_MAX_TOKENS = 1 << 20
+
+
+def apply_ids_noalloc(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seqlens: torch.Tensor,
+                      marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
+                      origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67, q_out=None,
+                      k_out=None, rot_dim: int = ROT_DIM):
+    """apply_ids without a workspace: the library's static per-GPU scratch stands in for it (at most
+    NOALLOC_MAX_TOKENS tokens).  Pass every output (start, amount, origin, seq_flags) to allocate
+    nothing here either.  The first call on a device must not be captured in a graph."""
+    dev = _require_cuda(q, k, ids, cu_seqlens, planes_out, start, amount, origin, seq_flags, q_out, k_out,
+                        pos_offset, origin_in)
+    dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, q_out, k_out)
+    _i32_vec(ids, "ids", q.shape[0])
+    _i32_vec(cu_seqlens, "cu_seqlens")
+    T = q.shape[0]
+    n = cu_seqlens.numel() - 1
+    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in")):
+        if t is not None:
+            _i32_vec(t, name, n)
+    ps = 0
+    if planes_out is not None:
+        if planes_out.dtype != torch.int32 or planes_out.dim() != 2 or planes_out.shape[0] != 3 \
+                or planes_out.shape[1] < T or planes_out.stride(1) != 1:
+            raise ValueError("planes_out must be an int32 [3, >= tokens] tensor with unit column stride")
+        ps = planes_out.stride(0)
+    mk = lambda t, name: _i32_vec(t, name, n) if t is not None else torch.empty(n, dtype=torch.int32, device=dev)
+    start, amount, origin, seq_flags = (mk(start, "start"), mk(amount, "amount"), mk(origin, "origin"),
+                                        mk(seq_flags, "seq_flags"))
+    with _on_device(dev):
+        _check(load().mrope_apply_ids_noalloc(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt,
+                                              float(theta), _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n,
+                                              int(marker_id), int(frame_len), _ptr(pos_offset), _ptr(origin_in),
+                                              _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
+                                              _ptr(seq_flags), _stream(dev)))
     return start, amount, origin, seq_flags, planes_out
 
 

@@ -2,6 +2,7 @@
 // and documented in include/mrope.h.
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -16,6 +17,7 @@ namespace mrope {
 static std::atomic<int> g_test_hooks{0};
 int test_hooks() { return g_test_hooks.load(std::memory_order_relaxed); }
 }  // namespace mrope
+
 
 namespace {
 
@@ -211,6 +213,46 @@ PagedKV make_paged(const void *v, int64_t v_tok, int64_t v_head, void *k_cache, 
 
 }  // namespace
 
+// ------------------------------------------------------------------ static scratch -------------
+// The workspace of mrope_apply_ids_noalloc: a file-scope device array, one copy per GPU, held until
+// the process ends.  In host code `scratch` only stands in for the symbol; the device address of a
+// GPU's copy comes from hipGetSymbolAddress with that GPU current, once, and is kept per device.
+// The first call on a device also clears the copy with a kernel on the caller's stream (so it must
+// not be captured in a graph); later calls tag their words with the device epoch counter kept in
+// the copy, so they need no clearing.
+constexpr int64_t kScratchMaxTokens = 1 << 20;
+constexpr size_t kScratchBytes = ws_layout(kScratchMaxTokens).total;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices];  // device address of each GPU's copy; set once under the mutex
+
+// The current device's copy of the scratch array, looked up and cleared on the first call.
+mrope_status scratch_for_current_device(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return fail(MROPE_ERR_HIP, "mrope_apply_ids_noalloc: no usable current device (%d)", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+            return fail(MROPE_ERR_ARG, "mrope_apply_ids_noalloc: the first call on a device clears its scratch "
+                                       "and must not be captured in a graph");
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress");
+        const hipError_t z = launch_workspace_init(ptr, kScratchBytes, stream);
+        if (z != hipSuccess) return hip_status(z, "mrope_apply_ids_noalloc scratch clear");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MROPE_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int mrope_abi_version(void) { return MROPE_ABI_VERSION; }
@@ -344,6 +386,45 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
     const Heads h = make_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
                                n_tokens, head_dim, q_out, k_out);
     return hip_status(launch_apply_ids(h, make_rotary(theta), sc, PagedKV{}, dtype, s), "mrope_apply_ids");
+}
+
+mrope_status mrope_apply_ids_noalloc(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads,
+                                     void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads,
+                                     int64_t n_tokens, int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta,
+                                     void *q_out, void *k_out, const int32_t *ids, const int32_t *cu_seqlens,
+                                     int32_t n_seqs, int32_t marker_id, int32_t frame_len, const int32_t *pos_offset,
+                                     const int32_t *origin_in, int32_t *planes_out, int64_t plane_stride,
+                                     int32_t *start, int32_t *amount, int32_t *origin, int32_t *seq_flags,
+                                     void *stream)
+{
+    if (n_tokens > kScratchMaxTokens)
+        return fail(MROPE_ERR_WORKSPACE, "mrope_apply_ids_noalloc takes at most %lld tokens (got %lld)",
+                    (long long)kScratchMaxTokens, (long long)n_tokens);
+    mrope_status st = check_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
+                                  n_tokens, head_dim, rot_dim, dtype, q_out, k_out);
+    if (st != MROPE_OK) return st;
+    if (!(theta > 0.0) || !std::isfinite(theta)) return fail(MROPE_ERR_ARG, "theta must be finite and > 0");
+    // the scratch stands in for a workspace of kScratchMaxTokens tokens: checked with a placeholder
+    // address here, before anything touches the device
+    const uintptr_t placeholder = 256;
+    st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes_out, plane_stride, reinterpret_cast<void *>(placeholder),
+                    kScratchBytes, false);
+    if (st != MROPE_OK) return st;
+    if ((st = check_frame_len(frame_len)) != MROPE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    void *ws = nullptr;
+    if ((st = scratch_for_current_device(s, &ws)) != MROPE_OK) return st;
+    // epoch 0: the device counter in the scratch tags each call (graph replays stay distinct)
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, pos_offset, origin_in,
+                              planes_out, plane_stride, start, amount, origin, seq_flags, ws, 0);
+    if (n_tokens == 0) {
+        if (n_seqs > 0 && any_scalar(sc)) return hip_status(launch_text_scalars(sc, s), "mrope_apply_ids_noalloc");
+        return MROPE_OK;
+    }
+    const Heads h = make_heads(q, q_tok_stride, q_head_stride, n_q_heads, k, k_tok_stride, k_head_stride, n_k_heads,
+                               n_tokens, head_dim, q_out, k_out);
+    return hip_status(launch_apply_ids(h, make_rotary(theta), sc, PagedKV{}, dtype, s), "mrope_apply_ids_noalloc");
 }
 
 mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads,

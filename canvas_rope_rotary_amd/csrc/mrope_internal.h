@@ -22,14 +22,14 @@ struct WsLayout {
     size_t status, parts, tagged, total;
 };
 
-inline size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
+constexpr size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
 
-inline WsLayout ws_layout(int64_t n_tokens)
+constexpr WsLayout ws_layout(int64_t n_tokens)
 {
     if (n_tokens < 0) n_tokens = 0;
     const size_t chunks = (size_t)((n_tokens + kChunkTokens - 1) / kChunkTokens);
     const size_t parts = (size_t)((n_tokens + kPartTokens - 1) / kPartTokens);
-    WsLayout w;
+    WsLayout w{};
     w.status = kWsHeaderBytes;
     w.parts = w.status + ws_round(chunks * 8);
     w.tagged = w.parts + ws_round(parts * 16);

@@ -213,6 +213,29 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              size_t workspace_bytes, uint32_t epoch, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * mrope_apply_ids_noalloc -- mrope_apply_ids for callers that cannot allocate device memory or pass
+ * a workspace: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors as mrope_apply_ids, without workspace, workspace_bytes and epoch.
+ * The workspace is a static device array inside the library: one copy per GPU, allocated when the
+ * library's code is loaded and held until the process ends (MROPE_NOALLOC_MAX_TOKENS tokens'
+ * worth, about 25.7 MB).  n_tokens above MROPE_NOALLOC_MAX_TOKENS returns MROPE_ERR_WORKSPACE.
+ * The call allocates nothing.  Its first call on a device looks the array up and clears it with a
+ * kernel on `stream`; that first call must not be captured in a graph (MROPE_ERR_ARG if it is).
+ * Each later call tags its words with the device epoch counter kept in the array, so calls and
+ * graph replays need no clearing.  All calls on one GPU share the array: calls that overlap on
+ * one GPU (different streams, not ordered) race.
+ * ------------------------------------------------------------------------------------------- */
+#define MROPE_NOALLOC_MAX_TOKENS (1 << 20)
+mrope_status mrope_apply_ids_noalloc(void *q, int64_t q_tok_stride, int64_t q_head_stride, int32_t n_q_heads,
+                                     void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads,
+                                     int64_t n_tokens, int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta,
+                                     void *q_out, void *k_out, const int32_t *ids, const int32_t *cu_seqlens,
+                                     int32_t n_seqs, int32_t marker_id, int32_t frame_len, const int32_t *pos_offset,
+                                     const int32_t *origin_in, int32_t *planes_out, int64_t plane_stride,
+                                     int32_t *start, int32_t *amount, int32_t *origin, int32_t *seq_flags,
+                                     void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Paged K/V cache (mrope_apply_kv, mrope_apply_ids_kv, mrope_decode).  The K and V caches are the
  * decoder's state ([card] "How the VLM rides the text-only engine": the keyCache [6, 1, 2, -1, 256],
  * 2 KV heads of 256 dims); their paging is the serving engine's layout.

@@ -194,3 +194,23 @@ def test_product_path_never_touches_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b|\boracle\.\w+\(|liboracle|mrope_oracle",
                                      src, re.M), f
+
+
+def _apply_ids_noalloc(lib, **kw):
+    a = dict(q=A, qt=2048, qh=256, nq=8, k=A, kt=512, kh=256, nk=2, n=1000, hd=256, rot=64, dt=BF16, theta=1e7,
+             ids=A, cu=A, ns=4, marker=248078, fl=0, planes=None, ps=0)
+    a.update(kw)
+    return lib.mrope_apply_ids_noalloc(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["n"],
+                                       a["hd"], a["rot"], a["dt"], a["theta"], None, None, a["ids"], a["cu"], a["ns"],
+                                       a["marker"], a["fl"], None, None, a["planes"], a["ps"], None, None, None, None,
+                                       None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=(1 << 20) + 1), WS), (dict(ids=None), ARG), (dict(cu=None), ARG), (dict(ns=0), ARG),
+    (dict(rot=32), UNSUP), (dict(q=A + 8), ALIGN), (dict(theta=0.0), ARG), (dict(fl=30), ARG),
+    (dict(planes=A, ps=999), ARG),
+])
+def test_apply_ids_noalloc_validation(lib, kw, code):
+    """Rejected on the host before the first use of the static scratch (nothing is launched)."""
+    assert _apply_ids_noalloc(lib, **kw) == code
