@@ -2,7 +2,9 @@
 oracle on the same inputs.  No method arithmetic here."""
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -54,6 +56,45 @@ def compare_heads(got: np.ndarray, x_in: np.ndarray, planes: np.ndarray, dtype: 
         ok, info = check_bf16(got, oracle.round_f16(ref))
     else:
         ok, info = check_fp32(got, ref)
+    assert ok, f"{what}: {info}"
+    return info
+
+
+def host_threads() -> int:
+    """Worker threads for host-side checks: the CPUs this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def compare_heads_all(got: torch.Tensor, x_in: np.ndarray, planes: np.ndarray, dtype: str, theta=1e7, what="",
+                      block: int = 8192):
+    """Every element of a full-size result against the oracle: `got` is the device result [rows,
+    heads, head_dim] (rows in the order of x_in and planes), copied to the host once; the oracle runs
+    over blocks of rows in host threads (its C calls release the interpreter lock).  The same gates
+    as compare_heads; the worst figures over all blocks are returned."""
+    host = host_heads(got)
+    n = host.shape[0]
+    assert x_in.shape[0] == n and planes.shape[1] == n, what
+
+    def one(lo):
+        hi = min(n, lo + block)
+        ref = oracle.rotate(as_f32(x_in[lo:hi], dtype), np.ascontiguousarray(planes[:, lo:hi]), theta)
+        if dtype == "bf16":
+            return check_bf16(host[lo:hi], oracle.round_bf16(ref))
+        if dtype == "f16":
+            return check_bf16(host[lo:hi], oracle.round_f16(ref))
+        return check_fp32(host[lo:hi], ref)
+
+    with ThreadPoolExecutor(host_threads()) as ex:
+        results = list(ex.map(one, range(0, n, block)))
+    ok = all(r[0] for r in results)
+    info = {"rows": n, "blocks": len(results)}
+    for key in results[0][1] if results else ():
+        vals = [r[1][key] for r in results]
+        info[key] = all(vals) if isinstance(vals[0], bool) else (sum(vals) if key.startswith("n_") else max(vals))
     assert ok, f"{what}: {info}"
     return info
 

@@ -16,7 +16,7 @@ import torch
 import canvas_rope_rotary_amd as mr
 import oracle
 from canvas_rope_rotary_amd import synth
-from gpu_util import MARKER, TORCH_DT, compare_heads, dev_heads, host_heads, i32, say
+from gpu_util import MARKER, TORCH_DT, compare_heads, compare_heads_all, dev_heads, host_heads, i32, say
 
 pytestmark = pytest.mark.gpu
 
@@ -171,9 +171,9 @@ def test_decode_with_v(dtype):
     assert not synth.to_f32(flat[~written], dtype).any() if dtype != "f32" else not flat[~written].any()
 
 
-def test_apply_ids_kv_full_size_sampled():
+def test_apply_ids_kv_full_size():
     """64 x 4096 bf16 prompts with V, caches of 16-token blocks with room for 1.25x the tokens:
-    planes in full, Q and the cache rows on sampled tokens (every frame, sequence ends, random)."""
+    planes, Q, every written K and V cache row in full."""
     b = synth.config2()
     T = b.n_tokens
     say(f"case: apply_ids_kv full size tokens={T}")
@@ -188,22 +188,12 @@ def test_apply_ids_kv_full_size_sampled():
                     planes_out=pl)
     epl, est, eam, eog = oracle.planes(b.ids, b.cu_seqlens, MARKER)
     np.testing.assert_array_equal(pl.cpu().numpy(), epl)
-    idx = set(np.random.default_rng(242).integers(0, T, size=6000).tolist())
-    for s in range(b.n_seqs):
-        lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
-        idx.update((lo, hi - 1))
-        if eog[s] >= 0:
-            idx.update(range(lo + int(eog[s]), min(lo + int(eog[s]) + 70, hi)))
-    idx = np.array(sorted(idx), np.int64)
-    compare_heads(host_heads(q[idx]), qn[idx], epl[:, idx], "bf16", what="q sampled")
+    compare_heads_all(q, qn, epl, "bf16", what="q")
     S = nb * 16
-    sl = slots[idx]
-    ok = (sl >= 0) & (sl < S)
-    rows = torch.from_numpy(sl[ok]).cuda()
-    got_k = host_heads(kc.view(S, 2, 256)[rows])
-    got_v = host_heads(vc.view(S, 2, 256)[rows])
-    compare_heads(got_k, kn[idx[ok]], epl[:, idx[ok]], "bf16", what="k cache sampled")
-    np.testing.assert_array_equal(got_v, vn[idx[ok]])
+    ok = (slots >= 0) & (slots < S)
+    rows = torch.from_numpy(slots[ok]).cuda()
+    compare_heads_all(kc.view(S, 2, 256)[rows], kn[ok], epl[:, ok], "bf16", what="k cache")
+    np.testing.assert_array_equal(host_heads(vc.view(S, 2, 256)[rows]), vn[ok])
     # every valid slot was written: no zero rows left among them (inputs ~ N(0, 1) are never all zero)
     all_ok = (slots >= 0) & (slots < S)
     written = kc.view(S, 2 * 256)[torch.from_numpy(slots[all_ok]).cuda()].abs().amax(dim=1)
@@ -213,8 +203,8 @@ def test_apply_ids_kv_full_size_sampled():
 @pytest.mark.parametrize("fused", [False, True, "planes_out"])
 def test_kv_past_the_store_hint_size(fused):
     """96 x 4096 bf16 tokens write 403 MB of Q in place, past the size from which the cache-writing
-    kernels' Q stores take the non-temporal hint: Q and the cache rows on sampled tokens.  With
-    planes_out the fused call runs as the scan launch and then mrope_apply_kv's launch."""
+    kernels' Q stores take the non-temporal hint: Q and every written cache row.  With planes_out
+    the fused call runs as the scan launch and then mrope_apply_kv's launch."""
     origins = [int(o) for o in np.random.default_rng(251).integers(0, 513, size=96)]
     b = synth._batch("96x4096-image-bf16", 251, [4096] * 96, origins, "bf16")
     T = b.n_tokens
@@ -237,16 +227,9 @@ def test_kv_past_the_store_hint_size(fused):
             np.testing.assert_array_equal(pl.cpu().numpy(), epl)
     else:
         mr.apply_kv(q, k, v, i32(epl), kc, vc, sl_dev)
-    idx = set(np.random.default_rng(253).integers(0, T, size=4000).tolist())
-    for s in range(b.n_seqs):
-        lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
-        idx.update((lo, hi - 1))
-        idx.update(range(lo + int(eog[s]), min(lo + int(eog[s]) + 70, hi)))
-    idx = np.array(sorted(idx), np.int64)
-    compare_heads(host_heads(q[torch.from_numpy(idx).cuda()]), qn[idx], epl[:, idx], "bf16", what="q sampled")
+    compare_heads_all(q, qn, epl, "bf16", what="q")
     S = nb * 16
-    sl = slots[idx]
-    ok = (sl >= 0) & (sl < S)
-    rows = torch.from_numpy(sl[ok]).cuda()
-    compare_heads(host_heads(kc.view(S, 2, 256)[rows]), kn[idx[ok]], epl[:, idx[ok]], "bf16", what="k cache sampled")
-    np.testing.assert_array_equal(host_heads(vc.view(S, 2, 256)[rows]), vn[idx[ok]])
+    ok = (slots >= 0) & (slots < S)
+    rows = torch.from_numpy(slots[ok]).cuda()
+    compare_heads_all(kc.view(S, 2, 256)[rows], kn[ok], epl[:, ok], "bf16", what="k cache")
+    np.testing.assert_array_equal(host_heads(vc.view(S, 2, 256)[rows]), vn[ok])

@@ -3,7 +3,7 @@
 Planes, start, amount, origin and flags: bit-exact.  Rotated Q/K: fp32 within 2e-6 of the oracle
 (pair-norm relative), bf16 within 1 ulp of the fp32 oracle rounded to bf16; the dims past the
 rotary part bit-identical.  Small inputs are compared element by element; the full-size workloads
-in full for planes and on sampled tokens for the rotation.
+in full, planes and every rotated element (the oracle runs over blocks of tokens in host threads).
 """
 import ctypes
 
@@ -14,7 +14,8 @@ import torch
 import canvas_rope_rotary_amd as mr
 import oracle
 from canvas_rope_rotary_amd import synth
-from gpu_util import MARKER, TORCH_DT, as_f32, compare_heads, dev_heads, expected_flags, host_heads, i32, say
+from gpu_util import (MARKER, TORCH_DT, as_f32, compare_heads, compare_heads_all, dev_heads, expected_flags, host_heads,
+                      i32, say)
 from parity import check_bf16, check_fp32
 
 pytestmark = pytest.mark.gpu
@@ -33,21 +34,6 @@ def _check_scan(b, pl, st, am, og, fl, what):
     if fl is not None:
         np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg=f"{what} flags")
     return epl, est, eam, eog
-
-
-def _sample_tokens(b, og, n_random=4096, seed=0):
-    idx = set()
-    g = np.random.default_rng(seed)
-    for s in range(b.n_seqs):
-        lo, hi = int(b.cu_seqlens[s]), int(b.cu_seqlens[s + 1])
-        if hi == lo:
-            continue
-        idx.update((lo, hi - 1))
-        if og[s] >= 0:
-            o = lo + int(og[s])
-            idx.update(range(o, min(o + 70, hi)))
-    idx.update(g.integers(0, b.n_tokens, size=min(n_random, b.n_tokens)).tolist())
-    return np.array(sorted(idx), np.int64)
 
 
 # ------------------------------------------------------------------ small, element by element ---
@@ -197,10 +183,8 @@ def test_fused_split_grid_levels(n_chunks, planes_out):
         epl, est, eam, eog = _oracle_planes(b)
         for got, want in ((st, est), (am, eam), (og, eog)):
             np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=b.name)
-    idx = np.arange(b.n_tokens) if b.n_tokens <= 25000 else _sample_tokens(b, eog, seed=n_chunks)
-    ti = torch.from_numpy(idx).cuda()
-    compare_heads(host_heads(q[ti]), qn[idx], epl[:, idx], "bf16", what=f"{b.name} q")
-    compare_heads(host_heads(k[ti]), kn[idx], epl[:, idx], "bf16", what=f"{b.name} k")
+    compare_heads_all(q, qn, epl, "bf16", what=f"{b.name} q")
+    compare_heads_all(k, kn, epl, "bf16", what=f"{b.name} k")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -491,8 +475,9 @@ def test_red_arms_fail_on_gpu_output():
 
 def _full_prefill(b, fused: bool, planes_out: bool = False):
     """The fused call runs as benchmarked, without planes_out: planes never leave the kernel, so the
-    scalars are compared bit for bit and the planes through the rotation.  With planes_out (large
-    inputs then take the scan launch and the rotation launch) the planes are compared in full too."""
+    scalars are compared bit for bit and the planes through the rotation.  With planes_out the
+    planes are compared in full too.  Every rotated element of Q and K is compared with the oracle
+    (host threads over blocks of tokens), and dims 64.. must be untouched."""
     say(f"case: {b.name} tokens={b.n_tokens} seqs={b.n_seqs} fused={fused} planes_out={planes_out}")
     qn, kn = b.qk()
     ids, cu = i32(b.ids), i32(b.cu_seqlens)
@@ -514,12 +499,11 @@ def _full_prefill(b, fused: bool, planes_out: bool = False):
         torch.cuda.synchronize()
         epl, est, eam, eog = _check_scan(b, pl, st, am, og, fl, b.name)
     assert torch.equal(q[..., 64:], q_tail) and torch.equal(k[..., 64:], k_tail)
-    idx = _sample_tokens(b, eog)
-    ti = torch.from_numpy(idx).cuda()
-    say(f"  sampled {idx.size} tokens")
-    compare_heads(host_heads(q[ti]), qn[idx], epl[:, idx], b.dtype, what=f"{b.name} q")
-    compare_heads(host_heads(k[ti]), kn[idx], epl[:, idx], b.dtype, what=f"{b.name} k")
-    del q, k, q_tail, k_tail
+    del q_tail, k_tail
+    info = compare_heads_all(q, qn, epl, b.dtype, what=f"{b.name} q")
+    compare_heads_all(k, kn, epl, b.dtype, what=f"{b.name} k")
+    say(f"  every element compared: {info}")
+    del q, k
     torch.cuda.empty_cache()
     return eog
 
@@ -560,7 +544,7 @@ def _image_batch(name, seed, n_seqs, length, dtype):
 @pytest.mark.parametrize("fused", [False, True])
 def test_fp32_past_the_store_hint_size(fused):
     """40 x 4096 fp32 tokens write 419 MB in place, past the size from which the rotation kernels'
-    stores take the non-temporal hint: the hinted kernels against the oracle on sampled tokens."""
+    stores take the non-temporal hint: the hinted kernels against the oracle, every element."""
     _full_prefill(_image_batch("40x4096-image-f32", 12, 40, 4096, "f32"), fused=fused)
 
 
@@ -569,9 +553,9 @@ def test_ragged_past_the_size_thresholds(seed, total, hi):
     """Ragged batches past the sizes where the fused kernel splits every chunk in two, where
     planes_out makes mrope_apply_ids two launches and where stores take the non-temporal hint: a
     total that leaves the last chunk partial (333,333 tokens, 408 sequences) and 3,426 short
-    sequences (more than one 64-sequence window per chunk).  Scalars and planes in full, rotation
-    on sampled tokens (every frame, every sequence end, random), for the fused call with and
-    without planes_out, out of place (inputs untouched), and for planes + apply."""
+    sequences (more than one 64-sequence window per chunk).  Scalars, planes and every rotated
+    element in full, for the fused call with and without planes_out, out of place (inputs
+    untouched), and for planes + apply."""
     lengths, kinds = synth.ragged_lengths(seed, total, hi=hi)
     g = np.random.default_rng(seed)
     placed = [int(g.integers(0, max(1, n - 67))) if k else None for n, k in zip(lengths, kinds)]
@@ -580,8 +564,6 @@ def test_ragged_past_the_size_thresholds(seed, total, hi):
     qn, kn = b.qk()
     ids, cu = i32(b.ids), i32(b.cu_seqlens)
     epl, est, eam, eog = _oracle_planes(b)
-    idx = _sample_tokens(b, eog, n_random=2000, seed=seed)
-    ti = torch.from_numpy(idx).cuda()
     for mode in ("fused", "fused_planes_out", "fused_out_of_place", "planes_apply"):
         q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
         pl = torch.full((3, b.n_tokens), -9, dtype=torch.int32, device="cuda")
@@ -590,8 +572,8 @@ def test_ragged_past_the_size_thresholds(seed, total, hi):
         elif mode == "fused_out_of_place":
             qo, ko = torch.empty_like(q), torch.empty_like(k)
             st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER, q_out=qo, k_out=ko)
-            np.testing.assert_array_equal(host_heads(q[ti]), qn[idx], err_msg="q input changed")
-            np.testing.assert_array_equal(host_heads(k[ti]), kn[idx], err_msg="k input changed")
+            np.testing.assert_array_equal(host_heads(q), qn, err_msg="q input changed")
+            np.testing.assert_array_equal(host_heads(k), kn, err_msg="k input changed")
             q, k = qo, ko
         elif mode == "fused_planes_out":
             st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER, planes_out=pl)
@@ -603,8 +585,8 @@ def test_ragged_past_the_size_thresholds(seed, total, hi):
         np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg=f"{mode} flags")
         if mode in ("fused_planes_out", "planes_apply"):
             np.testing.assert_array_equal(pl.cpu().numpy(), epl, err_msg=f"{mode} planes")
-        compare_heads(host_heads(q[ti]), qn[idx], epl[:, idx], "bf16", what=f"{mode} q")
-        compare_heads(host_heads(k[ti]), kn[idx], epl[:, idx], "bf16", what=f"{mode} k")
+        compare_heads_all(q, qn, epl, "bf16", what=f"{mode} q")
+        compare_heads_all(k, kn, epl, "bf16", what=f"{mode} k")
         del q, k, pl
         torch.cuda.empty_cache()
 
