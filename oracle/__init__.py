@@ -59,7 +59,9 @@ def _load():
     lib.oracle_frame_scalars.restype = None
     lib.oracle_planes.argtypes = [P, P, i32, i32, P, i64, P, P, P]
     lib.oracle_planes.restype = None
-    lib.oracle_planes_chunk.argtypes = [P, P, i32, i32, i32, P, P, P, i64, P, P, P]
+    lib.oracle_planes_chunk.argtypes = [P, P, i32, i32, i32, P, P, P, P, i64, P, P, P]
+    lib.oracle_seq_frame_len.argtypes = [P, i32, i32]
+    lib.oracle_seq_frame_len.restype = i32
     lib.oracle_frame_scalars_len.argtypes = [i32, i32, P, P]
     lib.oracle_frame_scalars_len.restype = None
     lib.oracle_planes_chunk.restype = None
@@ -121,25 +123,35 @@ def planes(ids, cu_seqlens, marker_id: int):
     return pl, st, am, og
 
 
-def planes_chunk(ids, cu_seqlens, marker_id: int, pos_offset=None, origin_in=None, frame_len: int = 67):
+def planes_chunk(ids, cu_seqlens, marker_id: int, pos_offset=None, origin_in=None, frame_len: int = 67,
+                 frame_len_seq=None):
     """Planes of a later piece of each sequence: token i of sequence s sits at pos_offset[s] + i, and
     origin_in[s] (-1 = none) is the origin found in the earlier pieces; frame_len tokens from the
-    origin to start.  Returns planes [3, L], start, amount, origin (the sequence's origin so far,
-    -1 = none)."""
+    origin to start, or frame_len_seq[s] for a sequence that gives its own (0: the call's; an entry
+    outside [65, 4096] also falls back to the call's).  Returns planes [3, L], start, amount,
+    origin (the sequence's origin so far, -1 = none)."""
     ids = _c(ids, np.int32)
     cu = _c(cu_seqlens, np.int32)
     n = cu.size - 1
     total = int(cu[-1])
     po = _c(pos_offset, np.int32) if pos_offset is not None else None
     oi = _c(origin_in, np.int32) if origin_in is not None else None
+    fs = _c(frame_len_seq, np.int32) if frame_len_seq is not None else None
     pl = np.zeros((3, max(total, 1)), np.int32)[:, :total].copy()
     st = np.zeros(n, np.int32)
     am = np.zeros(n, np.int32)
     og = np.zeros(n, np.int32)
     _load().oracle_planes_chunk(_ptr(ids), _ptr(cu), n, int(marker_id), int(frame_len),
+                                _ptr(fs) if fs is not None else None,
                                 _ptr(po) if po is not None else None,
                                 _ptr(oi) if oi is not None else None, _ptr(pl), total, _ptr(st), _ptr(am), _ptr(og))
     return pl, st, am, og
+
+
+def seq_frame_len(frame_len_seq, s: int, frame_len: int = 67) -> int:
+    """The frame length the oracle uses for sequence s (see oracle_seq_frame_len)."""
+    fs = _c(frame_len_seq, np.int32) if frame_len_seq is not None else None
+    return int(_load().oracle_seq_frame_len(_ptr(fs) if fs is not None else None, int(s), int(frame_len)))
 
 
 def inv_freq(theta: float = 1e7, rot_dim: int = 64) -> np.ndarray:

@@ -158,17 +158,33 @@ void oracle_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs
 }
 
 /* ---------------------------------------------------------------------------------------------
+ * The frame length of sequence s: frame_len_seq[s] when the caller gives one for it, else the call's
+ * frame_len.  An entry of 0 means "the call's"; an entry outside [65, 4096] cannot describe a frame
+ * (the canvas alone is 66 tokens with </image>, 65 without) and is replaced by the call's frame_len
+ * (the GPU flags such a sequence).  frame_len_seq may be NULL.
+ * ------------------------------------------------------------------------------------------- */
+int32_t oracle_seq_frame_len(const int32_t *frame_len_seq, int32_t s, int32_t frame_len)
+{
+    int32_t f = frame_len_seq ? frame_len_seq[s] : 0;
+    if (f == 0 || f < 65 || f > 4096) return frame_len;
+    return f;
+}
+
+/* ---------------------------------------------------------------------------------------------
  * Planes of a later piece of each sequence (chunked prefill, a second turn: Core AI model-zoo page,
  * section "Prefill in chunks and a second turn"; Hugging Face card, section "Measured", the chunked
  * prefill and second-question paragraphs).  The tokens of sequence s continue its earlier ones:
  * token i sits at position pos_offset[s] + i.  origin_in[s] is the canvas origin found in the earlier
  * pieces (-1: none yet); the first marker of the whole sequence wins, so a marker in this piece
  * counts only when no earlier piece had one.  pos_offset / origin_in may be NULL (0 / -1).
- * frame_len: tokens from O to start (67 for this model's template; see frame_offset).
+ * frame_len: tokens from O to start (67 for this model's template; see frame_offset), for every
+ * sequence whose frame_len_seq entry (NULL: none) does not give its own (oracle_seq_frame_len): a
+ * packed batch may mix templates whose frames end differently.
  * ------------------------------------------------------------------------------------------- */
 void oracle_planes_chunk(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
-                         int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes,
-                         int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin)
+                         int32_t frame_len, const int32_t *frame_len_seq, const int32_t *pos_offset,
+                         const int32_t *origin_in, int32_t *planes, int64_t plane_stride, int32_t *start,
+                         int32_t *amount, int32_t *origin)
 {
     for (int32_t s = 0; s < n_seqs; ++s) {
         int32_t b = cu_seqlens[s], n = cu_seqlens[s + 1] - cu_seqlens[s];
@@ -179,7 +195,7 @@ void oracle_planes_chunk(const int32_t *ids, const int32_t *cu_seqlens, int32_t 
             if (f >= 0) o = off + f;
         }
         int32_t st, am;
-        oracle_frame_scalars_len(o, frame_len, &st, &am);
+        oracle_frame_scalars_len(o, oracle_seq_frame_len(frame_len_seq, s, frame_len), &st, &am);
         start[s] = st;
         amount[s] = am;
         if (origin) origin[s] = o;

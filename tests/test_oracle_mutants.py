@@ -40,6 +40,14 @@ MUTANTS = [
     ("decode ignores amount", "int32_t plane = pos[s] - amount[s];", "int32_t plane = pos[s];"),
     ("pieces ignore the carried origin", "int32_t o = (origin_in && origin_in[s] >= 0) ? origin_in[s] : -1;",
      "int32_t o = -1;"),
+    ("per-sequence frame length ignored",
+     "oracle_frame_scalars_len(o, oracle_seq_frame_len(frame_len_seq, s, frame_len), &st, &am);",
+     "oracle_frame_scalars_len(o, frame_len, &st, &am);"),
+    ("per-sequence frame lengths one sequence late",
+     "int32_t f = frame_len_seq ? frame_len_seq[s] : 0;",
+     "int32_t f = frame_len_seq ? frame_len_seq[s > 0 ? s - 1 : 0] : 0;"),
+    ("unusable frame length kept", "if (f == 0 || f < 65 || f > 4096) return frame_len;",
+     "if (f == 0) return frame_len;"),
     ("pieces ignore the position offset", "int32_t off = pos_offset ? pos_offset[s] : 0;", "int32_t off = 0;"),
     ("paged block and row swapped", "const int64_t block = slot / block_size, within = slot % block_size;",
      "const int64_t block = slot % block_size, within = slot / block_size;"),

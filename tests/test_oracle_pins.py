@@ -509,3 +509,50 @@ def test_frame_len_67_is_the_default_rule():
     c = oracle.planes_chunk(b.ids, b.cu_seqlens, MARKER, frame_len=67)
     for x, y in zip(a, c):
         np.testing.assert_array_equal(x, y)
+
+
+def test_frame_len_per_sequence_mixed_batch():
+    """One packed batch mixing templates: frames of 65, 67 and 75 tokens, a sequence whose entry is 0
+    and one whose entry (64) cannot describe a frame -- both take the call's frame length (70 here).
+    Every sequence gets start = O + F and amount = F - 9 of its own F (the kit numbers and the closed
+    form above), a text-only sequence (1 << 30, 0) whatever its entry, and the planes of each
+    sequence equal those of the same tokens alone with that frame length (pinned by the table test)."""
+    lens = [300, 260, 280, 150, 90, 200, 120, 75]
+    placed = [5, 12, 0, None, 40, 7, 3, 0]
+    entries = [65, 67, 75, 75, 0, 64, 4097, 4096]
+    call = 70
+    g = synth.rng(41, 98)
+    parts = [synth.prompt_ids(g, n, o) for n, o in zip(lens, placed)]
+    ids = np.concatenate(parts)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pl, st, am, og = oracle.planes_chunk(ids, cu, MARKER, frame_len=call, frame_len_seq=entries)
+    for s, (n, o, e) in enumerate(zip(lens, placed, entries)):
+        f = e if 65 <= e <= 4096 else call
+        assert oracle.seq_frame_len(entries, s, call) == f
+        if o is None:
+            assert (st[s], am[s], og[s]) == (1 << 30, 0, -1)
+        else:
+            assert (st[s], am[s], og[s]) == (o + f, f - 9, o), s
+        alone = oracle.planes_chunk(parts[s], [0, n], MARKER, frame_len=f)
+        np.testing.assert_array_equal(pl[:, cu[s]:cu[s + 1]], alone[0], err_msg=f"sequence {s}")
+    # with every entry 0 the array changes nothing
+    zero = oracle.planes_chunk(ids, cu, MARKER, frame_len=call, frame_len_seq=np.zeros(len(lens)))
+    plain = oracle.planes_chunk(ids, cu, MARKER, frame_len=call)
+    for x, y in zip(zero, plain):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_frame_len_per_sequence_with_pieces():
+    """A later piece of a sequence with its own frame length: the 75-token frame of the carried
+    origin 10 ends at 85, so the piece starting at position 80 holds 5 marker-row tokens (10, 10, 10)
+    and then p - 66; the other sequence of the call (entry 0, call's 67) has p - 58 throughout."""
+    ids = synth.text_ids(synth.rng(5, 1), 40)
+    pl, st, am, og = oracle.planes_chunk(ids, [0, 20, 40], MARKER, pos_offset=[80, 100], origin_in=[10, 6],
+                                         frame_len=67, frame_len_seq=[75, 0])
+    assert (st[0], am[0], og[0]) == (85, 66, 10)
+    assert (st[1], am[1], og[1]) == (73, 58, 6)
+    for i in range(20):
+        p = 80 + i
+        want = (10, 10, 10) if p < 85 else (p - 66,) * 3
+        assert tuple(pl[:, i]) == want, p
+    np.testing.assert_array_equal(pl[0, 20:], np.arange(100, 120) - 58)
