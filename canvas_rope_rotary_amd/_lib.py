@@ -38,6 +38,7 @@ def set_test_hooks(flags: int) -> int:
 class MarkerFlags(enum.IntFlag):
     MULTI_MARKER = 1
     FRAME_OVERRUN = 2
+    BAD_FRAME_LEN = 4
 
 
 class MropeError(RuntimeError):
@@ -73,22 +74,22 @@ def load():
     lib.mrope_workspace_init.argtypes = [P, U64, P]
     lib.mrope_workspace_init.restype = ctypes.c_int
     U32 = ctypes.c_uint32
-    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
+    lib.mrope_planes.argtypes = [P, P, I32, I64, I32, I32, P, P, P, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_planes.restype = ctypes.c_int
     lib.mrope_apply.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, P, I64, F64, P, P, P]
     lib.mrope_apply.restype = ctypes.c_int
     lib.mrope_apply_ids.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
-                                    P, P, I32, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, P]
+                                    P, P, I32, I32, I32, P, P, P, P, I64, P, P, P, P, P, U64, U32, P]
     lib.mrope_apply_ids.restype = ctypes.c_int
     lib.mrope_apply_ids_noalloc.argtypes = [P, I64, I64, I32, P, I64, I64, I32, I64, I32, I32, I32, F64, P, P,
-                                            P, P, I32, I32, I32, P, P, P, I64, P, P, P, P, P]
+                                            P, P, I32, I32, I32, P, P, P, P, I64, P, P, P, P, P]
     lib.mrope_apply_ids_noalloc.restype = ctypes.c_int
     cache = [P, P, P, I32, I64, I64, I64, I64]  # k_cache, v_cache, slot_mapping, block_size, num_blocks, strides
     lib.mrope_apply_kv.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I64, I32, I32, I32, P, I64, F64,
                                    *cache, P]
     lib.mrope_apply_kv.restype = ctypes.c_int
     lib.mrope_apply_ids_kv.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I64, I32, I32, I32, F64,
-                                       P, P, I32, I32, I32, P, P, P, I64, P, P, P, P, P, U64, U32, *cache, P]
+                                       P, P, I32, I32, I32, P, P, P, P, I64, P, P, P, P, P, U64, U32, *cache, P]
     lib.mrope_apply_ids_kv.restype = ctypes.c_int
     lib.mrope_decode.argtypes = [P, I64, I64, I32, P, I64, I64, I32, P, I64, I64, I32, P, P, *cache,
                                  I32, I32, I32, F64, P]
@@ -235,18 +236,21 @@ def _workspace(ws, n_tokens, device):
 
 def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078, *, out=None, start=None,
            amount=None, origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67,
-           workspace: Workspace | None = None):
+           frame_len_seq=None, workspace: Workspace | None = None):
     """Canvas planes from token ids.  Returns (planes [3, L] int32, start [n], amount [n], origin [n],
     seq_flags [n]).  cu_seqlens[-1] must equal len(ids).  For a later piece of each sequence (chunked
     prefill, a second turn) pass pos_offset (position of the piece's first token) and origin_in (the
     previous piece's origin output).  frame_len: tokens from <image> to start (67: this template's
-    frame; 66 + k for k marker tokens after </image>; 65: Qwen-VL's rule)."""
-    dev = _require_cuda(ids, cu_seqlens, out, start, amount, origin, seq_flags, pos_offset, origin_in)
+    frame; 66 + k for k marker tokens after </image>; 65: Qwen-VL's rule); frame_len_seq (int32 [n],
+    optional): each sequence's own frame length, 0 = frame_len (an entry outside [65, 4096] also takes
+    frame_len and sets seq_flags bit 4)."""
+    dev = _require_cuda(ids, cu_seqlens, out, start, amount, origin, seq_flags, pos_offset, origin_in,
+                        frame_len_seq)
     _i32_vec(ids, "ids")
     _i32_vec(cu_seqlens, "cu_seqlens")
     L = ids.numel()
     n = cu_seqlens.numel() - 1
-    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in")):
+    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in"), (frame_len_seq, "frame_len_seq")):
         if t is not None:
             _i32_vec(t, name, n)
     if out is None:
@@ -258,7 +262,8 @@ def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078,
                                         mk(seq_flags, "seq_flags"))
     ws = _workspace(workspace, L, dev)
     with _on_device(dev):
-        _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), int(frame_len), _ptr(pos_offset),
+        _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), int(frame_len),
+                                   _ptr(frame_len_seq), _ptr(pos_offset),
                                    _ptr(origin_in), _ptr(out), out.stride(0),
                                    _ptr(start), _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr,
                                    ws.capacity, ws.next_epoch(), _stream(dev)))
@@ -302,18 +307,20 @@ def apply(q: torch.Tensor, k: torch.Tensor | None, planes_: torch.Tensor, theta:
 
 def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seqlens: torch.Tensor,
               marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
-              origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67, q_out=None,
-              k_out=None, workspace: Workspace | None = None, rot_dim: int = ROT_DIM):
+              origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67,
+              frame_len_seq=None, q_out=None, k_out=None, workspace: Workspace | None = None,
+              rot_dim: int = ROT_DIM):
     """Plane derivation fused with the rotation, one launch.  Returns (start, amount, origin,
-    seq_flags, planes_out or None).  pos_offset / origin_in / frame_len as in planes()."""
+    seq_flags, planes_out or None).  pos_offset / origin_in / frame_len / frame_len_seq as in
+    planes()."""
     dev = _require_cuda(q, k, ids, cu_seqlens, planes_out, start, amount, origin, seq_flags, q_out, k_out,
-                        pos_offset, origin_in)
+                        pos_offset, origin_in, frame_len_seq)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, q_out, k_out)
     _i32_vec(ids, "ids", q.shape[0])
     _i32_vec(cu_seqlens, "cu_seqlens")
     T = q.shape[0]
     n = cu_seqlens.numel() - 1
-    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in")):
+    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in"), (frame_len_seq, "frame_len_seq")):
         if t is not None:
             _i32_vec(t, name, n)
     ps = 0
@@ -329,7 +336,8 @@ def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seq
     with _on_device(dev):
         _check(load().mrope_apply_ids(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, float(theta),
                                       _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
-                                      int(frame_len), _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
+                                      int(frame_len), _ptr(frame_len_seq), _ptr(pos_offset), _ptr(origin_in),
+                                      _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
                                       _ptr(seq_flags), ws.ptr, ws.capacity, ws.next_epoch(), _stream(dev)))
     return start, amount, origin, seq_flags, planes_out
 
@@ -339,19 +347,19 @@ NOALLOC_MAX_TOKENS = 1 << 20
 
 def apply_ids_noalloc(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seqlens: torch.Tensor,
                       marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
-                      origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67, q_out=None,
-                      k_out=None, rot_dim: int = ROT_DIM):
+                      origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67,
+                      frame_len_seq=None, q_out=None, k_out=None, rot_dim: int = ROT_DIM):
     """apply_ids without a workspace: the library's static per-GPU scratch stands in for it (at most
     NOALLOC_MAX_TOKENS tokens).  Pass every output (start, amount, origin, seq_flags) to allocate
     nothing here either.  The first call on a device must not be captured in a graph."""
     dev = _require_cuda(q, k, ids, cu_seqlens, planes_out, start, amount, origin, seq_flags, q_out, k_out,
-                        pos_offset, origin_in)
+                        pos_offset, origin_in, frame_len_seq)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, q_out, k_out)
     _i32_vec(ids, "ids", q.shape[0])
     _i32_vec(cu_seqlens, "cu_seqlens")
     T = q.shape[0]
     n = cu_seqlens.numel() - 1
-    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in")):
+    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in"), (frame_len_seq, "frame_len_seq")):
         if t is not None:
             _i32_vec(t, name, n)
     ps = 0
@@ -366,7 +374,8 @@ def apply_ids_noalloc(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor
     with _on_device(dev):
         _check(load().mrope_apply_ids_noalloc(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt,
                                               float(theta), _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n,
-                                              int(marker_id), int(frame_len), _ptr(pos_offset), _ptr(origin_in),
+                                              int(marker_id), int(frame_len), _ptr(frame_len_seq),
+                                              _ptr(pos_offset), _ptr(origin_in),
                                               _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
                                               _ptr(seq_flags), _stream(dev)))
     return start, amount, origin, seq_flags, planes_out
@@ -420,18 +429,18 @@ def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: 
                  k_cache: torch.Tensor, v_cache: torch.Tensor | None, slot_mapping: torch.Tensor,
                  marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
                  origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67,
-                 workspace: Workspace | None = None, rot_dim: int = ROT_DIM):
+                 frame_len_seq=None, workspace: Workspace | None = None, rot_dim: int = ROT_DIM):
     """apply_ids with the cache write of apply_kv, in one launch: ids -> planes -> q rotated in
     place, k rotated into k_cache, v copied into v_cache.  Returns (start, amount, origin,
     seq_flags, planes_out or None)."""
     dev = _require_cuda(q, k, v, ids, cu_seqlens, k_cache, v_cache, slot_mapping, planes_out, start, amount, origin,
-                        seq_flags, pos_offset, origin_in)
+                        seq_flags, pos_offset, origin_in, frame_len_seq)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, None, None)
     _i32_vec(ids, "ids", q.shape[0])
     _i32_vec(cu_seqlens, "cu_seqlens")
     T = q.shape[0]
     n = cu_seqlens.numel() - 1
-    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in")):
+    for t, name in ((pos_offset, "pos_offset"), (origin_in, "origin_in"), (frame_len_seq, "frame_len_seq")):
         if t is not None:
             _i32_vec(t, name, n)
     ps = 0
@@ -448,7 +457,8 @@ def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: 
     with _on_device(dev):
         _check(load().mrope_apply_ids_kv(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
                                          float(theta), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
-                                         int(frame_len), _ptr(pos_offset), _ptr(origin_in), _ptr(planes_out), ps, _ptr(start),
+                                         int(frame_len), _ptr(frame_len_seq), _ptr(pos_offset), _ptr(origin_in),
+                                         _ptr(planes_out), ps, _ptr(start),
                                          _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr, ws.capacity,
                                          ws.next_epoch(), *cache, _stream(dev)))
     return start, amount, origin, seq_flags, planes_out

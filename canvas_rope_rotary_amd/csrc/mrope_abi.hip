@@ -131,9 +131,9 @@ mrope_status check_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, i
 }
 
 Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_tokens, int32_t marker,
-               int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes,
-               int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin, int32_t *flags, void *ws,
-               uint32_t epoch)
+               int32_t frame_len, const int32_t *frame_len_seq, const int32_t *pos_offset,
+               const int32_t *origin_in, int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount,
+               int32_t *origin, int32_t *flags, void *ws, uint32_t epoch)
 {
     Scan s;
     s.ids = ids;
@@ -150,6 +150,7 @@ Scan make_scan(const int32_t *ids, const int32_t *cu, int32_t n_seqs, int64_t n_
     s.pos_offset = pos_offset;
     s.origin_in = origin_in;
     s.frame_len = frame_len == 0 ? kDefaultFrameLen : frame_len;
+    s.frame_lens = frame_len_seq;
     s.workspace = ws;
     const WsLayout lay = ws_layout(n_tokens);
     s.parts = ws ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + lay.parts) : nullptr;
@@ -291,14 +292,14 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream)
 }
 
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
-                          int32_t marker_id, int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
-                          int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
+                          int32_t marker_id, int32_t frame_len, const int32_t *frame_len_seq,
+                          const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
                           int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch, void *stream)
 {
     mrope_status st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes, plane_stride, workspace, workspace_bytes, true);
     if (st != MROPE_OK) return st;
     if ((st = check_frame_len(frame_len)) != MROPE_OK) return st;
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, pos_offset, origin_in, planes,
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, frame_len_seq, pos_offset, origin_in, planes,
                               plane_stride, start, amount, origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
@@ -363,7 +364,8 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
                              int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *q_out, void *k_out,
                              const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
-                             int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
+                             int32_t frame_len, const int32_t *frame_len_seq, const int32_t *pos_offset,
+                             const int32_t *origin_in,
                              int32_t *planes_out, int64_t plane_stride, int32_t *start, int32_t *amount,
                              int32_t *origin, int32_t *seq_flags, void *workspace, size_t workspace_bytes,
                              uint32_t epoch, void *stream)
@@ -375,7 +377,7 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
     st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes_out, plane_stride, workspace, workspace_bytes, false);
     if (st != MROPE_OK) return st;
     if ((st = check_frame_len(frame_len)) != MROPE_OK) return st;
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, pos_offset, origin_in,
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, frame_len_seq, pos_offset, origin_in,
                               planes_out, plane_stride, start, amount, origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
@@ -392,8 +394,8 @@ mrope_status mrope_apply_ids_noalloc(void *q, int64_t q_tok_stride, int64_t q_he
                                      void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads,
                                      int64_t n_tokens, int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta,
                                      void *q_out, void *k_out, const int32_t *ids, const int32_t *cu_seqlens,
-                                     int32_t n_seqs, int32_t marker_id, int32_t frame_len, const int32_t *pos_offset,
-                                     const int32_t *origin_in, int32_t *planes_out, int64_t plane_stride,
+                                     int32_t n_seqs, int32_t marker_id, int32_t frame_len,
+                                     const int32_t *frame_len_seq, const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out, int64_t plane_stride,
                                      int32_t *start, int32_t *amount, int32_t *origin, int32_t *seq_flags,
                                      void *stream)
 {
@@ -416,7 +418,7 @@ mrope_status mrope_apply_ids_noalloc(void *q, int64_t q_tok_stride, int64_t q_he
     void *ws = nullptr;
     if ((st = scratch_for_current_device(s, &ws)) != MROPE_OK) return st;
     // epoch 0: the device counter in the scratch tags each call (graph replays stay distinct)
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, pos_offset, origin_in,
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, frame_len_seq, pos_offset, origin_in,
                               planes_out, plane_stride, start, amount, origin, seq_flags, ws, 0);
     if (n_tokens == 0) {
         if (n_seqs > 0 && any_scalar(sc)) return hip_status(launch_text_scalars(sc, s), "mrope_apply_ids_noalloc");
@@ -432,7 +434,7 @@ mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_st
                                 const void *v, int64_t v_tok_stride, int64_t v_head_stride, int64_t n_tokens,
                                 int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, const int32_t *ids,
                                 const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id, int32_t frame_len,
-                                const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
+                                const int32_t *frame_len_seq, const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
                                 int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
                                 int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
                                 void *k_cache, void *v_cache, const int64_t *slot_mapping, int32_t block_size,
@@ -449,7 +451,7 @@ mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_st
     st = check_scan(ids, cu_seqlens, n_seqs, n_tokens, planes_out, plane_stride, workspace, workspace_bytes, false);
     if (st != MROPE_OK) return st;
     if ((st = check_frame_len(frame_len)) != MROPE_OK) return st;
-    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, pos_offset, origin_in,
+    const Scan sc = make_scan(ids, cu_seqlens, n_seqs, n_tokens, marker_id, frame_len, frame_len_seq, pos_offset, origin_in,
                               planes_out, plane_stride, start, amount, origin, seq_flags, workspace, epoch);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();

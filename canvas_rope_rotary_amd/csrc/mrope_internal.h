@@ -16,7 +16,7 @@ constexpr size_t kWsHeaderBytes = 256;  // device epoch counter (+ padding)
 // Workspace of the plane-deriving calls (byte offsets; every region 256-byte aligned):
 //   header   the device epoch counter
 //   status   one 64-bit look-back word per 512-token chunk
-//   parts    two 64-bit words per 32-token part: the planes handover of the scan-first fused kernel
+//   parts    three 64-bit words per 32-token part: the planes handover of the scan-first fused kernel
 //   tagged   three 64-bit words per token: planes of parts that hold more than one sequence
 struct WsLayout {
     size_t status, parts, tagged, total;
@@ -32,7 +32,7 @@ constexpr WsLayout ws_layout(int64_t n_tokens)
     WsLayout w{};
     w.status = kWsHeaderBytes;
     w.parts = w.status + ws_round(chunks * 8);
-    w.tagged = w.parts + ws_round(parts * 16);
+    w.tagged = w.parts + ws_round(parts * 24);
     w.total = w.tagged + ws_round((size_t)n_tokens * 24);
     return w;
 }
@@ -72,6 +72,7 @@ struct Scan {
     const int32_t *pos_offset;  // nullable: position of each sequence's first token here (0)
     const int32_t *origin_in;   // nullable: origin found in earlier pieces, -1 = none
     int32_t frame_len;          // tokens from <image> to start (65 .. kMaxFrameLen)
+    const int32_t *frame_lens;  // nullable: per-sequence frame length (0 or out of range: frame_len)
     void *workspace;
     uint64_t *parts;     // workspace regions (see WsLayout); set by the host from n_tokens
     uint64_t *tagged;

@@ -311,13 +311,24 @@ __device__ void lookback(const Scan &sc, const uint64_t *status, int64_t chunk, 
     }
 }
 
-__device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t origin, bool multi, int64_t len)
+// Frame length of sequence s (s < n_seqs): its own entry when the call gives one that describes a
+// frame (65 .. kMaxFrameLen), else the call's; bad = the entry was neither 0 nor in that range.
+__device__ __forceinline__ int32_t seq_frame_len(const Scan &sc, int32_t s, bool &bad)
+{
+    const int32_t f = sc.frame_lens ? sc.frame_lens[s] : 0;
+    bad = f != 0 && (f < 65 || f > kMaxFrameLen);
+    return (f == 0 || bad) ? sc.frame_len : f;
+}
+
+__device__ __forceinline__ void write_scalars(const Scan &sc, int32_t s, int32_t origin, bool multi, int64_t len,
+                                              int32_t fl, bool bad_fl)
 {
     const bool img = origin >= 0;
-    if (sc.start) sc.start[s] = img ? origin + sc.frame_len : kTextStart;
-    if (sc.amount) sc.amount[s] = img ? sc.frame_len - kExtent : 0;
+    if (sc.start) sc.start[s] = img ? origin + fl : kTextStart;
+    if (sc.amount) sc.amount[s] = img ? fl - kExtent : 0;
     if (sc.origin) sc.origin[s] = img ? origin : -1;
-    if (sc.flags) sc.flags[s] = (multi ? 1 : 0) | ((img && (int64_t)origin + sc.frame_len > len) ? 2 : 0);
+    if (sc.flags)
+        sc.flags[s] = (multi ? 1 : 0) | ((img && (int64_t)origin + fl > len) ? 2 : 0) | (bad_fl ? 4 : 0);
 }
 
 // Scan of one chunk by one full wave.  Publishes the chunk's status word, looks back when the
@@ -333,20 +344,21 @@ struct NoHook {
 };
 
 // The sequence a token belongs to, as the scan hands it to a sink: the sequence's first token
-// (global index), the position of that token in the whole sequence (pos_offset), and the sequence's
-// canvas origin in positions (kNone when it has no marker so far).  Position of token g:
-// off + (g - begin).
+// (global index), the position of that token in the whole sequence (pos_offset), the sequence's
+// canvas origin in positions (kNone when it has no marker so far) and its frame length.  Position
+// of token g: off + (g - begin).
 struct SeqInfo {
     int64_t begin;
     int32_t off;
     int32_t org;
+    int32_t fl;
 };
 struct NoSingle {
-    __device__ bool operator()(int64_t, int32_t, int32_t) const { return false; }
+    __device__ bool operator()(int64_t, int32_t, int32_t, int32_t) const { return false; }
 };
 
 // after_issue() runs once the chunk's id and sequence-start loads are in flight, before any wait.
-// single(seq_begin, pos_offset, origin) is offered a chunk that lies in one sequence; returning true
+// single(seq_begin, pos_offset, origin, frame_len) is offered a chunk that lies in one sequence; returning true
 // takes the chunk's planes over in that form (every token of the chunk is handed over), and sink is
 // then not called.
 template <class Sink, class Hook = NoHook, class Single = NoSingle>
@@ -424,6 +436,8 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
         // the sequence's origin in its own positions: carried from an earlier piece, else found here
         const int32_t poff = (j < n && sc.pos_offset) ? sc.pos_offset[j] : 0;
         const int32_t oin = (j < n && sc.origin_in) ? sc.origin_in[j] : -1;
+        bool bad_fl = false;
+        const int32_t fl = j < n ? seq_frame_len(sc, j, bad_fl) : sc.frame_len;
         int32_t oseq = f == kNone ? kNone : poff + (int32_t)(f - W);
         if (oin >= 0) {
             mm = mm || f != kNone;
@@ -431,23 +445,23 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
         }
         if (j < n) {
             const int64_t fin = max<int64_t>(Wn - 1, 0);
-            if (owner && fin >= c0 && fin < c_end) write_scalars(sc, j, oseq == kNone ? -1 : oseq, mm, poff + (Wn - W));
+            if (owner && fin >= c0 && fin < c_end) write_scalars(sc, j, oseq == kNone ? -1 : oseq, mm, poff + (Wn - W), fl, bad_fl);
         }
         const int64_t w_lo = __shfl(W, 0), w_hi = __shfl(Wn, 63);
         if (s_first == s_last && s_first >= win && s_first - win < 64) {
             // the whole chunk lies in one sequence: no per-token search
             const int r = s_first - win;
-            const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r);
+            const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r), flr = __shfl(fl, r);
             const int64_t sb = __shfl(W, r);
-            if (!single(sb, offr, orr)) {
+            if (!single(sb, offr, orr, flr)) {
 #pragma unroll
                 for (int k = 0; k < kSub; ++k) {
                     const int64_t g = c0 + 64 * k + lane;
                     const bool ok = g < c_end;
                     const int32_t p = offr + (int32_t)(g - sb);
                     int32_t t = 0, h = 0, w = 0;
-                    if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, sc.frame_len, t, h, w);
-                    sink(k, ok, t, h, w, SeqInfo{sb, offr, orr});
+                    if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, flr, t, h, w);
+                    sink(k, ok, t, h, w, SeqInfo{sb, offr, orr, flr});
                 }
             }
         } else {
@@ -458,13 +472,13 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
 #pragma unroll
                 for (int step = 32; step > 0; step >>= 1)
                     if (__shfl(Wn, r + step - 1) <= g) r += step;
-                const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r);
+                const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r), flr = __shfl(fl, r);
                 const int64_t sb = __shfl(W, r);
                 const bool ok = g < c_end && g >= w_lo && g < w_hi;
                 const int32_t p = offr + (int32_t)(g - sb);
                 int32_t t = 0, h = 0, w = 0;
-                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, sc.frame_len, t, h, w);
-                sink(k, ok, t, h, w, SeqInfo{sb, offr, orr});
+                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, flr, t, h, w);
+                sink(k, ok, t, h, w, SeqInfo{sb, offr, orr, flr});
             }
         }
         if (win + 64 >= n || (int64_t)sc.cu[win + 64] > c_end) break;
@@ -1045,18 +1059,20 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
                });
 }
 
-// Fused: one part of a 512-token chunk per workgroup (2^part_log parts: halves for large inputs,
-// down to 32-token parts for small ones; each workgroup repeats the chunk's scan, so more
-// workgroups share the work and each has fewer sequential steps).  Every lane issues the Q/K loads of its first token, wave 0 scans the chunk into
-// LDS meanwhile, then the workgroup rotates its part 32 tokens at a time, each 8-lane group
-// prefetching its next token before rotating the current one.  KV as in apply_kernel (fixed head
+// Fused: one part of a 512-token chunk per workgroup (2^part_log parts, part_log >= 1: halves for
+// large inputs, down to 32-token parts for small ones; each workgroup repeats the chunk's scan, so
+// more workgroups share the work and each has fewer sequential steps).  Wave 0 scans the chunk into
+// LDS while waves 1-3 issue the Q/K loads of their first token (wave 0 issues its own after the
+// scan), then the workgroup rotates its part 32 tokens at a time, each 8-lane group prefetching its
+// next token before rotating the current one.  KV as in apply_kernel (fixed head
 // counts); the generic path writes the cache when pc.k_cache is set.
 template <int IO, int NQ, int NK, bool KV, bool NTS>
 __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, PagedKV pc, int part_log)
 {
     __shared__ int32_t s_pl[3][kChunk];
     __shared__ uint64_t s_ok[kSub];
-    __shared__ int64_t s_seq[2];  // a chunk inside one sequence: [1] = its begin; [0] = its offset | origin << 32
+    __shared__ int64_t s_seq[3];  // a chunk inside one sequence: [1] = its begin; [0] = its offset | origin << 32;
+                                  // [2] = its frame length
     __shared__ int32_t s_single;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1080,7 +1096,6 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     // include those loads (1 x 4096 tokens 17.8 -> 17.2 us, 4 x 4096 28.4 -> 25.7).  Issued early,
     // 8 x 32768 tokens took 122 us instead of 118: with long sequences a chunk's look-back waits on
     // its predecessors' look-backs, and each waited behind its wave 0's loads.
-    const bool w0_late = part_log > 0;
     int64_t g = r0 + (tid >> 3);
     Raw8<IO> qv[AQ], kv[AK];
     auto prologue = [&]() {
@@ -1114,20 +1129,18 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
                            sc.planes[2 * sc.plane_stride + gg] = w;
                        }
                    },
-                   [&]() {
-                       __builtin_amdgcn_s_barrier();
-                       if (!w0_late) prologue();
-                   },
-                   [&](int64_t sb, int32_t off, int32_t org) {
+                   [&]() { __builtin_amdgcn_s_barrier(); },
+                   [&](int64_t sb, int32_t off, int32_t org, int32_t fl) {
                        if (sc.planes) return false;
                        if (lane == 0) {
                            s_seq[1] = sb;
                            s_seq[0] = (int64_t)(uint32_t)off | ((int64_t)org << 32);
+                           s_seq[2] = fl;
                            s_single = 1;
                        }
                        return true;
                    });
-        if (w0_late) prologue();
+        prologue();
     }
     __syncthreads();
     wait_vm_all();  // the first token's loads: see apply_kernel
@@ -1139,12 +1152,13 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     const int64_t seq_begin = single ? s_seq[1] : 0;
     const int64_t seq_word = single ? s_seq[0] : 0;
     const int32_t seq_off = (int32_t)(uint32_t)seq_word, seq_org = (int32_t)(seq_word >> 32);
+    const int32_t seq_fl = single ? (int32_t)s_seq[2] : sc.frame_len;
     const int64_t p_c0 = single ? seq_off + (c0 - seq_begin) : 0;  // position of the chunk's first token
     const int64_t p_last = p_c0 + (c_end - 1 - c0);
     const bool before = seq_org == kNone || p_last < seq_org;
-    const bool after = !before && p_c0 - seq_org >= sc.frame_len;
+    const bool after = !before && p_c0 - seq_org >= seq_fl;
     const bool flat = single && (before || after);
-    const int32_t flat_c0 = (int32_t)(p_c0 - (after ? sc.frame_len - kExtent : 0));
+    const int32_t flat_c0 = (int32_t)(p_c0 - (after ? seq_fl - kExtent : 0));
     auto planes_of = [&](int64_t gt, bool &ok, int32_t &t, int32_t &h, int32_t &w) {
         if (flat) {
             ok = true;
@@ -1152,7 +1166,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         } else if (single) {
             const int32_t pp = seq_off + (int32_t)(gt - seq_begin);
             ok = true;
-            canvas_planes(pp, (seq_org != kNone && seq_org <= pp) ? seq_org : kNone, sc.frame_len, t, h, w);
+            canvas_planes(pp, (seq_org != kNone && seq_org <= pp) ? seq_org : kNone, seq_fl, t, h, w);
         } else {
             const int p = (int)(gt - c0);
             ok = (s_ok[p >> 6] >> (p & 63)) & 1u;
@@ -1197,8 +1211,9 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
 //   scan workgroups [0, S): one wave per 512-token chunk runs the chunk scan (ballots, look-back,
 //     scalars, planes_out) and hands the planes of each 32-token part of the chunk over through the
 //     workspace -- a part inside one sequence as two words (the position base, p = g + base, and the
-//     sequence's canvas origin), any other part as its tokens' planes, three words a token -- every
-//     word tagged with the launch's epoch;
+//     sequence's canvas origin; a third, its frame length, when the call gives frame lengths per
+//     sequence), any other part as its tokens' planes, three words a token -- every word tagged with
+//     the launch's epoch;
 //   rotation workgroups [S, S + R): one 32-token part each, shaped like mrope_apply's one-step
 //     workgroups: every lane issues its token's Q/K loads, then reads the part's handover words,
 //     derives its token's planes, rotates and stores.
@@ -1236,7 +1251,7 @@ __device__ void sf_scan_chunk(const Scan &sc, int64_t chunk, uint32_t ep, int la
             // one (a part whose tokens come in several calls is written so by each).
             const int leader = lane & 32;
             const int64_t lb = __shfl(si.begin, leader);
-            const int32_t lo = __shfl(si.off, leader), lg = __shfl(si.org, leader);
+            const int32_t lo = __shfl(si.off, leader), lg = __shfl(si.org, leader), lf = __shfl(si.fl, leader);
             const bool valid = g < c_end;
             const bool same = !valid || (ok && si.begin == lb && si.off == lo && si.org == lg);
             const uint64_t half = leader ? 0xffffffff00000000ull : 0x00000000ffffffffull;
@@ -1245,8 +1260,9 @@ __device__ void sf_scan_chunk(const Scan &sc, int64_t chunk, uint32_t ep, int la
             const int64_t part = (c0 + 64 * k + leader) / kPartTokens;
             if (single) {
                 if (lane == leader) {
-                    astore(sc.parts + 2 * part, tag_word(ep, kPartSingle, (uint32_t)(int32_t)((int64_t)lo - lb)));
-                    astore(sc.parts + 2 * part + 1, tag_word(ep, 0, (uint32_t)lg));
+                    astore(sc.parts + 3 * part, tag_word(ep, kPartSingle, (uint32_t)(int32_t)((int64_t)lo - lb)));
+                    astore(sc.parts + 3 * part + 1, tag_word(ep, 0, (uint32_t)lg));
+                    if (sc.frame_lens) astore(sc.parts + 3 * part + 2, tag_word(ep, 0, (uint32_t)lf));
                 }
             } else {
                 if (ok) {
@@ -1255,18 +1271,21 @@ __device__ void sf_scan_chunk(const Scan &sc, int64_t chunk, uint32_t ep, int la
                     astore(sc.tagged + 3 * g + 2, tag_word(ep, 0, (uint32_t)w));
                 }
                 if (lane == leader) {
-                    astore(sc.parts + 2 * part, tag_word(ep, kPartMulti, 0u));
-                    astore(sc.parts + 2 * part + 1, tag_word(ep, 0, 0u));
+                    astore(sc.parts + 3 * part, tag_word(ep, kPartMulti, 0u));
+                    astore(sc.parts + 3 * part + 1, tag_word(ep, 0, 0u));
+                    if (sc.frame_lens) astore(sc.parts + 3 * part + 2, tag_word(ep, 0, 0u));
                 }
             }
         },
         NoHook(),
-        [&](int64_t sb, int32_t off, int32_t org) {
+        [&](int64_t sb, int32_t off, int32_t org, int32_t fl) {
             if (sc.planes) return false;  // planes_out is written token by token (sink)
             const int64_t p0 = c0 / kPartTokens, np = (c_end - c0 + kPartTokens - 1) / kPartTokens;
             if (lane < np) {
-                astore(sc.parts + 2 * (p0 + lane), tag_word(ep, kPartSingle, (uint32_t)(int32_t)((int64_t)off - sb)));
-                astore(sc.parts + 2 * (p0 + lane) + 1, tag_word(ep, 0, (uint32_t)org));
+                uint64_t *rec = sc.parts + 3 * (p0 + lane);
+                astore(rec, tag_word(ep, kPartSingle, (uint32_t)(int32_t)((int64_t)off - sb)));
+                astore(rec + 1, tag_word(ep, 0, (uint32_t)org));
+                if (sc.frame_lens) astore(rec + 2, tag_word(ep, 0, (uint32_t)fl));
             }
             return true;
         });
@@ -1282,19 +1301,22 @@ __device__ void sf_planes(const Scan &sc, uint32_t ep, int lane, int64_t G, int6
     bool have = false;
     pt = ph = pw = 0;
     if (wait) {
-        uint64_t w0 = 0, w1 = 0;
+        uint64_t w0 = 0, w1 = 0, w2 = 0;
         bool ready = false;
+        const bool per_seq = sc.frame_lens != nullptr;
         for (int poll = 0;; ++poll) {
-            w0 = aload(sc.parts + 2 * part);
-            w1 = aload(sc.parts + 2 * part + 1);
-            ready = tagged_with(w0, ep) && tagged_with(w1, ep);
+            w0 = aload(sc.parts + 3 * part);
+            w1 = aload(sc.parts + 3 * part + 1);
+            if (per_seq) w2 = aload(sc.parts + 3 * part + 2);
+            ready = tagged_with(w0, ep) && tagged_with(w1, ep) && (!per_seq || tagged_with(w2, ep));
             if (ready || poll == kPolls) break;
             __builtin_amdgcn_s_sleep(8);
         }
         if (ready && ((w0 >> 32) & 3u) == kPartSingle) {
             const int32_t base = (int32_t)(uint32_t)w0, org = (int32_t)(uint32_t)w1;
+            const int32_t fl = per_seq ? (int32_t)(uint32_t)w2 : sc.frame_len;
             const int32_t p = (int32_t)g + base;
-            if (ok) canvas_planes(p, (org != kNone && org <= p) ? org : kNone, sc.frame_len, pt, ph, pw);
+            if (ok) canvas_planes(p, (org != kNone && org <= p) ? org : kNone, fl, pt, ph, pw);
             have = true;
         } else if (ready) {
             for (int poll = 0;; ++poll) {
@@ -1331,9 +1353,9 @@ __device__ void sf_planes(const Scan &sc, uint32_t ep, int lane, int64_t G, int6
             }
         },
         NoHook(),
-        [&](int64_t sb, int32_t off, int32_t org) {
+        [&](int64_t sb, int32_t off, int32_t org, int32_t fl) {
             const int32_t p = off + (int32_t)(g - sb);
-            if (ok) canvas_planes(p, (org != kNone && org <= p) ? org : kNone, sc.frame_len, pt, ph, pw);
+            if (ok) canvas_planes(p, (org != kNone && org <= p) ? org : kNone, fl, pt, ph, pw);
             return true;
         });
 }
@@ -1522,7 +1544,9 @@ __global__ void text_scalars_kernel(Scan sc)
     const int32_t s = blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= sc.n_seqs) return;
     const int32_t oin = sc.origin_in ? sc.origin_in[s] : -1;
-    write_scalars(sc, s, oin >= 0 ? oin : -1, false, sc.pos_offset ? sc.pos_offset[s] : 0);
+    bool bad_fl = false;
+    const int32_t fl = seq_frame_len(sc, s, bad_fl);
+    write_scalars(sc, s, oin >= 0 ? oin : -1, false, sc.pos_offset ? sc.pos_offset[s] : 0, fl, bad_fl);
 }
 
 // Device-counter epochs: advance the counter once the scan launch before it has finished.

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MROPE_ABI_VERSION 4
+#define MROPE_ABI_VERSION 5
 
 typedef enum {
     MROPE_OK = 0,
@@ -63,6 +63,8 @@ typedef enum {
 #define MROPE_SEQ_MULTI_MARKER 1u /* more than one <image> marker; planes follow the first frame */
 #define MROPE_SEQ_FRAME_OVERRUN 2u /* the frame (frame_len tokens from the marker, 67 by default)
                                      runs past the end of the sequence */
+#define MROPE_SEQ_BAD_FRAME_LEN 4u /* the sequence's frame_len_seq entry was neither 0 nor in
+                                     [65, 4096]; the call's frame_len was used instead */
 
 /* Text-only sequences get start = 2^30 and amount = 0 (card, start/amount paragraph). */
 #define MROPE_TEXT_ONLY_START (1 << 30)
@@ -94,8 +96,8 @@ int mrope_set_test_hooks(int flags);
  * device memory, zero-filled (or passed once through mrope_workspace_init) before its first use;
  * it needs no clearing between calls.  It holds a device epoch counter and room for one 64-bit
  * status word per 512-token chunk, through which a chunk hands the first marker of a sequence to
- * the chunks after it, then the planes handover of the scan-first fused kernel (16 bytes per 32
- * tokens, and 24 bytes per token for parts that hold more than one sequence): about 24.5 bytes per
+ * the chunks after it, then the planes handover of the scan-first fused kernel (24 bytes per 32
+ * tokens, and 24 bytes per token for parts that hold more than one sequence): about 24.8 bytes per
  * token in all.
  *
  * Epochs.  The plane-deriving calls take an `epoch` that tags the status words they write, so a
@@ -125,6 +127,12 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  *            markers that follow).  0 = 67, this template's one "\n"; 66 + k for a run of k such
  *            tokens; 65 for Qwen-VL's rule ([zoo] "CoreAIKit (VLChat)": +64 and 56 from the first
  *            pad).  Allowed: 0 or 65..4096.  amount = frame_len - 9 for every length.
+ * frame_len_seq  [n_seqs] int32 (nullable = every sequence takes frame_len): the frame length of
+ *            each sequence, for a packed batch whose prompts come from templates whose frames end
+ *            differently (65, 67, 66 + k as above).  An entry of 0 takes the call's frame_len; an
+ *            entry outside [65, 4096] also takes it and sets MROPE_SEQ_BAD_FRAME_LEN in seq_flags
+ *            (the status stays MROPE_OK: the host never reads the array).  Everything below that
+ *            names frame_len means the sequence's own.
  * pos_offset [n_seqs] int32 (nullable = all 0): position of each sequence's first token in this call
  *            within the whole sequence.  A prompt may be fed in pieces -- prefill in chunks, a second
  *            turn continuing the first ([zoo] section "Prefill in chunks and a second turn") -- and
@@ -158,8 +166,8 @@ mrope_status mrope_workspace_init(void *workspace, size_t bytes, void *stream);
  * that has not published after them is evaluated from its ids), so no chunk waits without bound.
  * ------------------------------------------------------------------------------------------- */
 mrope_status mrope_planes(const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
-                          int32_t marker_id, int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
-                          int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount,
+                          int32_t marker_id, int32_t frame_len, const int32_t *frame_len_seq,
+                          const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes, int64_t plane_stride, int32_t *start, int32_t *amount,
                           int32_t *origin, int32_t *seq_flags, void *workspace, size_t workspace_bytes,
                           uint32_t epoch, void *stream);
 
@@ -207,8 +215,9 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
                              int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads, int64_t n_tokens,
                              int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta, void *q_out,
                              void *k_out, const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs,
-                             int32_t marker_id, int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
-                             int32_t *planes_out, int64_t plane_stride, int32_t *start,
+                             int32_t marker_id, int32_t frame_len, const int32_t *frame_len_seq,
+                             const int32_t *pos_offset, const int32_t *origin_in, int32_t *planes_out,
+                             int64_t plane_stride, int32_t *start,
                              int32_t *amount, int32_t *origin, int32_t *seq_flags, void *workspace,
                              size_t workspace_bytes, uint32_t epoch, void *stream);
 
@@ -218,7 +227,7 @@ mrope_status mrope_apply_ids(void *q, int64_t q_tok_stride, int64_t q_head_strid
  * Arguments, results and errors as mrope_apply_ids, without workspace, workspace_bytes and epoch.
  * The workspace is a static device array inside the library: one copy per GPU, allocated when the
  * library's code is loaded and held until the process ends (MROPE_NOALLOC_MAX_TOKENS tokens'
- * worth, about 25.7 MB).  n_tokens above MROPE_NOALLOC_MAX_TOKENS returns MROPE_ERR_WORKSPACE.
+ * worth, about 26.0 MB).  n_tokens above MROPE_NOALLOC_MAX_TOKENS returns MROPE_ERR_WORKSPACE.
  * The call allocates nothing.  Its first call on a device looks the array up and clears it with a
  * kernel on `stream`; that first call must not be captured in a graph (MROPE_ERR_ARG if it is).
  * Each later call tags its words with the device epoch counter kept in the array, so calls and
@@ -230,7 +239,8 @@ mrope_status mrope_apply_ids_noalloc(void *q, int64_t q_tok_stride, int64_t q_he
                                      void *k, int64_t k_tok_stride, int64_t k_head_stride, int32_t n_k_heads,
                                      int64_t n_tokens, int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta,
                                      void *q_out, void *k_out, const int32_t *ids, const int32_t *cu_seqlens,
-                                     int32_t n_seqs, int32_t marker_id, int32_t frame_len, const int32_t *pos_offset,
+                                     int32_t n_seqs, int32_t marker_id, int32_t frame_len,
+                                     const int32_t *frame_len_seq, const int32_t *pos_offset,
                                      const int32_t *origin_in, int32_t *planes_out, int64_t plane_stride,
                                      int32_t *start, int32_t *amount, int32_t *origin, int32_t *seq_flags,
                                      void *stream);
@@ -276,9 +286,8 @@ mrope_status mrope_apply_ids_kv(void *q, int64_t q_tok_stride, int64_t q_head_st
                                 const void *v, int64_t v_tok_stride, int64_t v_head_stride, int64_t n_tokens,
                                 int32_t head_dim, int32_t rot_dim, int32_t dtype, double theta,
                                 const int32_t *ids, const int32_t *cu_seqlens, int32_t n_seqs, int32_t marker_id,
-                                int32_t frame_len, const int32_t *pos_offset, const int32_t *origin_in,
-                                int32_t *planes_out,
-                                int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
+                                int32_t frame_len, const int32_t *frame_len_seq, const int32_t *pos_offset,
+                                const int32_t *origin_in, int32_t *planes_out, int64_t plane_stride, int32_t *start, int32_t *amount, int32_t *origin,
                                 int32_t *seq_flags, void *workspace, size_t workspace_bytes, uint32_t epoch,
                                 void *k_cache, void *v_cache, const int64_t *slot_mapping, int32_t block_size,
                                 int64_t num_blocks, int64_t cache_block_stride, int64_t cache_tok_stride,

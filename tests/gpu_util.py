@@ -99,13 +99,23 @@ def compare_heads_all(got: torch.Tensor, x_in: np.ndarray, planes: np.ndarray, d
     return info
 
 
-def expected_flags(b: synth.Prefill, origin: np.ndarray) -> np.ndarray:
-    """Data-fault bits: >1 marker in the sequence; frame (67 tokens from the marker) past the end."""
+def expected_flags(b: synth.Prefill, origin: np.ndarray, frame_len: int = synth.FRAME_TOKENS,
+                   frame_len_seq=None) -> np.ndarray:
+    """Data-fault bits of whole sequences: 1 = more than one marker in the sequence; 2 = the frame
+    (frame_len tokens from the marker, or the sequence's own frame_len_seq entry) runs past the end;
+    4 = the sequence's frame_len_seq entry is neither 0 nor in [65, 4096] (frame_len is used)."""
     out = np.zeros(b.n_seqs, np.int32)
     for s in range(b.n_seqs):
         lo, hi = b.cu_seqlens[s], b.cu_seqlens[s + 1]
+        f = frame_len
+        if frame_len_seq is not None and int(frame_len_seq[s]) != 0:
+            e = int(frame_len_seq[s])
+            if 65 <= e <= 4096:
+                f = e
+            else:
+                out[s] |= 4
         if int((b.ids[lo:hi] == MARKER).sum()) >= 2:
             out[s] |= 1
-        if origin[s] >= 0 and origin[s] + synth.FRAME_TOKENS > hi - lo:
+        if origin[s] >= 0 and origin[s] + f > hi - lo:
             out[s] |= 2
     return out

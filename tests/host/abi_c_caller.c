@@ -142,7 +142,7 @@ int main(void)
     report("workspace init", mrope_workspace_init(d_ws, ws_bytes, stream) == MROPE_OK, "");
 
     /* 1. planes + apply, fp32 */
-    int st = mrope_planes(d_ids, d_cu, n_seqs, T, MARKER, 0, NULL, NULL, d_pl, T, d_st, d_am, d_og, NULL, d_ws,
+    int st = mrope_planes(d_ids, d_cu, n_seqs, T, MARKER, 0, NULL, NULL, NULL, d_pl, T, d_st, d_am, d_og, NULL, d_ws,
                           ws_bytes, 1u, stream);
     report("mrope_planes status", st == MROPE_OK, st == MROPE_OK ? "" : mrope_last_error());
     st = mrope_apply(d_q, NQ * HD, HD, NQ, d_k, NK * HD, HD, NK, T, HD, ROT, MROPE_F32, d_pl, T, THETA, NULL,
@@ -204,11 +204,11 @@ int main(void)
     HIP_OK(hipMalloc(&d_qo, 2 * nq));
     HIP_OK(hipMalloc(&d_ko, 2 * nk));
     st = mrope_apply_ids(d_qb, NQ * HD, HD, NQ, d_kb, NK * HD, HD, NK, T, HD, ROT, MROPE_BF16, THETA, d_qo, d_ko,
-                         d_ids, d_cu, n_seqs, MARKER, 0, NULL, NULL, NULL, T, NULL, NULL, NULL, NULL, d_ws, ws_bytes,
+                         d_ids, d_cu, n_seqs, MARKER, 0, NULL, NULL, NULL, NULL, T, NULL, NULL, NULL, NULL, d_ws, ws_bytes,
                          3u, stream);
     report("mrope_apply_ids out of place status", st == MROPE_OK, st == MROPE_OK ? "" : mrope_last_error());
     st = mrope_apply_ids(d_qb, NQ * HD, HD, NQ, d_kb, NK * HD, HD, NK, T, HD, ROT, MROPE_BF16, THETA, NULL, NULL,
-                         d_ids, d_cu, n_seqs, MARKER, 0, NULL, NULL, NULL, T, d_st, d_am, d_og, NULL, d_ws, ws_bytes,
+                         d_ids, d_cu, n_seqs, MARKER, 0, NULL, NULL, NULL, NULL, T, d_st, d_am, d_og, NULL, d_ws, ws_bytes,
                          2u, stream);
     report("mrope_apply_ids status", st == MROPE_OK, st == MROPE_OK ? "" : mrope_last_error());
     HIP_OK(hipStreamSynchronize(stream));

@@ -29,19 +29,19 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.mrope_abi_version() == 4
+    assert lib.mrope_abi_version() == 5
     for code, text in ((OK, "ok"), (ARG, "invalid argument"), (HIP, "HIP runtime error")):
         assert lib.mrope_status_string(code).decode() == text
     assert lib.mrope_status_string(99).decode() == "unknown status"
 
 
 def test_workspace_bytes(lib):
-    """Header, one status word per 512-token chunk, two words per 32-token part, three words per
+    """Header, one status word per 512-token chunk, three words per 32-token part, three words per
     token; every region rounded up to 256 bytes."""
     r = lambda b: (b + 255) // 256 * 256
     for n in (0, 1, 31, 32, 64, 65, 511, 512, 513, 1 << 20, 3_000_001):
         chunks, parts = -(-n // 512), -(-n // 32)
-        assert lib.mrope_workspace_bytes(n) == 256 + r(8 * chunks) + r(16 * parts) + r(24 * n), n
+        assert lib.mrope_workspace_bytes(n) == 256 + r(8 * chunks) + r(24 * parts) + r(24 * n), n
 
 
 def test_test_hooks_round_trip(lib):
@@ -83,7 +83,7 @@ def test_apply_nothing_to_do(lib):
 def _planes(lib, **kw):
     a = dict(ids=A, cu=A, ns=4, n=1000, marker=248078, fl=0, planes=A, ps=1000, ws=A, wsb=10 ** 6)
     a.update(kw)
-    return lib.mrope_planes(a["ids"], a["cu"], a["ns"], a["n"], a["marker"], a["fl"], None, None, a["planes"], a["ps"], None,
+    return lib.mrope_planes(a["ids"], a["cu"], a["ns"], a["n"], a["marker"], a["fl"], None, None, None, a["planes"], a["ps"], None,
                             None, None, None, a["ws"], a["wsb"], 1, None)
 
 
@@ -173,7 +173,7 @@ def _apply_ids_kv(lib, **kw):
     a.update(kw)
     return lib.mrope_apply_ids_kv(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["v"],
                                   a["vt"], a["vh"], a["n"], a["hd"], a["rot"], a["dt"], a["theta"], a["ids"], a["cu"],
-                                  a["ns"], a["marker"], a["fl"], None, None, None, 0, None, None, None, None, a["ws"],
+                                  a["ns"], a["marker"], a["fl"], None, None, None, None, 0, None, None, None, None, a["ws"],
                                   a["wsb"], 1, *_cache_args(a), None)
 
 
@@ -202,7 +202,7 @@ def _apply_ids_noalloc(lib, **kw):
     a.update(kw)
     return lib.mrope_apply_ids_noalloc(a["q"], a["qt"], a["qh"], a["nq"], a["k"], a["kt"], a["kh"], a["nk"], a["n"],
                                        a["hd"], a["rot"], a["dt"], a["theta"], None, None, a["ids"], a["cu"], a["ns"],
-                                       a["marker"], a["fl"], None, None, a["planes"], a["ps"], None, None, None, None,
+                                       a["marker"], a["fl"], None, None, None, a["planes"], a["ps"], None, None, None, None,
                                        None)
 
 

@@ -667,7 +667,7 @@ def test_device_epoch_mode_through_c_abi():
         st, am, og, fl = (torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(4))
         p = lambda t: ctypes.c_void_p(t.data_ptr())
         ws.ensure(L)
-        rc = lib.mrope_planes(p(ids), p(cu), n, L, MARKER, 0, None, None, p(pl), L, p(st), p(am), p(og), p(fl), ws.ptr,
+        rc = lib.mrope_planes(p(ids), p(cu), n, L, MARKER, 0, None, None, None, p(pl), L, p(st), p(am), p(og), p(fl), ws.ptr,
                               ws.capacity, 0, stream)
         assert rc == 0
         _check_scan(b, pl, st, am, og, fl, f"device epoch call {i}")
