@@ -117,6 +117,13 @@ __device__ __forceinline__ uint32_t launch_epoch(const Scan &sc)
 }
 
 // ------------------------------------------------------------------ wave helpers ---------------
+// v's value in lane r (r wave-uniform): two scalar reads, no LDS permute.
+__device__ __forceinline__ int64_t lane_value(int64_t v, int r)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)v, r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)((uint64_t)v >> 32), r);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ int32_t wave_min(int32_t v)
 {
 #pragma unroll
@@ -177,6 +184,27 @@ __device__ void wave_count_le2(const int32_t *cu, int32_t n, int64_t ka, int64_t
     cb = res[1];
 }
 
+// A lower bound lo on the number of entries of the non-decreasing array cu[0..n] that are <= key,
+// within 63 of it: the 128-ary search above for one key, stopped once the candidates fit one
+// 64-entry window (one level up to 8,063 sequences).  A window of cu loaded from lo - 1 then holds
+// the exact count's last entry.
+__device__ int32_t wave_bracket_le(const int32_t *cu, int32_t n, int64_t key, int lane)
+{
+    int32_t lo = 0, hi = n + 1;
+    while (hi - lo > 63) {
+        const int32_t stride = (hi - lo + 127) / 128;
+        const int32_t p0 = lo + (2 * lane) * stride, p1 = p0 + stride;
+        const int32_t x0 = cu[min(p0, n)], x1 = cu[min(p1, n)];
+        const int c = __builtin_popcountll(__ballot(p0 < hi && (int64_t)x0 <= key)) +
+                      __builtin_popcountll(__ballot(p1 < hi && (int64_t)x1 <= key));
+        if (c == 0) return lo;
+        const int32_t nhi = min(hi, lo + c * stride);
+        lo = lo + (c - 1) * stride + 1;
+        hi = nhi;
+    }
+    return lo;
+}
+
 // Bits [lo, hi) of a 64-bit word, for any lo, hi (clamped to [0, 64]).
 __device__ __forceinline__ uint64_t bit_range(int lo, int hi)
 {
@@ -196,6 +224,7 @@ __device__ __forceinline__ uint64_t bit_range(int lo, int hi)
 // in an earlier chunk comes from the decoupled look-back below.
 constexpr int kChunk = 512;
 constexpr int kSub = kChunk / 64;
+constexpr int kWalkSeqs = 8;  // a chunk touched by up to this many sequences of a window walks them
 
 struct ChunkMasks {
     uint64_t m[kSub];  // bit i of m[k]: token c0 + 64k + i is a marker
@@ -369,35 +398,53 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
     const int64_t c_end = min<int64_t>(c0 + kChunk, sc.n_tokens);
     const int32_t n = sc.n_seqs;
 
+    // A window of 64 sequences: lane l holds sequence win + l -- its begin W and end Wn (INT64_MAX
+    // past the last sequence), position offset, carried origin and frame-length entry, all loaded in
+    // one round trip.
+    int32_t win;
+    int64_t W, Wn;
+    int32_t w_off, w_oin, w_fl;
+    auto load_window = [&](int32_t at) {
+        const int32_t j = at + lane;
+        const int32_t w0 = sc.cu[min(j, n)], w1 = sc.cu[min(j + 1, n)];
+        const int32_t js = min(j, max(n - 1, 0));
+        w_off = sc.pos_offset ? sc.pos_offset[js] : 0;
+        w_oin = sc.origin_in ? sc.origin_in[js] : -1;
+        w_fl = sc.frame_lens ? sc.frame_lens[js] : 0;
+        W = j <= n ? (int64_t)w0 : INT64_MAX;
+        Wn = j < n ? (int64_t)w1 : INT64_MAX;
+    };
+
     // id loads and the sequence search go out together
     int32_t idv[kSub];
     issue_ids(sc, c0, c_end, c0, lane, idv);
-    int32_t cnt_first, cnt_last, win;
-    int64_t W, Wn;
     if (n < 64) {
-        // every sequence start fits one window: it is loaded with the ids, and the chunk's first and
-        // last sequences are counted by ballot -- one round trip instead of a search, then a window
+        // every sequence fits one window: it is loaded with the ids, and the chunk's first and last
+        // sequences are counted by ballot -- one round trip instead of a search, then a window
         win = 0;
-        const int32_t w0 = sc.cu[min(lane, n)], w1 = sc.cu[min(lane + 1, n)];
+        load_window(0);
         after_issue();
-        W = lane <= n ? (int64_t)w0 : INT64_MAX;
-        Wn = lane < n ? (int64_t)w1 : INT64_MAX;
-        cnt_first = __builtin_popcountll(__ballot(W <= c0));
-        cnt_last = __builtin_popcountll(__ballot(W <= c_end - 1));
     } else {
         after_issue();
-        wave_count_le2(sc.cu, n, c0, c_end - 1, lane, cnt_first, cnt_last);
-        // first window of 64 sequences (chunk 0 starts at sequence 0 so leading empty sequences
-        // get their scalars); it also holds the starts of the chunk's first and, usually, last
-        // sequence
-        win = c0 == 0 ? 0 : max(cnt_first - 1, 0);
-        const int32_t j = win + lane;
-        const int32_t w0 = sc.cu[min(j, n)], w1 = sc.cu[min(j + 1, n)];
-        W = j <= n ? (int64_t)w0 : INT64_MAX;
-        Wn = j < n ? (int64_t)w1 : INT64_MAX;
+        // the window starts just below the chunk's first sequence (chunk 0: at sequence 0, so
+        // leading empty sequences get their scalars)
+        win = c0 == 0 ? 0 : max(wave_bracket_le(sc.cu, n, c0, lane) - 1, 0);
+        load_window(win);
     }
+    // Every entry below the window is <= c0, so a ballot over the window counts the sequences that
+    // begin at or before c0 and c_end - 1 -- unless the window's last entry is still <= c_end - 1:
+    // then more than 64 sequences touch the chunk and an exact search counts them.
+    int32_t cnt_first = win + __builtin_popcountll(__ballot(W <= c0));
+    int32_t cnt_last = win + __builtin_popcountll(__ballot(W <= c_end - 1));
+    if (__shfl(W, 63) <= c_end - 1) wave_count_le2(sc.cu, n, c0, c_end - 1, lane, cnt_first, cnt_last);
     ChunkMasks cm;
     ballot_ids(sc, idv, cm);
+    // Most chunks hold no marker at all (one per image sequence): they skip the bit searches, whose
+    // 64-bit VALU arithmetic is a sizeable part of a wave's instructions.
+    uint64_t any_marker = 0;
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) any_marker |= cm.m[k];
+    const bool has_marker = __builtin_amdgcn_readfirstlane((uint32_t)(any_marker != 0)) != 0;
     const int32_t s_first = cnt_first - 1, s_last = cnt_last - 1;
     const bool first_ok = s_first >= 0 && s_first < n;
     int64_t s0_begin = c0;
@@ -409,9 +456,9 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
     const bool last_open = need_carry && s_last == s_first;
 
     // the chunk's last sequence: its part in this chunk, published before the look-back
-    int32_t f_last;
-    bool m_last;
-    first_in(cm, c0, (int)(max(sl_begin, c0) - c0), (int)(c_end - c0), f_last, m_last);
+    int32_t f_last = kNone;
+    bool m_last = false;
+    if (has_marker) first_in(cm, c0, (int)(max(sl_begin, c0) - c0), (int)(c_end - c0), f_last, m_last);
     if (owner && lane == 0) astore(status + chunk, status_word(ep, last_open ? kAgg : kIncl, m_last, last_ok ? f_last : kNone));
 
     int32_t carry = kNone;
@@ -426,18 +473,18 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
 
     while (true) {
         const int32_t j = win + lane;
-        int32_t f;
-        bool mm;
-        first_in(cm, c0, (int)(max(min(W, c_end), c0) - c0), (int)(max(min(Wn, c_end), c0) - c0), f, mm);
+        int32_t f = kNone;
+        bool mm = false;
+        if (has_marker) first_in(cm, c0, (int)(max(min(W, c_end), c0) - c0), (int)(max(min(Wn, c_end), c0) - c0), f, mm);
         if (need_carry && j == s_first) {
             mm = mm || carry_multi || (carry != kNone && f != kNone);
             f = min(f, carry);
         }
         // the sequence's origin in its own positions: carried from an earlier piece, else found here
-        const int32_t poff = (j < n && sc.pos_offset) ? sc.pos_offset[j] : 0;
-        const int32_t oin = (j < n && sc.origin_in) ? sc.origin_in[j] : -1;
-        bool bad_fl = false;
-        const int32_t fl = j < n ? seq_frame_len(sc, j, bad_fl) : sc.frame_len;
+        const int32_t poff = j < n ? w_off : 0;
+        const int32_t oin = j < n ? w_oin : -1;
+        const bool bad_fl = j < n && w_fl != 0 && (w_fl < 65 || w_fl > kMaxFrameLen);
+        const int32_t fl = (j < n && w_fl != 0 && !bad_fl) ? w_fl : sc.frame_len;
         int32_t oseq = f == kNone ? kNone : poff + (int32_t)(f - W);
         if (oin >= 0) {
             mm = mm || f != kNone;
@@ -465,28 +512,63 @@ __device__ void scan_chunk(const Scan &sc, uint64_t *status, int64_t chunk, uint
                 }
             }
         } else {
+            // The window lanes whose sequences touch the chunk: [r_lo, r_hi].  A token belongs to the
+            // last of them that begins at or before it.  A few sequences are walked in a uniform loop
+            // -- each one's begin, origin, offset and frame length read from its lane into scalars,
+            // every token selecting it when it begins at or before the token -- which costs two
+            // instructions per sequence and token block; a chunk of many short sequences searches
+            // the window per token (six dependent shuffles).  Measured on 1,048,576 ragged tokens:
+            // the chunks holding 2-5 sequences ended 2.4 us after the others with the search.
+            const int r_lo = max(s_first - win, 0), r_hi = min(s_last - win, 63);
+            if (r_lo <= r_hi && r_hi - r_lo < kWalkSeqs) {
+                int64_t sbk[kSub];
+                int32_t ork[kSub], ofk[kSub], flk[kSub];
+                for (int r = r_lo; r <= r_hi; ++r) {
+                    const int64_t wr = lane_value(W, r);
+                    const int32_t o_r = __builtin_amdgcn_readlane(oseq, r), f_r = __builtin_amdgcn_readlane(poff, r);
+                    const int32_t l_r = __builtin_amdgcn_readlane(fl, r);
 #pragma unroll
-            for (int k = 0; k < kSub; ++k) {
-                const int64_t g = c0 + 64 * k + lane;
-                int r = 0;
+                    for (int k = 0; k < kSub; ++k) {
+                        if (r == r_lo || c0 + 64 * k + lane >= wr) {
+                            sbk[k] = wr;
+                            ork[k] = o_r;
+                            ofk[k] = f_r;
+                            flk[k] = l_r;
+                        }
+                    }
+                }
+                const int64_t t_lo = lane_value(W, r_lo), t_hi = lane_value(Wn, r_hi);
 #pragma unroll
-                for (int step = 32; step > 0; step >>= 1)
-                    if (__shfl(Wn, r + step - 1) <= g) r += step;
-                const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r), flr = __shfl(fl, r);
-                const int64_t sb = __shfl(W, r);
-                const bool ok = g < c_end && g >= w_lo && g < w_hi;
-                const int32_t p = offr + (int32_t)(g - sb);
-                int32_t t = 0, h = 0, w = 0;
-                if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, flr, t, h, w);
-                sink(k, ok, t, h, w, SeqInfo{sb, offr, orr, flr});
+                for (int k = 0; k < kSub; ++k) {
+                    const int64_t g = c0 + 64 * k + lane;
+                    const bool ok = g < c_end && g >= t_lo && g < t_hi;
+                    const int32_t p = ofk[k] + (int32_t)(g - sbk[k]);
+                    int32_t t = 0, h = 0, w = 0;
+                    if (ok) canvas_planes(p, (ork[k] != kNone && ork[k] <= p) ? ork[k] : kNone, flk[k], t, h, w);
+                    sink(k, ok, t, h, w, SeqInfo{sbk[k], ofk[k], ork[k], flk[k]});
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < kSub; ++k) {
+                    const int64_t g = c0 + 64 * k + lane;
+                    int r = 0;
+#pragma unroll
+                    for (int step = 32; step > 0; step >>= 1)
+                        if (__shfl(Wn, r + step - 1) <= g) r += step;
+                    const int32_t orr = __shfl(oseq, r), offr = __shfl(poff, r), flr = __shfl(fl, r);
+                    const int64_t sb = __shfl(W, r);
+                    const bool ok = g < c_end && g >= w_lo && g < w_hi;
+                    const int32_t p = offr + (int32_t)(g - sb);
+                    int32_t t = 0, h = 0, w = 0;
+                    if (ok) canvas_planes(p, (orr != kNone && orr <= p) ? orr : kNone, flr, t, h, w);
+                    sink(k, ok, t, h, w, SeqInfo{sb, offr, orr, flr});
+                }
             }
         }
-        if (win + 64 >= n || (int64_t)sc.cu[win + 64] > c_end) break;
+        // the next window's first begin is this window's last end (cu[win + 64])
+        if (win + 64 >= n || __shfl(Wn, 63) > c_end) break;
         win += 64;
-        const int32_t jn = win + lane;
-        const int32_t w0 = sc.cu[min(jn, n)], w1 = sc.cu[min(jn + 1, n)];
-        W = jn <= n ? (int64_t)w0 : INT64_MAX;
-        Wn = jn < n ? (int64_t)w1 : INT64_MAX;
+        load_window(win);
     }
 }
 
