@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "canvas M-RoPE Q+K tokens/sec and achieved HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+PATTERN_LIB = os.path.join(ROOT, "bench_pattern.so")
 WORKLOADS = {
     5: "1,048,576 ragged tokens (log-uniform lengths 64..16384, half text-only, half one image frame), bf16: "
        "planes from int32 ids + in-place rotary of Q[1048576,8,256] and K[1048576,2,256], one call",
@@ -418,6 +419,77 @@ def cpu_baseline_threads(b, qn, kn, threads: int, passes: int = 3):
                       f"{passes} passes, {threads} threads"}
 
 
+def pattern_mode(args, dev, stream):
+    """The rotary kernels of one workload beside reference kernels that move the same bytes with no
+    rotary arithmetic (bench_pattern.hip): the first 128 B of every 512 B head of ten heads a token
+    read only, written only, and read and written in place, plus dense reads, writes and a copy of
+    that byte count.  Each kernel is timed per launch (events) in three interleaved rounds."""
+    import ctypes
+
+    import torch
+
+    from canvas_rope_rotary_amd import synth
+
+    if not os.path.exists(PATTERN_LIB):
+        raise RuntimeError(f"{PATTERN_LIB} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(PATTERN_LIB)
+    lib.pattern_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.pattern_launch.restype = ctypes.c_int
+    cfg = synth.CONFIGS[args.config]()
+    L = cfg.n_tokens
+    b = Batch(cfg, dev)
+    b.make_planes()
+    heads = torch.empty((L, 10, 256), dtype=torch.bfloat16, device=dev).normal_()
+    nb = L * 10 * 128                      # the rotated bytes of every head, one direction
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(7)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    hs = ctypes.c_void_p(stream.cuda_stream)
+
+    def kernel(kind, a, bb, n):
+        def run():
+            rc = lib.pattern_launch(kind, ctypes.c_void_p(a.data_ptr()),
+                                    ctypes.c_void_p(bb.data_ptr() if bb is not None else 0), n, 0x9E3779B9,
+                                    ctypes.c_void_p(sink.data_ptr()), hs)
+            if rc != 0:
+                raise RuntimeError(f"pattern kernel {kind}: hipError {rc}")
+        return run
+
+    variants = [
+        ("sparse_read", kernel(0, heads, None, L), nb),
+        ("sparse_write", kernel(1, heads, None, L), nb),
+        ("sparse_read_write", kernel(2, heads, None, L), 2 * nb),
+        ("dense_read", kernel(3, src, None, nb), nb),
+        ("dense_write", kernel(4, dst, None, nb), nb),
+        ("dense_copy", kernel(5, src, dst, nb), 2 * nb),
+        ("mrope_apply", b.apply, algorithmic_bytes_apply(L)),
+        ("mrope_apply_ids", b.fused, algorithmic_bytes_fused(L)),
+    ]
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_s:
+        b.fused()
+        torch.cuda.synchronize()
+    durs = {name: [] for name, _, _ in variants}
+    for rnd in range(3):
+        for name, fn, _ in variants:
+            for _ in range(5):
+                fn()
+            d, _ = per_launch(fn, args.steps, stream)
+            durs[name] += d
+        log(f"pattern round {rnd} done")
+    out = {}
+    for name, _, byts in variants:
+        d = durs[name]
+        out[name] = dict(summary(d), bytes_per_launch=byts, tb_s_p50=byts / pct(d, 0.5) / 1e12)
+    print(json.dumps({"mode": "pattern", "workload": WORKLOADS[args.config], "tokens": L, "kernels": out}), flush=True)
+    log("| kernel | bytes per launch | p10 us | p50 us | p90 us | TB/s at p50 |")
+    log("|---|---|---|---|---|---|")
+    for name, k in out.items():
+        log(f"| {name} | {k['bytes_per_launch']:,} | {k['p10_us']:.1f} | {k['p50_us']:.1f} | {k['p90_us']:.1f} | "
+            f"{k['tb_s_p50']:.3f} |")
+
+
 KERNEL_CALLS = (  # rocprofv3 kernel name fragment -> the C entry point it serves
     ("apply_ids_sf_kernel", "mrope_apply_ids"),
     ("apply_ids_kernel", "mrope_apply_ids"),
@@ -522,10 +594,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--extras", action="store_true",
                     help="also time L=110 fp32, fp16/fp32 I/O, out of place, the K/V cache write and decode")
-    ap.add_argument("--mode", choices=("bench", "copy", "counters"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "copy", "counters", "pattern"), default="bench",
                     help="copy: only a plain 1 GiB device copy, repeated (calibrates rocprofv3 HBM counters); "
                          "counters: summarize four rocprofv3 --pmc run directories (no GPU) into "
-                         "profiles/hbm_counters.json")
+                         "profiles/hbm_counters.json; pattern: the rotary kernels beside reference kernels "
+                         "that move the same bytes without the arithmetic (bench_pattern.hip)")
     ap.add_argument("--fetch", help="counters mode: FETCH_SIZE run of the bench")
     ap.add_argument("--write", help="counters mode: WRITE_SIZE run of the bench")
     ap.add_argument("--fetch-copy", help="counters mode: FETCH_SIZE run of --mode copy")
@@ -559,6 +632,9 @@ def main():
         return
     mr._lib.load()
     stream = torch.cuda.current_stream(dev)
+    if args.mode == "pattern":
+        pattern_mode(args, dev, stream)
+        return
 
     cfg = synth.CONFIGS[args.config]()
     log(f"workload {cfg.name}: {cfg.n_tokens} tokens, {cfg.n_seqs} sequences; generating inputs")
