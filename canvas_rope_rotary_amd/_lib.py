@@ -28,6 +28,7 @@ EXPORTS = ("mrope_abi_version", "mrope_status_string", "mrope_last_error", "mrop
 HOOK_FUSED_CHUNKED = 1
 HOOK_FUSED_SCAN_FIRST = 2
 HOOK_SCAN_FALLBACK = 4
+HOOK_F32_EIGHT_LANES = 8
 
 
 def set_test_hooks(flags: int) -> int:

@@ -276,7 +276,8 @@ const char *mrope_last_error(void) { return g_last_error; }
 int mrope_set_test_hooks(int flags)
 {
     const int prev = g_test_hooks.load(std::memory_order_relaxed);
-    g_test_hooks.store(flags & (kHookFusedChunked | kHookFusedScanFirst | kHookScanFallback), std::memory_order_relaxed);
+    g_test_hooks.store(flags & (kHookFusedChunked | kHookFusedScanFirst | kHookScanFallback | kHookF32EightLanes),
+                       std::memory_order_relaxed);
     return prev;
 }
 

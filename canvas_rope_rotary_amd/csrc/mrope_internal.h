@@ -79,11 +79,13 @@ struct Scan {
     uint32_t epoch;      // tags this launch's status words; 0 = use (and advance) the device counter
 };
 
-// Test and tuning hooks (mrope_set_test_hooks): which fused kernel serves mrope_apply_ids, and a
-// mode that makes the scan-first kernel's rotation workgroups derive their planes themselves.
+// Test and tuning hooks (mrope_set_test_hooks): which fused kernel serves mrope_apply_ids, a mode
+// that makes the scan-first kernel's rotation workgroups derive their planes themselves, and the
+// lane layout of mrope_apply in fp32.
 constexpr int kHookFusedChunked = 1;   // always the chunk-per-workgroup fused kernel
 constexpr int kHookFusedScanFirst = 2; // always the scan-first fused kernel (8 Q + 2 K heads)
 constexpr int kHookScanFallback = 4;   // scan-first: rotation workgroups first, no waiting
+constexpr int kHookF32EightLanes = 8;  // mrope_apply in fp32: the eight-lane kernel, not sixteen lanes
 int test_hooks();
 
 // Paged K/V cache destination.  Element (block, row, head, d) of either cache is at

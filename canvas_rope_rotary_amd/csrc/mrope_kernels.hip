@@ -1014,6 +1014,157 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(Heads hd, Rotary rot, con
     }
 }
 
+// ------------------------------------------------------------------ fp32: sixteen lanes a token --
+// An fp32 head's rotated dims are 256 bytes.  In the eight-lane layout each lane loads two 16-byte
+// vectors per head, and the prefetching loop over ten heads then needs about 256 VGPRs: one wave
+// per SIMD.  mrope_apply in fp32 (8 Q + 2 K heads, no cache) takes sixteen lanes a token instead:
+// lane l = 2m + half holds dims [32 half + 4m, 32 half + 4m + 4) -- frequencies 4m .. 4m+3, the x_j
+// side (half 0) or the x_{j+32} side (half 1) -- one 16-byte vector per head, the 16-bit types'
+// register budget.  Each lane evaluates two of its pair's four sincos and the pair swaps them by
+// DPP, as in the eight-lane layout; every output is the same double expression, rounded once.
+constexpr int kLanesW = 16;
+constexpr int kTokPerBlockW = kBlock / kLanesW;
+
+struct LaneFreq2 {
+    float f[2];
+    uint32_t sel;
+    int half;
+};
+
+// The two inverse frequencies a lane evaluates (2q, 2q + 1 with q = 2m + half) and their planes,
+// taken from the kernel arguments by uniform selects (see lane_freq).
+__device__ __forceinline__ LaneFreq2 lane_freq2(const Rotary &rot, int m, int half)
+{
+    LaneFreq2 r;
+    const int q = 2 * m + half;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float v = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float x = rot.inv_freq[2 * t + i];
+            asm volatile("" : "+s"(x));
+            v = q == t ? x : v;
+        }
+        r.f[i] = v;
+    }
+    r.sel = (uint32_t)(rot.plane_sel >> (4 * q));
+    r.half = half;
+    return r;
+}
+
+// (cos, sign*sin) of frequencies 4m .. 4m+3 for lane pair m, as pair_sincos.
+__device__ __forceinline__ void pair_sincos4(const LaneFreq2 &lf, int32_t pt, int32_t ph, int32_t pw,
+                                             double (&c)[4], double (&ss)[4])
+{
+    const int half = lf.half;
+    double oc[2], os[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t pl = (lf.sel >> (2 * i)) & 3u;
+        const int32_t pos = pl == 1u ? ph : (pl == 2u ? pw : pt);
+        const float a = (float)pos * lf.f[i];
+        sincos_angle(a, &os[i], &oc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const double pc = swap_pair(oc[i]), ps = swap_pair(os[i]);
+        c[i] = half ? pc : oc[i];
+        c[2 + i] = half ? oc[i] : pc;
+        const double s_lo = half ? ps : os[i], s_hi = half ? os[i] : ps;
+        ss[i] = half ? s_lo : -s_lo;
+        ss[2 + i] = half ? s_hi : -s_hi;
+    }
+}
+
+// Four fp32 dims of one head: own from this lane, the partner's by DPP.
+__device__ __forceinline__ uint4 rotate4(const uint4 &own, const double (&c)[4], const double (&ss)[4])
+{
+    const float x[4] = {__uint_as_float(own.x), __uint_as_float(own.y), __uint_as_float(own.z), __uint_as_float(own.w)};
+    const float p[4] = {__uint_as_float(swap_pair(own.x)), __uint_as_float(swap_pair(own.y)),
+                        __uint_as_float(swap_pair(own.z)), __uint_as_float(swap_pair(own.w))};
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (float)__builtin_fma((double)x[e], c[e], (double)p[e] * ss[e]);
+    return make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3]));
+}
+
+template <int NQ, int NK>
+__device__ __forceinline__ void load_token_w(const Heads &hd, int64_t g, int e0, uint4 (&qv)[NQ], uint4 (&kv)[NK])
+{
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) qv[h] = load16_nt(static_cast<const float *>(hd.q) + q_off(hd, g, h) + e0);
+#pragma unroll
+    for (int h = 0; h < NK; ++h) kv[h] = load16_nt(static_cast<const float *>(hd.k) + k_off(hd, g, h) + e0);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16_as(void *base, int64_t elem, const uint4 &v)
+{
+    float *p = static_cast<float *>(base) + elem;
+    if constexpr (NT) __builtin_nontemporal_store((u32x4_t){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
+    else *reinterpret_cast<uint4 *>(p) = v;
+}
+
+// apply_kernel's loop for fp32 with sixteen lanes a token: 4-token groups, one per wave per step,
+// each 16-lane group prefetching its next token before rotating the current one.
+template <int NQ, int NK, bool NTS>
+__global__ __launch_bounds__(kBlock) void apply_f32w_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
+                                                            int64_t ps)
+{
+    const int tid = threadIdx.x;
+    const int l = tid & 15, m = l >> 1, half = l & 1;
+    const int e0 = 32 * half + 4 * m;
+    const LaneFreq2 lf = lane_freq2(rot, m, half);
+    const int64_t stride = (int64_t)gridDim.x * kTokPerBlockW;
+    int64_t G = (int64_t)blockIdx.x * kTokPerBlockW + (tid >> 6) * 4;  // first token of the wave's group
+    const int sub = (tid & 63) >> 4;
+    int64_t g = G + sub;
+    bool ok = g < hd.n_tokens;
+    int32_t pt = 0, ph = 0, pw = 0;
+    uint4 qv[NQ], kv[NK];
+    if (ok) {
+        pt = planes[g];
+        ph = planes[ps + g];
+        pw = planes[2 * ps + g];
+        load_token_w<NQ, NK>(hd, g, e0, qv, kv);
+    }
+    wait_vm_all();  // as in apply_kernel
+    void *qo = hd.q_out ? hd.q_out : hd.q;
+    void *ko = hd.k_out ? hd.k_out : hd.k;
+    while (G < hd.n_tokens) {
+        const int64_t Gn = G + stride;
+        const int64_t gn = Gn + sub;
+        const bool okn = gn < hd.n_tokens;
+        int32_t nt = 0, nh = 0, nw = 0;
+        uint4 qn[NQ], kn[NK];
+        if (okn) {
+            nt = planes[gn];
+            nh = planes[ps + gn];
+            nw = planes[2 * ps + gn];
+            load_token_w<NQ, NK>(hd, gn, e0, qn, kn);
+        }
+        if (ok) {
+            double c[4], ss[4];
+            pair_sincos4(lf, pt, ph, pw, c, ss);
+#pragma unroll
+            for (int h = 0; h < NQ; ++h) store16_as<NTS>(qo, q_off(hd, g, h) + e0, rotate4(qv[h], c, ss));
+#pragma unroll
+            for (int h = 0; h < NK; ++h) store16_as<NTS>(ko, k_off(hd, g, h) + e0, rotate4(kv[h], c, ss));
+        }
+        G = Gn;
+        g = gn;
+        ok = okn;
+        pt = nt;
+        ph = nh;
+        pw = nw;
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) qv[h] = qn[h];
+#pragma unroll
+        for (int h = 0; h < NK; ++h) kv[h] = kn[h];
+    }
+}
+
 // One token of the cache-writing path (fixed head counts, head_dim 256): every load of the token --
 // its Q and K rotation chunks, K pass-through and V chunks -- goes out at once, then the math, then
 // the stores (Q in place, K and V into the cache slot, nothing for a slot outside the cache).  No
@@ -1771,6 +1922,17 @@ static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t 
                 const unsigned kv_blocks = (unsigned)groups;
                 if (nts) apply_kv_kernel<IO, 8, 2, true><<<kv_blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
                 else apply_kv_kernel<IO, 8, 2, false><<<kv_blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
+                return hipGetLastError();
+            }
+        }
+        if constexpr (IO == kIoF32) {
+            if (!(test_hooks() & kHookF32EightLanes)) {
+                // sixteen lanes a token: the same grid policy over 16-token workgroup steps
+                const int64_t groups_w = (h.n_tokens + kTokPerBlockW - 1) / kTokPerBlockW;
+                const int64_t cap_w = groups_w > 16 * persistent ? groups_w : persistent;
+                const unsigned blocks_w = (unsigned)(groups_w < cap_w ? groups_w : cap_w);
+                if (nts) apply_f32w_kernel<8, 2, true><<<blocks_w, kBlock, 0, st>>>(h, r, planes, ps);
+                else apply_f32w_kernel<8, 2, false><<<blocks_w, kBlock, 0, st>>>(h, r, planes, ps);
                 return hipGetLastError();
             }
         }

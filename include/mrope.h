@@ -83,10 +83,13 @@ const char *mrope_last_error(void);
  *   MROPE_HOOK_FUSED_CHUNKED     always the chunk-per-workgroup fused kernel
  *   MROPE_HOOK_FUSED_SCAN_FIRST  always the scan-first fused kernel (8 Q + 2 K heads, no cache write)
  *   MROPE_HOOK_SCAN_FALLBACK     scan-first kernel whose rotation workgroups derive their planes
- *                                themselves instead of waiting for the scan's handover */
+ *                                themselves instead of waiting for the scan's handover
+ *   MROPE_HOOK_F32_EIGHT_LANES   mrope_apply in fp32 with eight lanes a token (two 16-byte loads per
+ *                                head and lane) instead of sixteen */
 #define MROPE_HOOK_FUSED_CHUNKED 1
 #define MROPE_HOOK_FUSED_SCAN_FIRST 2
 #define MROPE_HOOK_SCAN_FALLBACK 4
+#define MROPE_HOOK_F32_EIGHT_LANES 8
 int mrope_set_test_hooks(int flags);
 
 /* ---------------------------------------------------------------------------------------------

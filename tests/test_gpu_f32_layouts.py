@@ -1,0 +1,90 @@
+"""GPU parity of mrope_apply in fp32 in both lane layouts: sixteen lanes a token (the default) and
+eight (MROPE_HOOK_F32_EIGHT_LANES).  Each is compared with the oracle (fp32 gate) and with the other
+bit for bit, in place and out of place, on strided views, and past the size from which in-place
+stores take the non-temporal hint."""
+import numpy as np
+import pytest
+import torch
+
+import canvas_rope_rotary_amd as mr
+import oracle
+from canvas_rope_rotary_amd import _lib, synth
+from gpu_util import MARKER, compare_heads, compare_heads_all, dev_heads, host_heads, i32, say
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = {"sixteen": 0, "eight": _lib.HOOK_F32_EIGHT_LANES}
+
+
+def _both_layouts(run):
+    out = {}
+    for name, hook in LAYOUTS.items():
+        prev = _lib.set_test_hooks(hook)
+        try:
+            out[name] = run()
+        finally:
+            _lib.set_test_hooks(prev)
+    return out
+
+
+@pytest.mark.parametrize("seed,n_seqs,max_len", [(601, 1, 110), (602, 30, 700), (603, 7, 5000)])
+@pytest.mark.parametrize("out_of_place", [False, True])
+def test_f32_layouts_match_oracle_and_each_other(seed, n_seqs, max_len, out_of_place):
+    b = synth.random_batch(seed, n_seqs, max_len=max_len, min_len=max_len if n_seqs == 1 else 1, dtype="f32")
+    qn, kn = b.qk()
+    pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    say(f"case: fp32 layouts seed={seed} tokens={b.n_tokens} out_of_place={out_of_place}")
+
+    def run():
+        q, k = dev_heads(qn, "f32"), dev_heads(kn, "f32")
+        if out_of_place:
+            qo, ko = torch.full_like(q, -3.0), torch.full_like(k, -3.0)
+            mr.apply(q, k, pl, q_out=qo, k_out=ko)
+            np.testing.assert_array_equal(host_heads(q), qn)
+            return host_heads(qo), host_heads(ko)
+        mr.apply(q, k, pl)
+        return host_heads(q), host_heads(k)
+
+    res = _both_layouts(run)
+    for name, (q, k) in res.items():
+        compare_heads(q, qn, epl, "f32", what=f"{name} q")
+        compare_heads(k, kn, epl, "f32", what=f"{name} k")
+    for a, c in zip(res["sixteen"], res["eight"]):
+        np.testing.assert_array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+def test_f32_layouts_on_strided_views():
+    """Q and K as head-slices of one fused [T, 12, 256] projection buffer."""
+    b = synth.random_batch(611, 12, max_len=900, dtype="f32")
+    qn, kn = b.qk()
+    T = b.n_tokens
+    pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    filler = np.full((T, 2, 256), 7.0, np.float32)
+    say(f"case: fp32 layouts on views, {T} tokens")
+
+    def run():
+        fused = torch.from_numpy(np.concatenate([qn, kn, filler], axis=1)).cuda()
+        mr.apply(fused[:, :8], fused[:, 8:10], pl)
+        out = fused.cpu().numpy()
+        np.testing.assert_array_equal(out[:, 10:], filler)
+        return out[:, :8].copy(), out[:, 8:10].copy()
+
+    res = _both_layouts(run)
+    for name, (q, k) in res.items():
+        compare_heads(q, qn, epl, "f32", what=f"{name} view q")
+        compare_heads(k, kn, epl, "f32", what=f"{name} view k")
+
+
+def test_f32_sixteen_lanes_past_the_store_hint_size():
+    """48 x 4,096 fp32 tokens write 402 MB in place: the hinted stores; every element compared."""
+    b = synth.random_batch(621, 48, max_len=4096, min_len=4096, dtype="f32")
+    qn, kn = b.qk()
+    pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    q, k = dev_heads(qn, "f32"), dev_heads(kn, "f32")
+    say(f"case: fp32 sixteen lanes, {b.n_tokens} tokens")
+    mr.apply(q, k, pl)
+    compare_heads_all(q, qn, epl, "f32", what="q")
+    compare_heads_all(k, kn, epl, "f32", what="k")
