@@ -382,6 +382,25 @@ def apply_ids_noalloc(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor
     return start, amount, origin, seq_flags, planes_out
 
 
+def check_slots(slot_mapping: torch.Tensor, num_slots: int) -> None:
+    """Debug check for a cache write: raise ValueError when two entries of slot_mapping name the
+    same slot inside the cache ([0, num_slots)), where which token lands is undefined.  Runs torch
+    operations on the mapping's device and waits for them; the cache-writing calls run it when
+    given check_slots=True."""
+    s = slot_mapping.reshape(-1)
+    s = s[(s >= 0) & (s < num_slots)]
+    if s.numel() < 2:
+        return
+    srt = torch.sort(s).values
+    dup = srt[1:] == srt[:-1]
+    if bool(dup.any()):
+        first = int(srt[1:][dup][0])
+        raise ValueError(f"slot_mapping names slot {first} (and {int(dup.sum())} repeats in all) more than once")
+
+
+_slot_check = check_slots  # the cache-writing calls' keyword of the same name shadows it there
+
+
 def _paged(k_cache, v_cache, slot_mapping, v, n_rows: int, nk: int, D: int, dtype, what: str):
     """Check a paged K/V cache pair and its slots; returns the C arguments (v strides, cache args)."""
     if k_cache is None or slot_mapping is None:
@@ -408,11 +427,13 @@ def _paged(k_cache, v_cache, slot_mapping, v, n_rows: int, nk: int, D: int, dtyp
 
 
 def apply_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, planes_: torch.Tensor, k_cache: torch.Tensor,
-             v_cache: torch.Tensor | None, slot_mapping: torch.Tensor, theta: float = 1e7, *, rot_dim: int = ROT_DIM):
+             v_cache: torch.Tensor | None, slot_mapping: torch.Tensor, theta: float = 1e7, *, rot_dim: int = ROT_DIM,
+             check_slots: bool = False):
     """Prefill rotation with the paged K/V cache write: q [T, Hq, D] rotated in place; k [T, Hk, D]
     rotated and written whole into k_cache [num_blocks, block_size, Hk, D] at slot_mapping (int64
     [T]; slots outside the cache are skipped); v [T, Hk, D] copied into v_cache.  k and v are not
-    modified.  Returns (q, k_cache, v_cache)."""
+    modified.  check_slots: first raise ValueError if two tokens share a slot (see check_slots()).
+    Returns (q, k_cache, v_cache)."""
     dev = _require_cuda(q, k, v, planes_, k_cache, v_cache, slot_mapping)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, None, None)
     T = q.shape[0]
@@ -420,6 +441,8 @@ def apply_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, planes_: 
             or planes_.stride(1) != 1:
         raise ValueError("planes must be an int32 [3, >= tokens] tensor with unit column stride")
     (vt, vh), cache = _paged(k_cache, v_cache, slot_mapping, v, T, nk, D, q.dtype, "apply_kv")
+    if check_slots:
+        _slot_check(slot_mapping, k_cache.shape[0] * k_cache.shape[1])
     with _on_device(dev):
         _check(load().mrope_apply_kv(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
                                      _ptr(planes_), planes_.stride(0), float(theta), *cache, _stream(dev)))
@@ -430,10 +453,11 @@ def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: 
                  k_cache: torch.Tensor, v_cache: torch.Tensor | None, slot_mapping: torch.Tensor,
                  marker_id: int = 248078, theta: float = 1e7, *, planes_out=None, start=None, amount=None,
                  origin=None, seq_flags=None, pos_offset=None, origin_in=None, frame_len: int = 67,
-                 frame_len_seq=None, workspace: Workspace | None = None, rot_dim: int = ROT_DIM):
+                 frame_len_seq=None, workspace: Workspace | None = None, rot_dim: int = ROT_DIM,
+                 check_slots: bool = False):
     """apply_ids with the cache write of apply_kv, in one launch: ids -> planes -> q rotated in
-    place, k rotated into k_cache, v copied into v_cache.  Returns (start, amount, origin,
-    seq_flags, planes_out or None)."""
+    place, k rotated into k_cache, v copied into v_cache.  check_slots as in apply_kv.  Returns
+    (start, amount, origin, seq_flags, planes_out or None)."""
     dev = _require_cuda(q, k, v, ids, cu_seqlens, k_cache, v_cache, slot_mapping, planes_out, start, amount, origin,
                         seq_flags, pos_offset, origin_in, frame_len_seq)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, None, None)
@@ -451,6 +475,8 @@ def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: 
             raise ValueError("planes_out must be an int32 [3, >= tokens] tensor with unit column stride")
         ps = planes_out.stride(0)
     (vt, vh), cache = _paged(k_cache, v_cache, slot_mapping, v, T, nk, D, q.dtype, "apply_ids_kv")
+    if check_slots:
+        _slot_check(slot_mapping, k_cache.shape[0] * k_cache.shape[1])
     mk = lambda t, name: _i32_vec(t, name, n) if t is not None else torch.empty(n, dtype=torch.int32, device=dev)
     start, amount, origin, seq_flags = (mk(start, "start"), mk(amount, "amount"), mk(origin, "origin"),
                                         mk(seq_flags, "seq_flags"))
@@ -467,11 +493,12 @@ def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: 
 
 def decode(q: torch.Tensor, k: torch.Tensor | None, pos: torch.Tensor, amount: torch.Tensor,
            k_cache: torch.Tensor | None, slot_mapping: torch.Tensor | None, theta: float = 1e7, *,
-           v: torch.Tensor | None = None, v_cache: torch.Tensor | None = None, rot_dim: int = ROT_DIM):
+           v: torch.Tensor | None = None, v_cache: torch.Tensor | None = None, rot_dim: int = ROT_DIM,
+           check_slots: bool = False):
     """One generated token per sequence: rotate q [S, Hq, D] in place at plane pos - amount; rotate
     k [S, Hk, D] and write it into k_cache [num_blocks, block_size, Hk, D] at slot_mapping (int64,
     slots outside the cache are skipped); copy v [S, Hk, D] (optional) into v_cache at the same
-    slots."""
+    slots.  check_slots as in apply_kv."""
     dev = _require_cuda(q, k, pos, amount, k_cache, slot_mapping, v, v_cache)
     dt, qt, qh, nq, kt, kh, nk, D = _qk_args(q, k, None, None)
     S = q.shape[0]
@@ -479,6 +506,8 @@ def decode(q: torch.Tensor, k: torch.Tensor | None, pos: torch.Tensor, amount: t
     _i32_vec(amount, "amount", S)
     if nk:
         (vt, vh), cache = _paged(k_cache, v_cache, slot_mapping, v, S, nk, D, q.dtype, "decode")
+        if check_slots:
+            _slot_check(slot_mapping, k_cache.shape[0] * k_cache.shape[1])
     else:
         (vt, vh), cache = (0, 0), (None, None, None, 1, 0, 0, 0, 0)
     with _on_device(dev):

@@ -214,3 +214,18 @@ def _apply_ids_noalloc(lib, **kw):
 def test_apply_ids_noalloc_validation(lib, kw, code):
     """Rejected on the host before the first use of the static scratch (nothing is launched)."""
     assert _apply_ids_noalloc(lib, **kw) == code
+
+
+def test_check_slots_flags_shared_slots():
+    """The cache-writing calls' debug check: slots outside the cache never count; two tokens on one
+    slot inside it do (torch operations only, so CPU tensors serve)."""
+    import torch
+
+    import canvas_rope_rotary_amd as mr
+
+    mr.check_slots(torch.tensor([0, 5, 3, -1, -1, 64, 64, 2], dtype=torch.int64), 64)
+    mr.check_slots(torch.tensor([], dtype=torch.int64), 64)
+    with pytest.raises(ValueError, match="slot 3"):
+        mr.check_slots(torch.tensor([0, 3, 7, 3], dtype=torch.int64), 64)
+    with pytest.raises(ValueError):
+        mr.check_slots(torch.tensor([63, 1, 63], dtype=torch.int64), 64)

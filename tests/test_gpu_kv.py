@@ -233,3 +233,24 @@ def test_kv_past_the_store_hint_size(fused):
     rows = torch.from_numpy(slots[ok]).cuda()
     compare_heads_all(kc.view(S, 2, 256)[rows], kn[ok], epl[:, ok], "bf16", what="k cache")
     np.testing.assert_array_equal(host_heads(vc.view(S, 2, 256)[rows]), vn[ok])
+
+
+def test_check_slots_option():
+    """check_slots=True: distinct slots run as usual; a slot named twice raises before anything is
+    launched (q keeps its values)."""
+    d = synth.config4(n_seqs=64, num_blocks=128)
+    qn, kn = d.qk()
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    kc = new_cache(d.num_blocks, d.block_size, 2, 256, "bf16", 0.0)
+    pos, am = torch.from_numpy(d.pos).cuda(), torch.from_numpy(d.amount).cuda()
+    say("case: decode check_slots")
+    mr.decode(q, k, pos, am, kc, torch.from_numpy(d.slot_mapping).cuda(), check_slots=True)
+    planes = np.stack([d.pos - d.amount] * 3).astype(np.int32)
+    compare_heads(host_heads(q), qn, planes, "bf16", what="decode q")
+    dup = d.slot_mapping.copy()
+    dup[7] = dup[3]
+    before = host_heads(q)
+    with pytest.raises(ValueError):
+        mr.decode(q, k, pos, am, kc, torch.from_numpy(dup).cuda(), check_slots=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_heads(q), before)
