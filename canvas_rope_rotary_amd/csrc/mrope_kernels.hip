@@ -75,14 +75,15 @@ __device__ __forceinline__ void canvas_planes(int32_t p, int32_t o, int32_t fl, 
 
 // ------------------------------------------------------------------ workspace ------------------
 // Header (256 bytes): the device epoch counter, used when the caller passes epoch 0; then one status
-// word per 64-token tile.
+// word per 512-token chunk, the scan-first kernel's part records and its per-token planes of shared
+// parts (ws_layout).
 struct WsHeader {
     uint32_t epoch;
 };
 
-// status word of a tile: [63:34] epoch | [33:32] flag | [31] multi | [30:0] first marker (global idx)
-constexpr uint64_t kAgg = 1;   // value covers only this tile's part of its last sequence
-constexpr uint64_t kIncl = 2;  // value covers the whole sequence up to the end of this tile
+// status word of a chunk: [63:34] epoch | [33:32] flag | [31] multi | [30:0] first marker (global idx)
+constexpr uint64_t kAgg = 1;   // value covers only this chunk's part of its last sequence
+constexpr uint64_t kIncl = 2;  // value covers the whole sequence up to the end of this chunk
 constexpr uint32_t kEpochMask = 0x1fffffffu;  // caller epochs use 29 bits ...
 constexpr uint32_t kDeviceEpochBit = 0x20000000u;  // ... device-counter epochs carry bit 29 as well
 
@@ -2046,8 +2047,10 @@ hipError_t launch_apply_ids(const Heads &h, const Rotary &r, const Scan &s, cons
     }
     // With the planes wanted in memory anyway (planes_out) and past the size where mrope_apply
     // takes one step per workgroup, the scan writes planes_out and the rotation reads it back: one
-    // workgroup per chunk cannot use that grid.  Measured (bf16): 1,048,576 ragged tokens 17.5 +
-    // 465 us against 508 us fused; 524,288 tokens ~243 against 261 us.
+    // workgroup per chunk cannot use that grid.  The scan-first kernel serves the model's heads
+    // without a cache write; this route serves the cache-writing call.  Measured (bf16, before the
+    // scan-first kernel): 1,048,576 ragged tokens 17.5 + 465 us against 508 us fused; 524,288
+    // tokens ~243 against 261 us.
     const int64_t one_step_from = (int64_t)compute_units() * kApplyBlocksPerCU * 16 * kTokPerBlock;
     if (s.planes && fixed_heads(h, pc, io) && h.n_tokens > one_step_from) {
         const hipError_t e = launch_planes(s, stream);

@@ -15,10 +15,11 @@
  *
  * Conventions for every entry point
  *   - Pointers to tensors are DEVICE pointers owned by the caller.  The library allocates no
- *     device memory.  State that crosses calls lives in the caller's workspace (see
+ *     device memory (mrope_apply_ids_noalloc's workspace is a static device array of the library,
+ *     see there).  State that crosses calls lives in the caller's workspace (see
  *     mrope_workspace_bytes); the library itself keeps only a per-thread copy of the last error
- *     text (mrope_last_error) and, per device, the compute-unit count it sizes its grids by (read
- *     once).
+ *     text (mrope_last_error), per device the compute-unit count it sizes its grids by (read once)
+ *     and the static array's address, and the process-wide test-hook flags (mrope_set_test_hooks).
  *   - Every call enqueues its work on `stream` (a hipStream_t; NULL = the null stream) and returns
  *     without synchronising.  Calls issue no memset and no allocation, so they can be captured in a
  *     HIP graph.
@@ -28,7 +29,8 @@
  *   - Strides are in ELEMENTS of the tensor's dtype.  Q and K element (t, h, d) is at
  *     t*tok_stride + h*head_stride + d; d is contiguous.
  *   - Data-dependent conditions (two image markers in a sequence, a frame running past the end of
- *     its sequence) are reported per sequence in the optional seq_flags array, never by a status.
+ *     its sequence, a per-sequence frame length that describes no frame) are reported per sequence
+ *     in the optional seq_flags array, never by a status.
  *   - Calls that share a workspace must be ordered (same stream, or synchronised); concurrent calls
  *     on one workspace race.
  */
