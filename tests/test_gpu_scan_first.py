@@ -141,3 +141,27 @@ def test_repeated_calls_share_a_workspace(mode):
         epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
         compare_heads(host_heads(q), qn, epl, "bf16", what=f"{mode} call {i} q")
         compare_heads(host_heads(k), kn, epl, "bf16", what=f"{mode} call {i} k")
+
+
+def test_two_level_sequence_search(mode):
+    """20,000 sequences of 0..12 tokens: past 8,063 sequences the bracket search takes two levels
+    before the window load, and chunks hold dozens of sequences (walked, searched, or counted past
+    the window)."""
+    g = np.random.default_rng(17)
+    lens = g.integers(0, 13, size=20000)
+    ids = synth.text_ids(synth.rng(17, 4), int(lens.sum()))
+    ids[g.integers(0, ids.size, size=3000)] = MARKER
+    cu = np.zeros(lens.size + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    b = synth.Prefill("two-level", ids, cu, [None] * lens.size, "bf16", seed=17)
+    say(f"case: {mode} 20000 sequences, {b.n_tokens} tokens")
+    _run(b, mode, True)
+    fls = g.choice(np.array([65, 67, 75, 0], np.int32), size=lens.size)
+    qn, kn = b.qk()
+    q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+    st, am, og, fl, _ = mr.apply_ids(q, k, i32(b.ids), i32(b.cu_seqlens), MARKER, frame_len_seq=i32(fls))
+    epl, est, eam, eog = oracle.planes_chunk(b.ids, b.cu_seqlens, MARKER, frame_len_seq=fls)
+    for got, want, name in ((st, est, "start"), (am, eam, "amount"), (og, eog, "origin")):
+        np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"{mode} two-level {name}")
+    compare_heads(host_heads(q), qn, epl, "bf16", what=f"{mode} two-level q")
+    compare_heads(host_heads(k), kn, epl, "bf16", what=f"{mode} two-level k")
