@@ -490,6 +490,42 @@ def pattern_mode(args, dev, stream):
             f"{k['tb_s_p50']:.3f} |")
 
 
+def f32_mode(args, dev, stream):
+    """mrope_apply in fp32 on 64 x 4,096 image prompts in both lane layouts, interleaved: sixteen
+    lanes a token (the library's choice) and eight (the MROPE_HOOK_F32_EIGHT_LANES test hook).
+    Per-launch events, three rounds of `steps` launches after 5 untimed ones each."""
+    import numpy as np
+    import torch
+
+    import canvas_rope_rotary_amd as mr
+    from canvas_rope_rotary_amd import _lib, synth
+
+    cfg = synth.CONFIGS[2]()
+    L = cfg.n_tokens
+    qn, kn = cfg.qk()
+    q = torch.from_numpy(synth.to_f32(qn, "bf16")).to(dev)
+    k = torch.from_numpy(synth.to_f32(kn, "bf16")).to(dev)
+    del qn, kn
+    pl, *_ = mr.planes(torch.from_numpy(cfg.ids).to(dev), torch.from_numpy(cfg.cu_seqlens).to(dev), synth.IMAGE_ID)
+    byts = L * (10 * 64 * 4 * 2 + 12)
+    durs = {"sixteen_lanes": [], "eight_lanes": []}
+    hooks = {"sixteen_lanes": 0, "eight_lanes": _lib.HOOK_F32_EIGHT_LANES}
+    prev = _lib.set_test_hooks(0)
+    try:
+        for rnd in range(3):
+            for name, hk in hooks.items():
+                _lib.set_test_hooks(hk)
+                for _ in range(5):
+                    mr.apply(q, k, pl)
+                d, _ = per_launch(lambda: mr.apply(q, k, pl), args.steps, stream)
+                durs[name] += d
+    finally:
+        _lib.set_test_hooks(prev)
+    out = {name: dict(summary(d), gbs_p50=byts / pct(d, 0.5) / 1e9) for name, d in durs.items()}
+    print(json.dumps({"mode": "f32", "workload": "64 x 4,096 image prompts, fp32 Q[262144,8,256] and K[262144,2,256] "
+                      "in place, planes given", "algorithmic_bytes_per_launch": byts, "kernels": out}), flush=True)
+
+
 KERNEL_CALLS = (  # rocprofv3 kernel name fragment -> the C entry point it serves
     ("apply_ids_sf_kernel", "mrope_apply_ids"),
     ("apply_ids_kernel", "mrope_apply_ids"),
@@ -594,11 +630,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--extras", action="store_true",
                     help="also time L=110 fp32, fp16/fp32 I/O, out of place, the K/V cache write and decode")
-    ap.add_argument("--mode", choices=("bench", "copy", "counters", "pattern"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "copy", "counters", "pattern", "f32"), default="bench",
                     help="copy: only a plain 1 GiB device copy, repeated (calibrates rocprofv3 HBM counters); "
                          "counters: summarize four rocprofv3 --pmc run directories (no GPU) into "
                          "profiles/hbm_counters.json; pattern: the rotary kernels beside reference kernels "
-                         "that move the same bytes without the arithmetic (bench_pattern.hip)")
+                         "that move the same bytes without the arithmetic (bench_pattern.hip); f32: "
+                         "mrope_apply in fp32 in both lane layouts")
     ap.add_argument("--fetch", help="counters mode: FETCH_SIZE run of the bench")
     ap.add_argument("--write", help="counters mode: WRITE_SIZE run of the bench")
     ap.add_argument("--fetch-copy", help="counters mode: FETCH_SIZE run of --mode copy")
@@ -634,6 +671,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.mode == "pattern":
         pattern_mode(args, dev, stream)
+        return
+    if args.mode == "f32":
+        f32_mode(args, dev, stream)
         return
 
     cfg = synth.CONFIGS[args.config]()
