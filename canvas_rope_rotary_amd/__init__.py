@@ -23,11 +23,11 @@ from __future__ import annotations
 from . import _lib
 from ._lib import (MROPE_BF16, MROPE_F16, MROPE_F32, MarkerFlags, MropeError, TEXT_ONLY_START, Workspace, apply, apply_ids,
                    apply_ids_kv, apply_ids_noalloc, apply_kv, check_slots, cu_seqlens_from_lens, decode, library_path,
-                   planes)
+                   planes, prepare, PreparedCall)
 
 IMAGE_ID = 248078
 DEFAULT_THETA = 1e7
 
 __all__ = ["planes", "apply", "apply_ids", "apply_ids_noalloc", "apply_kv", "apply_ids_kv", "decode", "Workspace", "MropeError", "MarkerFlags",
-           "check_slots", "cu_seqlens_from_lens", "library_path", "IMAGE_ID", "DEFAULT_THETA", "TEXT_ONLY_START",
+           "check_slots", "prepare", "PreparedCall", "cu_seqlens_from_lens", "library_path", "IMAGE_ID", "DEFAULT_THETA", "TEXT_ONLY_START",
            "MROPE_F32", "MROPE_BF16", "MROPE_F16"]

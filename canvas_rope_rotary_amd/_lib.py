@@ -105,6 +105,31 @@ def _check(status: int):
         raise MropeError(status, f"{lib.mrope_status_string(status).decode()}: {lib.mrope_last_error().decode()}")
 
 
+# While prepare() runs a binding function, the C calls it would make are recorded here instead.
+_recording: list | None = None
+
+
+class _EpochSlot:
+    """Stands for a workspace's next epoch in a recorded call: each run of the prepared call takes a
+    fresh one."""
+
+    __slots__ = ("ws",)
+
+    def __init__(self, ws):
+        self.ws = ws
+
+
+def _epoch(ws):
+    return _EpochSlot(ws) if _recording is not None else ws.next_epoch()
+
+
+def _invoke(cfunc, *args):
+    if _recording is not None:
+        _recording.append((cfunc, args))
+        return
+    _check(cfunc(*args))
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -263,11 +288,11 @@ def planes(ids: torch.Tensor, cu_seqlens: torch.Tensor, marker_id: int = 248078,
                                         mk(seq_flags, "seq_flags"))
     ws = _workspace(workspace, L, dev)
     with _on_device(dev):
-        _check(load().mrope_planes(_ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), int(frame_len),
+        _invoke(load().mrope_planes, _ptr(ids), _ptr(cu_seqlens), n, L, int(marker_id), int(frame_len),
                                    _ptr(frame_len_seq), _ptr(pos_offset),
                                    _ptr(origin_in), _ptr(out), out.stride(0),
                                    _ptr(start), _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr,
-                                   ws.capacity, ws.next_epoch(), _stream(dev)))
+                                   ws.capacity, _epoch(ws), _stream(dev))
     return out, start, amount, origin, seq_flags
 
 
@@ -301,8 +326,8 @@ def apply(q: torch.Tensor, k: torch.Tensor | None, planes_: torch.Tensor, theta:
             or planes_.stride(1) != 1:
         raise ValueError("planes must be an int32 [3, >= tokens] tensor with unit column stride")
     with _on_device(dev):
-        _check(load().mrope_apply(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, _ptr(planes_),
-                                  planes_.stride(0), float(theta), _ptr(q_out), _ptr(k_out), _stream(dev)))
+        _invoke(load().mrope_apply, _ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, _ptr(planes_),
+                                  planes_.stride(0), float(theta), _ptr(q_out), _ptr(k_out), _stream(dev))
     return (q_out if q_out is not None else q), (k_out if k_out is not None else k)
 
 
@@ -335,11 +360,11 @@ def apply_ids(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor, cu_seq
                                         mk(seq_flags, "seq_flags"))
     ws = _workspace(workspace, T, dev)
     with _on_device(dev):
-        _check(load().mrope_apply_ids(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, float(theta),
+        _invoke(load().mrope_apply_ids, _ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt, float(theta),
                                       _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
                                       int(frame_len), _ptr(frame_len_seq), _ptr(pos_offset), _ptr(origin_in),
                                       _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
-                                      _ptr(seq_flags), ws.ptr, ws.capacity, ws.next_epoch(), _stream(dev)))
+                                      _ptr(seq_flags), ws.ptr, ws.capacity, _epoch(ws), _stream(dev))
     return start, amount, origin, seq_flags, planes_out
 
 
@@ -373,12 +398,12 @@ def apply_ids_noalloc(q: torch.Tensor, k: torch.Tensor | None, ids: torch.Tensor
     start, amount, origin, seq_flags = (mk(start, "start"), mk(amount, "amount"), mk(origin, "origin"),
                                         mk(seq_flags, "seq_flags"))
     with _on_device(dev):
-        _check(load().mrope_apply_ids_noalloc(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt,
+        _invoke(load().mrope_apply_ids_noalloc, _ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, T, D, rot_dim, dt,
                                               float(theta), _ptr(q_out), _ptr(k_out), _ptr(ids), _ptr(cu_seqlens), n,
                                               int(marker_id), int(frame_len), _ptr(frame_len_seq),
                                               _ptr(pos_offset), _ptr(origin_in),
                                               _ptr(planes_out), ps, _ptr(start), _ptr(amount), _ptr(origin),
-                                              _ptr(seq_flags), _stream(dev)))
+                                              _ptr(seq_flags), _stream(dev))
     return start, amount, origin, seq_flags, planes_out
 
 
@@ -444,8 +469,8 @@ def apply_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, planes_: 
     if check_slots:
         _slot_check(slot_mapping, k_cache.shape[0] * k_cache.shape[1])
     with _on_device(dev):
-        _check(load().mrope_apply_kv(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
-                                     _ptr(planes_), planes_.stride(0), float(theta), *cache, _stream(dev)))
+        _invoke(load().mrope_apply_kv, _ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
+                                     _ptr(planes_), planes_.stride(0), float(theta), *cache, _stream(dev))
     return q, k_cache, v_cache
 
 
@@ -482,12 +507,12 @@ def apply_ids_kv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None, ids: 
                                         mk(seq_flags, "seq_flags"))
     ws = _workspace(workspace, T, dev)
     with _on_device(dev):
-        _check(load().mrope_apply_ids_kv(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
+        _invoke(load().mrope_apply_ids_kv, _ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, T, D, rot_dim, dt,
                                          float(theta), _ptr(ids), _ptr(cu_seqlens), n, int(marker_id),
                                          int(frame_len), _ptr(frame_len_seq), _ptr(pos_offset), _ptr(origin_in),
                                          _ptr(planes_out), ps, _ptr(start),
                                          _ptr(amount), _ptr(origin), _ptr(seq_flags), ws.ptr, ws.capacity,
-                                         ws.next_epoch(), *cache, _stream(dev)))
+                                         _epoch(ws), *cache, _stream(dev))
     return start, amount, origin, seq_flags, planes_out
 
 
@@ -511,6 +536,68 @@ def decode(q: torch.Tensor, k: torch.Tensor | None, pos: torch.Tensor, amount: t
     else:
         (vt, vh), cache = (0, 0), (None, None, None, 1, 0, 0, 0, 0)
     with _on_device(dev):
-        _check(load().mrope_decode(_ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, S, _ptr(pos),
-                                   _ptr(amount), *cache, D, rot_dim, dt, float(theta), _stream(dev)))
+        _invoke(load().mrope_decode, _ptr(q), qt, qh, nq, _ptr(k), kt, kh, nk, _ptr(v), vt, vh, S, _ptr(pos),
+                                   _ptr(amount), *cache, D, rot_dim, dt, float(theta), _stream(dev))
     return q, k_cache
+
+
+class PreparedCall:
+    """One binding call with its arguments checked and marshalled once (see prepare()).  Calling it
+    launches the same C call again, on the stream and with the tensors bound at preparation; a call
+    with a workspace takes a fresh epoch each time.  `result` is what the binding function returned
+    (the same output tensors are written by every run)."""
+
+    __slots__ = ("_dev", "_calls", "result")
+
+    def __init__(self, dev, calls, result):
+        self._dev = dev
+        self._calls = []
+        for cfunc, args in calls:
+            # arguments as ctypes values of the declared types: ctypes then converts nothing per call
+            conv, slots = [], []
+            for t, a in zip(cfunc.argtypes, args):
+                if isinstance(a, _EpochSlot):
+                    slots.append((t(0), a.ws))
+                    conv.append(slots[-1][0])
+                elif a is None or isinstance(a, ctypes._SimpleCData):
+                    conv.append(a)
+                else:
+                    conv.append(t(a))
+            self._calls.append((cfunc, conv, slots))
+        self.result = result
+
+    def __call__(self):
+        with _on_device(self._dev):
+            for cfunc, args, slots in self._calls:
+                for cell, ws in slots:
+                    ws.calls = ws.calls % ((1 << 29) - 1) + 1
+                    cell.value = ws.calls
+                _check(cfunc(*args))
+        return self.result
+
+
+def prepare(fn, *args, **kwargs) -> PreparedCall:
+    """Check and marshal a call of one of this module's functions (planes, apply, apply_ids,
+    apply_ids_noalloc, apply_kv, apply_ids_kv, decode) once, without launching it, and return a
+    PreparedCall that launches it each time it is called -- for an eager loop that repeats a call on
+    the same buffers (a decode step), where the per-call argument checks would otherwise cost more
+    host time than the GPU work.  The stream current now is the one every run launches on.  Output
+    tensors the call would allocate are allocated here once.  The prepared call must not be run
+    inside HIP-graph capture (capture the plain call instead: its epochs come from the device)."""
+    global _recording
+    if _recording is not None:
+        raise RuntimeError("prepare() does not nest")
+    rec = []
+    _recording = rec
+    try:
+        result = fn(*args, **kwargs)
+    finally:
+        _recording = None
+    if not rec:
+        raise ValueError(f"{getattr(fn, '__name__', fn)} made no library call to prepare")
+    dev = None
+    for a in list(args) + list(kwargs.values()):
+        if isinstance(a, torch.Tensor) and a.is_cuda:
+            dev = a.device
+            break
+    return PreparedCall(dev, rec, result)
