@@ -491,9 +491,10 @@ def pattern_mode(args, dev, stream):
 
 
 def f32_mode(args, dev, stream):
-    """mrope_apply in fp32 on 64 x 4,096 image prompts in both lane layouts, interleaved: sixteen
-    lanes a token (the library's choice) and eight (the MROPE_HOOK_F32_EIGHT_LANES test hook).
-    Per-launch events, three rounds of `steps` launches after 5 untimed ones each."""
+    """mrope_apply (planes given) and mrope_apply_ids (planes from ids) in fp32 on 64 x 4,096 image
+    prompts in both lane layouts, interleaved: sixteen lanes a token (the library's choice) and
+    eight (the MROPE_HOOK_F32_EIGHT_LANES test hook).  Per-launch events, three rounds of `steps`
+    launches after 5 untimed ones each."""
     import numpy as np
     import torch
 
@@ -506,24 +507,32 @@ def f32_mode(args, dev, stream):
     q = torch.from_numpy(synth.to_f32(qn, "bf16")).to(dev)
     k = torch.from_numpy(synth.to_f32(kn, "bf16")).to(dev)
     del qn, kn
-    pl, *_ = mr.planes(torch.from_numpy(cfg.ids).to(dev), torch.from_numpy(cfg.cu_seqlens).to(dev), synth.IMAGE_ID)
-    byts = L * (10 * 64 * 4 * 2 + 12)
-    durs = {"sixteen_lanes": [], "eight_lanes": []}
+    ids = torch.from_numpy(cfg.ids).to(dev)
+    cu = torch.from_numpy(cfg.cu_seqlens).to(dev)
+    pl, *_ = mr.planes(ids, cu, synth.IMAGE_ID)
+    ws = mr.Workspace(L, dev)
+    calls = {"mrope_apply": (lambda: mr.apply(q, k, pl), L * (10 * 64 * 4 * 2 + 12)),
+             "mrope_apply_ids": (lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, workspace=ws),
+                                 L * (10 * 64 * 4 * 2 + 4))}
     hooks = {"sixteen_lanes": 0, "eight_lanes": _lib.HOOK_F32_EIGHT_LANES}
+    durs = {(c, h): [] for c in calls for h in hooks}
     prev = _lib.set_test_hooks(0)
     try:
         for rnd in range(3):
-            for name, hk in hooks.items():
-                _lib.set_test_hooks(hk)
-                for _ in range(5):
-                    mr.apply(q, k, pl)
-                d, _ = per_launch(lambda: mr.apply(q, k, pl), args.steps, stream)
-                durs[name] += d
+            for c, (fn, _) in calls.items():
+                for h, hk in hooks.items():
+                    _lib.set_test_hooks(hk)
+                    for _ in range(5):
+                        fn()
+                    d, _ = per_launch(fn, args.steps, stream)
+                    durs[(c, h)] += d
     finally:
         _lib.set_test_hooks(prev)
-    out = {name: dict(summary(d), gbs_p50=byts / pct(d, 0.5) / 1e9) for name, d in durs.items()}
+    out = {c: {h: dict(summary(durs[(c, h)]), gbs_p50=calls[c][1] / pct(durs[(c, h)], 0.5) / 1e9) for h in hooks}
+           for c in calls}
     print(json.dumps({"mode": "f32", "workload": "64 x 4,096 image prompts, fp32 Q[262144,8,256] and K[262144,2,256] "
-                      "in place, planes given", "algorithmic_bytes_per_launch": byts, "kernels": out}), flush=True)
+                      "in place", "algorithmic_bytes_per_launch": {c: v[1] for c, v in calls.items()},
+                      "kernels": out}), flush=True)
 
 
 KERNEL_CALLS = (  # rocprofv3 kernel name fragment -> the C entry point it serves

@@ -30,6 +30,7 @@
 // (nearest even).
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "mrope_internal.h"
 #include "mrope_math.h"
@@ -1299,10 +1300,21 @@ __global__ __launch_bounds__(kBlock) void planes_kernel(Scan sc, int64_t n_chunk
 // LDS while waves 1-3 issue the Q/K loads of their first token (wave 0 issues its own after the
 // scan), then the workgroup rotates its part 32 tokens at a time, each 8-lane group prefetching its
 // next token before rotating the current one.  KV as in apply_kernel (fixed head
-// counts); the generic path writes the cache when pc.k_cache is set.
-template <int IO, int NQ, int NK, bool KV, bool NTS>
+// counts); the generic path writes the cache when pc.k_cache is set.  W16: fp32 with sixteen lanes
+// a token (apply_f32w_kernel's layout), 16 tokens a step.
+template <bool W16>
+__device__ __forceinline__ auto fused_lane_freq(const Rotary &rot, int m, int half)
+{
+    if constexpr (W16) return lane_freq2(rot, m, half);
+    else return lane_freq<true>(rot, m, half);
+}
+
+template <int IO, int NQ, int NK, bool KV, bool NTS, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, PagedKV pc, int part_log)
 {
+    static_assert(!W16 || (IO == kIoF32 && NQ > 0 && NK > 0 && !KV), "sixteen lanes: fp32, fixed heads, no cache");
+    constexpr int kLanes = W16 ? kLanesW : kLanesPerTok;
+    constexpr int kStep = kBlock / kLanes;  // tokens a workgroup step
     __shared__ int32_t s_pl[3][kChunk];
     __shared__ uint64_t s_ok[kSub];
     __shared__ int64_t s_seq[3];  // a chunk inside one sequence: [1] = its begin; [0] = its offset | origin << 32;
@@ -1310,9 +1322,9 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     __shared__ int32_t s_single;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int l = tid & 7, m = l >> 1, half = l & 1;
-    const int e0 = 32 * half + 8 * m;
-    const LaneFreq lf = lane_freq<true>(rot, m, half);
+    const int l = tid & (kLanes - 1), m = l >> 1, half = l & 1;
+    const int e0 = 32 * half + (W16 ? 4 : 8) * m;
+    const auto lf = fused_lane_freq<W16>(rot, m, half);
     const int64_t chunk = (int64_t)(blockIdx.x >> part_log);
     const int64_t c0 = chunk * kChunk;
     const int64_t c_end = min<int64_t>(c0 + kChunk, hd.n_tokens);
@@ -1330,10 +1342,13 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     // include those loads (1 x 4096 tokens 17.8 -> 17.2 us, 4 x 4096 28.4 -> 25.7).  Issued early,
     // 8 x 32768 tokens took 122 us instead of 118: with long sequences a chunk's look-back waits on
     // its predecessors' look-backs, and each waited behind its wave 0's loads.
-    int64_t g = r0 + (tid >> 3);
-    Raw8<IO> qv[AQ], kv[AK];
+    int64_t g = r0 + tid / kLanes;
+    using TokReg = std::conditional_t<W16, uint4, Raw8<IO>>;
+    TokReg qv[AQ], kv[AK];
     auto prologue = [&]() {
-        if constexpr (kFixed && !KV) {
+        if constexpr (W16) {
+            if (g < r_end) load_token_w<AQ, AK>(hd, g, e0, qv, kv);
+        } else if constexpr (kFixed && !KV) {
             if (g < r_end) load_token_fixed<IO, AQ, AK>(hd, g, e0, qv, kv);
         }
     };
@@ -1410,13 +1425,30 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         }
     };
 
-    while (g < r_end) {  // the eight lanes of a token stay together
+    while (g < r_end) {  // the lanes of a token stay together
         bool ok;
         int32_t pt, ph, pw;
         planes_of(g, ok, pt, ph, pw);
-        const int64_t gn = g + kTokPerBlock;
+        const int64_t gn = g + kStep;
         double c[8], ss[8];
-        if constexpr (kFixed && KV) {
+        if constexpr (W16) {
+            uint4 qn[AQ], kn[AK];
+            if (gn < r_end) load_token_w<AQ, AK>(hd, gn, e0, qn, kn);
+            if (ok) {
+                double c4[4], ss4[4];
+                pair_sincos4(lf, pt, ph, pw, c4, ss4);
+                void *qo = hd.q_out ? hd.q_out : hd.q;
+                void *ko = hd.k_out ? hd.k_out : hd.k;
+#pragma unroll
+                for (int h = 0; h < AQ; ++h) store16_as<NTS>(qo, q_off(hd, g, h) + e0, rotate4(qv[h], c4, ss4));
+#pragma unroll
+                for (int h = 0; h < AK; ++h) store16_as<NTS>(ko, k_off(hd, g, h) + e0, rotate4(kv[h], c4, ss4));
+            }
+#pragma unroll
+            for (int h = 0; h < AQ; ++h) qv[h] = qn[h];
+#pragma unroll
+            for (int h = 0; h < AK; ++h) kv[h] = kn[h];
+        } else if constexpr (kFixed && KV) {
             if (ok) kv_token<IO, AQ, AK, NTS>(hd, pc, lf, g, e0, l, pt, ph, pw, pc.slots[g]);
         } else if constexpr (kFixed) {
             Raw8<IO> qn[AQ], kn[AK];
@@ -1979,6 +2011,13 @@ static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan
             if (pc.k_cache) {
                 if (nts) apply_ids_kernel<IO, 8, 2, true, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
                 else apply_ids_kernel<IO, 8, 2, true, false><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+                done = true;
+            }
+        }
+        if constexpr (IO == kIoF32) {
+            if (!done && !(test_hooks() & kHookF32EightLanes)) {
+                if (nts) apply_ids_kernel<IO, 8, 2, false, true, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+                else apply_ids_kernel<IO, 8, 2, false, false, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
                 done = true;
             }
         }

@@ -1,5 +1,5 @@
-"""GPU parity of mrope_apply in fp32 in both lane layouts: sixteen lanes a token (the default) and
-eight (MROPE_HOOK_F32_EIGHT_LANES).  Each is compared with the oracle (fp32 gate) and with the other
+"""GPU parity of mrope_apply and of the chunked fused mrope_apply_ids in fp32 in both lane layouts:
+sixteen lanes a token (the default) and eight (MROPE_HOOK_F32_EIGHT_LANES).  Each is compared with the oracle (fp32 gate) and with the other
 bit for bit, in place and out of place, on strided views, and past the size from which in-place
 stores take the non-temporal hint."""
 import numpy as np
@@ -88,3 +88,29 @@ def test_f32_sixteen_lanes_past_the_store_hint_size():
     mr.apply(q, k, pl)
     compare_heads_all(q, qn, epl, "f32", what="q")
     compare_heads_all(k, kn, epl, "f32", what="k")
+
+
+@pytest.mark.parametrize("seed,n_seqs,max_len", [(631, 1, 110), (632, 40, 900), (633, 6, 4096)])
+@pytest.mark.parametrize("planes_out", [False, True])
+def test_f32_fused_layouts_match_oracle_and_each_other(seed, n_seqs, max_len, planes_out):
+    """The chunked fused kernel (up to 262,144 tokens): planes from ids, then the rotation in either
+    layout; chunks inside one sequence (handover) and shared by several (LDS planes)."""
+    b = synth.random_batch(seed, n_seqs, max_len=max_len, min_len=max_len if n_seqs == 1 else 1, dtype="f32")
+    qn, kn = b.qk()
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    say(f"case: fp32 fused layouts seed={seed} tokens={b.n_tokens} planes_out={planes_out}")
+
+    def run():
+        q, k = dev_heads(qn, "f32"), dev_heads(kn, "f32")
+        pl = torch.full((3, b.n_tokens), -7, dtype=torch.int32, device="cuda") if planes_out else None
+        mr.apply_ids(q, k, i32(b.ids), i32(b.cu_seqlens), MARKER, planes_out=pl)
+        if planes_out:
+            np.testing.assert_array_equal(pl.cpu().numpy(), epl)
+        return host_heads(q), host_heads(k)
+
+    res = _both_layouts(run)
+    for name, (q, k) in res.items():
+        compare_heads(q, qn, epl, "f32", what=f"fused {name} q")
+        compare_heads(k, kn, epl, "f32", what=f"fused {name} k")
+    for a, c in zip(res["sixteen"], res["eight"]):
+        np.testing.assert_array_equal(a.view(np.uint32), c.view(np.uint32))
