@@ -1658,10 +1658,11 @@ __device__ __forceinline__ void sf_block_role(int64_t b, int64_t n_scan, int64_t
     idx = ng * kPartsPerScanBlock + (u - ng * span);
 }
 
-template <int IO, bool NTS>
+template <int IO, bool NTS, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void apply_ids_sf_kernel(Heads hd, Rotary rot, Scan sc, int64_t n_scan_blocks,
                                                               int64_t lead, int hooks)
 {
+    static_assert(!W16 || IO == kIoF32, "sixteen lanes: fp32");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const uint32_t ep = launch_epoch(sc);
@@ -1676,6 +1677,41 @@ __global__ __launch_bounds__(kBlock) void apply_ids_sf_kernel(Heads hd, Rotary r
         return;
     }
     const int64_t part = idx;
+    if constexpr (W16) {
+        // fp32 with sixteen lanes a token (apply_f32w_kernel's layout): the part in two 16-token
+        // steps, both steps' Q/K loads issued before the handover is read; each wave takes tokens
+        // [G, G + 4) of a step
+        const int l = tid & 15, m = l >> 1, half = l & 1;
+        const int e0 = 32 * half + 4 * m;
+        const int64_t G0 = part * kPartTokens + (tid >> 6) * 4;
+        const int64_t g0 = G0 + ((tid & 63) >> 4);
+        uint4 qv[2][8], kv[2][2];
+        bool ok[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            ok[st] = g0 + 16 * st < hd.n_tokens;
+            if (ok[st]) load_token_w<8, 2>(hd, g0 + 16 * st, e0, qv[st], kv[st]);
+        }
+        const LaneFreq2 lf = lane_freq2(rot, m, half);
+        void *qo = hd.q_out ? hd.q_out : hd.q;
+        void *ko = hd.k_out ? hd.k_out : hd.k;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int64_t G = G0 + 16 * st, g = g0 + 16 * st;
+            if (G >= hd.n_tokens) break;  // wave-uniform
+            int32_t pt, ph, pw;
+            sf_planes(sc, ep, lane, G, g, ok[st], !rot_first, pt, ph, pw);
+            if (ok[st]) {
+                double c[4], ss[4];
+                pair_sincos4(lf, pt, ph, pw, c, ss);
+#pragma unroll
+                for (int h = 0; h < 8; ++h) store16_as<NTS>(qo, q_off(hd, g, h) + e0, rotate4(qv[st][h], c, ss));
+#pragma unroll
+                for (int h = 0; h < 2; ++h) store16_as<NTS>(ko, k_off(hd, g, h) + e0, rotate4(kv[st][h], c, ss));
+            }
+        }
+        return;
+    }
     const int l = tid & 7, m = l >> 1, half = l & 1;
     const int e0 = 32 * half + 8 * m;
     const int64_t G = part * kPartTokens + (tid >> 6) * 8;  // the wave's first token
@@ -2049,12 +2085,21 @@ static hipError_t apply_ids_sf_dispatch(const Heads &h, const Rotary &r, const S
     const int64_t rot_blocks = (hooks & kHookScanFallback) ? n_parts
                                                            : std::max(n_parts, (n_scan - lead) * kPartsPerScanBlock);
     const unsigned blocks = (unsigned)(n_scan + rot_blocks);
-    // Two workgroups per CU: the kernel needs 127 VGPRs (four could be resident), but more
+    // Two workgroups per CU: the kernel needs 141 VGPRs (three could be resident), but more
     // concurrent 32-token parts make the HBM stream slower.  Measured on 1,048,576 ragged tokens:
     // 480 us at four workgroups per CU, 476 at three, 468 at two (mrope_apply, two by its registers:
     // 467), 680 at one.  The unused dynamic LDS holds the occupancy there.
     constexpr unsigned kOccupancyLds = 64 << 10;
-    if (nt_stores<IO>(h, PagedKV{}))
+    const bool nts = nt_stores<IO>(h, PagedKV{});
+    if constexpr (IO == kIoF32) {
+        if (!(hooks & kHookF32EightLanes)) {
+            if (nts) apply_ids_sf_kernel<IO, true, true><<<blocks, kBlock, kOccupancyLds, st>>>(h, r, s, n_scan, lead, hooks);
+            else apply_ids_sf_kernel<IO, false, true><<<blocks, kBlock, kOccupancyLds, st>>>(h, r, s, n_scan, lead, hooks);
+            const hipError_t e = hipGetLastError();
+            return e != hipSuccess ? e : bump_if_device_epoch(s, st);
+        }
+    }
+    if (nts)
         apply_ids_sf_kernel<IO, true><<<blocks, kBlock, kOccupancyLds, st>>>(h, r, s, n_scan, lead, hooks);
     else
         apply_ids_sf_kernel<IO, false><<<blocks, kBlock, kOccupancyLds, st>>>(h, r, s, n_scan, lead, hooks);

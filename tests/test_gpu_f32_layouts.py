@@ -16,10 +16,10 @@ pytestmark = pytest.mark.gpu
 LAYOUTS = {"sixteen": 0, "eight": _lib.HOOK_F32_EIGHT_LANES}
 
 
-def _both_layouts(run):
+def _both_layouts(run, extra_hooks=0):
     out = {}
     for name, hook in LAYOUTS.items():
-        prev = _lib.set_test_hooks(hook)
+        prev = _lib.set_test_hooks(hook | extra_hooks)
         try:
             out[name] = run()
         finally:
@@ -92,13 +92,15 @@ def test_f32_sixteen_lanes_past_the_store_hint_size():
 
 @pytest.mark.parametrize("seed,n_seqs,max_len", [(631, 1, 110), (632, 40, 900), (633, 6, 4096)])
 @pytest.mark.parametrize("planes_out", [False, True])
-def test_f32_fused_layouts_match_oracle_and_each_other(seed, n_seqs, max_len, planes_out):
-    """The chunked fused kernel (up to 262,144 tokens): planes from ids, then the rotation in either
-    layout; chunks inside one sequence (handover) and shared by several (LDS planes)."""
+@pytest.mark.parametrize("kernel", ["chunked", "scan_first"])
+def test_f32_fused_layouts_match_oracle_and_each_other(seed, n_seqs, max_len, planes_out, kernel):
+    """The fused kernels -- chunked (up to 262,144 tokens) and scan-first (past it; forced here by its
+    test hook) -- in either layout: chunks inside one sequence and shared by several, parts handed
+    over whole and token by token."""
     b = synth.random_batch(seed, n_seqs, max_len=max_len, min_len=max_len if n_seqs == 1 else 1, dtype="f32")
     qn, kn = b.qk()
     epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
-    say(f"case: fp32 fused layouts seed={seed} tokens={b.n_tokens} planes_out={planes_out}")
+    say(f"case: fp32 fused {kernel} layouts seed={seed} tokens={b.n_tokens} planes_out={planes_out}")
 
     def run():
         q, k = dev_heads(qn, "f32"), dev_heads(kn, "f32")
@@ -108,9 +110,9 @@ def test_f32_fused_layouts_match_oracle_and_each_other(seed, n_seqs, max_len, pl
             np.testing.assert_array_equal(pl.cpu().numpy(), epl)
         return host_heads(q), host_heads(k)
 
-    res = _both_layouts(run)
+    res = _both_layouts(run, _lib.HOOK_FUSED_SCAN_FIRST if kernel == "scan_first" else _lib.HOOK_FUSED_CHUNKED)
     for name, (q, k) in res.items():
-        compare_heads(q, qn, epl, "f32", what=f"fused {name} q")
-        compare_heads(k, kn, epl, "f32", what=f"fused {name} k")
+        compare_heads(q, qn, epl, "f32", what=f"fused {kernel} {name} q")
+        compare_heads(k, kn, epl, "f32", what=f"fused {kernel} {name} k")
     for a, c in zip(res["sixteen"], res["eight"]):
         np.testing.assert_array_equal(a.view(np.uint32), c.view(np.uint32))
