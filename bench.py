@@ -36,6 +36,10 @@ HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 PATTERN_LIB = os.path.join(ROOT, "bench_pattern.so")
 WORKLOADS = {
+    1: "one image prompt, L = 110 (O = 6), fp32: planes from int32 ids + in-place rotary of Q[110,8,256] and "
+       "K[110,2,256], one call",
+    4: "decode step of 4096 sequences (p ~ U{100..32000}, amount 58), bf16: Q[4096,8,256] rotated in place, "
+       "K[4096,2,256] rotated and written whole into a 1 GiB paged cache of 16-token blocks",
     5: "1,048,576 ragged tokens (log-uniform lengths 64..16384, half text-only, half one image frame), bf16: "
        "planes from int32 ids + in-place rotary of Q[1048576,8,256] and K[1048576,2,256], one call",
     3: "8 prompts x 32768 tokens, one image frame each, bf16: planes from int32 ids + in-place rotary of "
@@ -535,6 +539,97 @@ def f32_mode(args, dev, stream):
                       "kernels": out}), flush=True)
 
 
+def small_config_bench(args, dev, stream):
+    """Configs 1 (one fp32 image prompt through mrope_apply_ids) and 4 (a decode step of 4,096
+    sequences): launch- and latency-bound steps, shorter than the host's time to launch them, so
+    `warmup` steps and then `steps` steps are captured in two HIP graphs; the timed region replays
+    the second once (events around it: GPU time per step, the graph's per-node launch included)."""
+    import numpy as np
+    import torch
+
+    import canvas_rope_rotary_amd as mr
+    import oracle
+    from canvas_rope_rotary_amd import synth
+
+    if args.config == 1:
+        cfg = synth.config1()
+        qn, kn = cfg.qk()
+        q, k = torch.from_numpy(qn).to(dev), torch.from_numpy(kn).to(dev)
+        ids = torch.from_numpy(cfg.ids).to(dev)
+        cu = torch.from_numpy(cfg.cu_seqlens).to(dev)
+        ws = mr.Workspace(cfg.n_tokens, dev)
+        outs = [torch.empty(cfg.n_seqs, dtype=torch.int32, device=dev) for _ in range(4)]
+        step = lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, start=outs[0], amount=outs[1], origin=outs[2],
+                                    seq_flags=outs[3], workspace=ws)
+        tokens, byts, kernel, io = cfg.n_tokens, cfg.n_tokens * (10 * 64 * 4 * 2 + 4), "mrope_apply_ids", "f32"
+        extra = {"tokens": cfg.n_tokens, "seqs": cfg.n_seqs}
+    else:
+        d = synth.config4()
+        qn, kn = d.qk()
+        q = torch.from_numpy(qn.view(np.int16)).view(torch.bfloat16).to(dev)
+        k = torch.from_numpy(kn.view(np.int16)).view(torch.bfloat16).to(dev)
+        cache = torch.zeros((d.num_blocks, d.block_size, d.n_k_heads, d.head_dim), dtype=torch.bfloat16, device=dev)
+        pos, amount = torch.from_numpy(d.pos).to(dev), torch.from_numpy(d.amount).to(dev)
+        slots = torch.from_numpy(d.slot_mapping).to(dev)
+        step = lambda: mr.decode(q, k, pos, amount, cache, slots)
+        tokens, kernel, io = d.n_seqs, "mrope_decode", "bf16"
+        byts = d.n_seqs * (8 * 64 * 2 * 2 + 2 * 256 * 2 * 2 + 4 + 4 + 8)
+        extra = {"seqs": d.n_seqs, "cache_blocks": d.num_blocks, "block_size": d.block_size}
+    # capture one step (its first run, on a side stream, outside the capture)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gw, g = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for _ in range(max(args.warmup, 1)):
+            step()
+    with torch.cuda.graph(g):
+        for _ in range(args.steps):
+            step()
+    gw.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    achieved = byts / us / 1e3
+    out = {
+        "metric": METRIC, "value": tokens / (us / 1e6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "io_dtype": io, "angle_dtype": "f32", "data": "synthetic",
+        "config": dict({"workload": WORKLOADS[args.config]}, **extra),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kernel,
+                     "algorithmic_bytes_per_launch": byts,
+                     "note": "launch- and latency-bound: GPU time per step of a replayed graph of `steps` steps"},
+    }
+    if not args.no_cpu_baseline:
+        if args.config == 4:
+            ref = np.zeros((d.num_blocks, d.block_size, d.n_k_heads, d.head_dim), np.float32)
+            qf, kf = synth.to_f32(qn, "bf16"), synth.to_f32(kn, "bf16")
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            if args.config == 1:
+                pl, *_ = oracle.planes(cfg.ids, cfg.cu_seqlens, synth.IMAGE_ID)
+                oracle.rotate(np.concatenate([qn, kn], axis=1), pl)
+            else:
+                oracle.decode(qf, kf, d.pos, d.amount, ref, d.slot_mapping, d.block_size)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 5.0) and passes >= 3:
+                break
+        out["cpu_baseline"] = {"value": tokens * passes / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole step, {passes} passes in {el:.1f} s, one thread",
+                               "cpu": host_cpu_model()}
+    print(json.dumps(out), flush=True)
+
+
 KERNEL_CALLS = (  # rocprofv3 kernel name fragment -> the C entry point it serves
     ("apply_ids_sf_kernel", "mrope_apply_ids"),
     ("apply_ids_kernel", "mrope_apply_ids"),
@@ -627,8 +722,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, choices=(2, 3, 5), default=5,
-                    help="headline workload: 5 = 1,048,576 ragged tokens (default), 3 = 8 x 32768, 2 = 64 x 4096")
+    ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=5,
+                    help="workload: 5 = 1,048,576 ragged tokens (default), 3 = 8 x 32768, 2 = 64 x 4096, "
+                         "1 = one fp32 image prompt of 110 tokens, 4 = a decode step of 4096 sequences")
     ap.add_argument("--cold-reps", type=int, default=20, help="cache-cold single launches (0: none)")
     ap.add_argument("--settle-s", type=float, default=0.25,
                     help="untimed step launches for this many seconds before the warmup steps")
@@ -683,6 +779,9 @@ def main():
         return
     if args.mode == "f32":
         f32_mode(args, dev, stream)
+        return
+    if args.config in (1, 4):
+        small_config_bench(args, dev, stream)
         return
 
     cfg = synth.CONFIGS[args.config]()
