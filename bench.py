@@ -427,7 +427,9 @@ def pattern_mode(args, dev, stream):
     """The rotary kernels of one workload beside reference kernels that move the same bytes with no
     rotary arithmetic (bench_pattern.hip): the first 128 B of every 512 B head of ten heads a token
     read only, written only, and read and written in place, plus dense reads, writes and a copy of
-    that byte count.  Each kernel is timed per launch (events) in three interleaved rounds."""
+    that byte count; the in-place pass and the copy also in the lane maps that stream them fastest
+    (a (token, head) piece per eight lanes in single-wave workgroups; one 16-byte vector per lane).
+    Each kernel is timed per launch (events) in three interleaved rounds."""
     import ctypes
 
     import torch
@@ -467,6 +469,8 @@ def pattern_mode(args, dev, stream):
         ("dense_read", kernel(3, src, None, nb), nb),
         ("dense_write", kernel(4, dst, None, nb), nb),
         ("dense_copy", kernel(5, src, dst, nb), 2 * nb),
+        ("sparse_read_write_piece_waves", kernel(6, heads, None, L), 2 * nb),
+        ("dense_copy_one_vector_per_lane", kernel(7, src, dst, nb), 2 * nb),
         ("mrope_apply", b.apply, algorithmic_bytes_apply(L)),
         ("mrope_apply_ids", b.fused, algorithmic_bytes_fused(L)),
     ]

@@ -87,21 +87,47 @@ __global__ __launch_bounds__(kBlock) void dense_copy(const u32x4 *src, u32x4 *ds
         if (base + j * kBlock < n) __builtin_nontemporal_store(v[j], dst + base + j * kBlock);
 }
 
+// The same in-place pattern with another lane map: eight lanes on one 128-byte (token, head) piece,
+// eight pieces -- consecutive in (token, head) order -- per single-wave workgroup.  Of the lane maps
+// and occupancies tried for a plain read + write pass over the pattern, this one streams fastest.
+__global__ __launch_bounds__(64) void sparse_rw_pieces(u32x4 *buf, int64_t pieces, uint32_t magic)
+{
+    const int64_t c = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 3);
+    if (c >= pieces) return;
+    u32x4 *p = buf + (c / kHeads) * kHeads * kHeadVec + (c % kHeads) * kHeadVec + (threadIdx.x & 7);
+    const u32x4 v = __builtin_nontemporal_load(p);
+    const u32x4 m = {magic, magic, magic, magic};
+    __builtin_nontemporal_store(v ^ m, p);
+}
+
+// Dense copy with one 16-byte vector per lane.
+__global__ __launch_bounds__(kBlock) void dense_copy_v1(const u32x4 *src, u32x4 *dst, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 }  // namespace
 
 // kind: 0 sparse read, 1 sparse write, 2 sparse read + write in place (a: [n tokens][10][512 B]);
-//       3 dense read of a, 4 dense write of a, 5 dense copy a -> b (n bytes, a multiple of 16).
+//       3 dense read of a, 4 dense write of a, 5 dense copy a -> b (n bytes, a multiple of 16);
+//       6 as 2 with a (token, head) piece per eight lanes and single-wave workgroups;
+//       7 as 5 with one 16-byte vector per lane.
 // sink: 64 words of device memory the read kernels may write.  Returns a hipError_t.
 extern "C" int pattern_launch(int kind, void *a, void *b, int64_t n, uint32_t magic, void *sink, void *stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n <= 0 || !a) return (int)hipErrorInvalidValue;
+    if (kind < 0 || kind > 7) return (int)hipErrorInvalidValue;
     if (kind <= 2) {
         const unsigned blocks = (unsigned)((n + kBlock / 8 - 1) / (kBlock / 8));
         u32x4 *p = static_cast<u32x4 *>(a);
         if (kind == 0) sparse_read<<<blocks, kBlock, 0, s>>>(p, n, magic, static_cast<uint32_t *>(sink));
         if (kind == 1) sparse_write<<<blocks, kBlock, 0, s>>>(p, n, magic);
         if (kind == 2) sparse_rw<<<blocks, kBlock, 0, s>>>(p, n, magic);
+    } else if (kind == 6) {
+        const int64_t pieces = n * kHeads;
+        sparse_rw_pieces<<<(unsigned)((pieces + 7) / 8), 64, 0, s>>>(static_cast<u32x4 *>(a), pieces, magic);
     } else {
         if (n % 16) return (int)hipErrorInvalidValue;
         const int64_t v = n / 16;
@@ -109,9 +135,10 @@ extern "C" int pattern_launch(int kind, void *a, void *b, int64_t n, uint32_t ma
         u32x4 *p = static_cast<u32x4 *>(a);
         if (kind == 3) dense_read<<<blocks, kBlock, 0, s>>>(p, v, magic, static_cast<uint32_t *>(sink));
         if (kind == 4) dense_write<<<blocks, kBlock, 0, s>>>(p, v, magic);
-        if (kind == 5) {
+        if (kind == 5 || kind == 7) {
             if (!b) return (int)hipErrorInvalidValue;
-            dense_copy<<<blocks, kBlock, 0, s>>>(p, static_cast<u32x4 *>(b), v);
+            if (kind == 5) dense_copy<<<blocks, kBlock, 0, s>>>(p, static_cast<u32x4 *>(b), v);
+            else dense_copy_v1<<<(unsigned)((v + kBlock - 1) / kBlock), kBlock, 0, s>>>(p, static_cast<u32x4 *>(b), v);
         }
     }
     return (int)hipGetLastError();
