@@ -499,9 +499,11 @@ def pattern_mode(args, dev, stream):
 
 
 def f32_mode(args, dev, stream):
-    """mrope_apply (planes given) and mrope_apply_ids (planes from ids) in fp32 on 64 x 4,096 image
-    prompts in both lane layouts, interleaved: sixteen lanes a token (the library's choice) and
-    eight (the MROPE_HOOK_F32_EIGHT_LANES test hook).  Per-launch events, three rounds of `steps`
+    """mrope_apply (planes given), mrope_apply_ids (planes from ids) and the cache-writing calls
+    (mrope_apply_kv, mrope_apply_ids_kv: K rotated and V copied into 16-token paged caches through a
+    random permutation of slots) in fp32 on 64 x 4,096 image prompts in both lane layouts,
+    interleaved: sixteen lanes a token (the library's choice) and eight (the MROPE_HOOK_F32_EIGHT_LANES
+    test hook; for the cache writes, the generic kernels).  Per-launch events, three rounds of `steps`
     launches after 5 untimed ones each."""
     import numpy as np
     import torch
@@ -519,9 +521,19 @@ def f32_mode(args, dev, stream):
     cu = torch.from_numpy(cfg.cu_seqlens).to(dev)
     pl, *_ = mr.planes(ids, cu, synth.IMAGE_ID)
     ws = mr.Workspace(L, dev)
+    vh = torch.from_numpy(np.asarray(synth.normal(cfg.seed, 77, L * 2 * 256), np.float32)).view(L, 2, 256).to(dev)
+    kc = torch.zeros((L // 16, 16, 2, 256), dtype=torch.float32, device=dev)
+    vc = torch.zeros_like(kc)
+    slots = torch.from_numpy(np.random.default_rng(cfg.seed).permutation(L).astype(np.int64)).to(dev)
+    # cache writes per token: Q's rotated dims read and written, K and V heads read whole and
+    # written whole into the cache, the slot, and the planes (12 B) or the id (4 B)
+    kv_bytes = 8 * 64 * 4 * 2 + 2 * (2 * 256 * 4) * 2 + 8
     calls = {"mrope_apply": (lambda: mr.apply(q, k, pl), L * (10 * 64 * 4 * 2 + 12)),
              "mrope_apply_ids": (lambda: mr.apply_ids(q, k, ids, cu, synth.IMAGE_ID, workspace=ws),
-                                 L * (10 * 64 * 4 * 2 + 4))}
+                                 L * (10 * 64 * 4 * 2 + 4)),
+             "mrope_apply_kv": (lambda: mr.apply_kv(q, k, vh, pl, kc, vc, slots), L * (kv_bytes + 12)),
+             "mrope_apply_ids_kv": (lambda: mr.apply_ids_kv(q, k, vh, ids, cu, kc, vc, slots, synth.IMAGE_ID,
+                                                            workspace=ws), L * (kv_bytes + 4))}
     hooks = {"sixteen_lanes": 0, "eight_lanes": _lib.HOOK_F32_EIGHT_LANES}
     durs = {(c, h): [] for c in calls for h in hooks}
     prev = _lib.set_test_hooks(0)
@@ -539,7 +551,8 @@ def f32_mode(args, dev, stream):
     out = {c: {h: dict(summary(durs[(c, h)]), gbs_p50=calls[c][1] / pct(durs[(c, h)], 0.5) / 1e9) for h in hooks}
            for c in calls}
     print(json.dumps({"mode": "f32", "workload": "64 x 4,096 image prompts, fp32 Q[262144,8,256] and K[262144,2,256] "
-                      "in place", "algorithmic_bytes_per_launch": {c: v[1] for c, v in calls.items()},
+                      "in place; the cache writes with V[262144,2,256] into 16-token paged K/V caches",
+                      "algorithmic_bytes_per_launch": {c: v[1] for c, v in calls.items()},
                       "kernels": out}), flush=True)
 
 

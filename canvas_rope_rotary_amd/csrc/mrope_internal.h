@@ -85,7 +85,7 @@ struct Scan {
 constexpr int kHookFusedChunked = 1;   // always the chunk-per-workgroup fused kernel
 constexpr int kHookFusedScanFirst = 2; // always the scan-first fused kernel (8 Q + 2 K heads)
 constexpr int kHookScanFallback = 4;   // scan-first: rotation workgroups first, no waiting
-constexpr int kHookF32EightLanes = 8;  // mrope_apply in fp32: the eight-lane kernel, not sixteen lanes
+constexpr int kHookF32EightLanes = 8;  // fp32: the eight-lane (or generic cache-writing) kernels, not sixteen lanes
 int test_hooks();
 
 // Paged K/V cache destination.  Element (block, row, head, d) of either cache is at

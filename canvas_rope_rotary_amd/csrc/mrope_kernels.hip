@@ -1204,6 +1204,75 @@ __global__ __launch_bounds__(kBlock) void apply_kv_kernel(Heads hd, Rotary rot, 
     }
 }
 
+// fp32 cache writes with sixteen lanes a token (fixed head counts, head_dim 256): lane l = 2m + half
+// holds dims [32 half + 4m, 32 half + 4m + 4) of every rotated head, as in apply_f32w_kernel; a K
+// head's pass-through dims (64..255, 48 16-byte vectors) and a V head (64 vectors) go as every
+// sixteenth vector, so each instruction of a token's sixteen lanes covers 256 contiguous bytes.  Per
+// lane: 8 Q + 2 K rotation vectors, 6 K pass-through and 8 V -- the 24 16-byte loads a lane of the
+// 16-bit kernel issues (kv_token) -- all in flight before the math.
+template <int NK>
+struct CopyChunksW {
+    uint4 k[NK][3];
+    uint4 v[NK][4];
+};
+
+template <int NQ, int NK, bool NTS>
+__device__ __forceinline__ void kv_token_w(const Heads &hd, const PagedKV &pc, const LaneFreq2 &lf, int64_t g, int e0,
+                                           int l, int32_t pt, int32_t ph, int32_t pw, int64_t slot)
+{
+    uint4 qv[NQ], kv[NK];
+    CopyChunksW<NK> cc;
+    load_token_w<NQ, NK>(hd, g, e0, qv, kv);
+    const float *kp = static_cast<const float *>(hd.k);
+#pragma unroll
+    for (int h = 0; h < NK; ++h)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) cc.k[h][i] = load16_nt(kp + k_off(hd, g, h) + 64 + 4 * (l + 16 * i));
+    if (pc.v) {
+        const float *vp = static_cast<const float *>(pc.v);
+#pragma unroll
+        for (int h = 0; h < NK; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cc.v[h][i] = load16_nt(vp + v_off(pc, g, h) + 4 * (l + 16 * i));
+    }
+    double c[4], ss[4];
+    pair_sincos4(lf, pt, ph, pw, c, ss);
+    void *qo = hd.q_out ? hd.q_out : hd.q;
+#pragma unroll
+    for (int h = 0; h < NQ; ++h) store16_as<NTS>(qo, q_off(hd, g, h) + e0, rotate4(qv[h], c, ss));
+    if (!slot_ok(pc, slot)) return;
+#pragma unroll
+    for (int h = 0; h < NK; ++h) {
+        const int64_t o = cache_off(pc, slot, h);
+        store16_as<true>(pc.k_cache, o + e0, rotate4(kv[h], c, ss));
+#pragma unroll
+        for (int i = 0; i < 3; ++i) store16_as<true>(pc.k_cache, o + 64 + 4 * (l + 16 * i), cc.k[h][i]);
+        if (pc.v) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) store16_as<true>(pc.v_cache, o + 4 * (l + 16 * i), cc.v[h][i]);
+        }
+    }
+}
+
+// mrope_apply_kv in fp32, fixed head counts: a grid-stride loop over 4-token groups (16 tokens a
+// workgroup step) like apply_kv_kernel.
+template <int NQ, int NK, bool NTS>
+__global__ __launch_bounds__(kBlock) void apply_kv_f32w_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
+                                                               int64_t ps, PagedKV pc)
+{
+    const int tid = threadIdx.x;
+    const int l = tid & 15, m = l >> 1, half = l & 1;
+    const int e0 = 32 * half + 4 * m;
+    const LaneFreq2 lf = lane_freq2(rot, m, half);
+    const int64_t stride = (int64_t)gridDim.x * kTokPerBlockW;
+    const int sub = (tid & 63) >> 4;
+    for (int64_t G = (int64_t)blockIdx.x * kTokPerBlockW + (tid >> 6) * 4; G < hd.n_tokens; G += stride) {
+        const int64_t g = G + sub;
+        if (g < hd.n_tokens)
+            kv_token_w<NQ, NK, NTS>(hd, pc, lf, g, e0, l, planes[g], planes[ps + g], planes[2 * ps + g], pc.slots[g]);
+    }
+}
+
 // Any head counts and head_dim: one token per 8-lane group, one head at a time.
 template <int IO>
 __global__ __launch_bounds__(kBlock) void apply_any_kernel(Heads hd, Rotary rot, const int32_t *__restrict__ planes,
@@ -1312,7 +1381,7 @@ __device__ __forceinline__ auto fused_lane_freq(const Rotary &rot, int m, int ha
 template <int IO, int NQ, int NK, bool KV, bool NTS, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot, Scan sc, PagedKV pc, int part_log)
 {
-    static_assert(!W16 || (IO == kIoF32 && NQ > 0 && NK > 0 && !KV), "sixteen lanes: fp32, fixed heads, no cache");
+    static_assert(!W16 || (IO == kIoF32 && NQ > 0 && NK > 0), "sixteen lanes: fp32, fixed heads");
     constexpr int kLanes = W16 ? kLanesW : kLanesPerTok;
     constexpr int kStep = kBlock / kLanes;  // tokens a workgroup step
     __shared__ int32_t s_pl[3][kChunk];
@@ -1346,7 +1415,7 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
     using TokReg = std::conditional_t<W16, uint4, Raw8<IO>>;
     TokReg qv[AQ], kv[AK];
     auto prologue = [&]() {
-        if constexpr (W16) {
+        if constexpr (W16 && !KV) {
             if (g < r_end) load_token_w<AQ, AK>(hd, g, e0, qv, kv);
         } else if constexpr (kFixed && !KV) {
             if (g < r_end) load_token_fixed<IO, AQ, AK>(hd, g, e0, qv, kv);
@@ -1431,7 +1500,9 @@ __global__ __launch_bounds__(kBlock) void apply_ids_kernel(Heads hd, Rotary rot,
         planes_of(g, ok, pt, ph, pw);
         const int64_t gn = g + kStep;
         double c[8], ss[8];
-        if constexpr (W16) {
+        if constexpr (W16 && KV) {
+            if (ok) kv_token_w<AQ, AK, NTS>(hd, pc, lf, g, e0, l, pt, ph, pw, pc.slots[g]);
+        } else if constexpr (W16) {
             uint4 qn[AQ], kn[AK];
             if (gn < r_end) load_token_w<AQ, AK>(hd, gn, e0, qn, kn);
             if (ok) {
@@ -1917,11 +1988,12 @@ static int compute_units()
 }
 
 // The fixed-head kernels cover the model's shape (8 Q heads, 2 KV heads); with a cache they also
-// need head_dim 256 and 16-bit I/O (fp32 copy chunks would not fit the register budget).
+// need head_dim 256, and in fp32 the sixteen-lane layout (eight lanes would carry twice the copy
+// chunks a lane): with the eight-lane hook, fp32 cache writes take the generic kernels.
 static bool fixed_heads(const Heads &h, const PagedKV &pc, int io)
 {
     if (h.nq != 8 || h.nk != 2) return false;
-    return !pc.k_cache || (h.head_dim == 256 && io != kIoF32);
+    return !pc.k_cache || (h.head_dim == 256 && (io != kIoF32 || !(test_hooks() & kHookF32EightLanes)));
 }
 
 // The fixed-head kernels' Q/K stores take the non-temporal hint (the NTS template argument) out of
@@ -1995,6 +2067,13 @@ static hipError_t apply_dispatch(const Heads &h, const Rotary &r, const int32_t 
             }
         }
         if constexpr (IO == kIoF32) {
+            if (pc.k_cache) {
+                // sixteen lanes a token, one step per workgroup at every size (as the 16-bit kernel)
+                const unsigned kv_blocks = (unsigned)((h.n_tokens + kTokPerBlockW - 1) / kTokPerBlockW);
+                if (nts) apply_kv_f32w_kernel<8, 2, true><<<kv_blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
+                else apply_kv_f32w_kernel<8, 2, false><<<kv_blocks, kBlock, 0, st>>>(h, r, planes, ps, pc);
+                return hipGetLastError();
+            }
             if (!(test_hooks() & kHookF32EightLanes)) {
                 // sixteen lanes a token: the same grid policy over 16-token workgroup steps
                 const int64_t groups_w = (h.n_tokens + kTokPerBlockW - 1) / kTokPerBlockW;
@@ -2051,6 +2130,11 @@ static hipError_t apply_ids_dispatch(const Heads &h, const Rotary &r, const Scan
             }
         }
         if constexpr (IO == kIoF32) {
+            if (pc.k_cache) {
+                if (nts) apply_ids_kernel<IO, 8, 2, true, true, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+                else apply_ids_kernel<IO, 8, 2, true, false, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
+                done = true;
+            }
             if (!done && !(test_hooks() & kHookF32EightLanes)) {
                 if (nts) apply_ids_kernel<IO, 8, 2, false, true, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);
                 else apply_ids_kernel<IO, 8, 2, false, false, true><<<blocks, kBlock, 0, st>>>(h, r, s, pc, part_log);

@@ -86,8 +86,10 @@ const char *mrope_last_error(void);
  *   MROPE_HOOK_FUSED_SCAN_FIRST  always the scan-first fused kernel (8 Q + 2 K heads, no cache write)
  *   MROPE_HOOK_SCAN_FALLBACK     scan-first kernel whose rotation workgroups derive their planes
  *                                themselves instead of waiting for the scan's handover
- *   MROPE_HOOK_F32_EIGHT_LANES   mrope_apply in fp32 with eight lanes a token (two 16-byte loads per
- *                                head and lane) instead of sixteen */
+ *   MROPE_HOOK_F32_EIGHT_LANES   fp32 with eight lanes a token (two 16-byte loads per head and lane)
+ *                                instead of sixteen: mrope_apply, mrope_apply_ids, and the cache
+ *                                writes of mrope_apply_kv / mrope_apply_ids_kv (then the generic
+ *                                kernels, one head at a time) */
 #define MROPE_HOOK_FUSED_CHUNKED 1
 #define MROPE_HOOK_FUSED_SCAN_FIRST 2
 #define MROPE_HOOK_SCAN_FALLBACK 4

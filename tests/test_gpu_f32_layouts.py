@@ -1,7 +1,9 @@
-"""GPU parity of mrope_apply and of the chunked fused mrope_apply_ids in fp32 in both lane layouts:
-sixteen lanes a token (the default) and eight (MROPE_HOOK_F32_EIGHT_LANES).  Each is compared with the oracle (fp32 gate) and with the other
-bit for bit, in place and out of place, on strided views, and past the size from which in-place
-stores take the non-temporal hint."""
+"""GPU parity of mrope_apply, of the fused mrope_apply_ids and of the cache-writing calls
+(mrope_apply_kv, mrope_apply_ids_kv) in fp32 in both lane layouts: sixteen lanes a token (the default
+for 8 Q + 2 K heads) and eight (MROPE_HOOK_F32_EIGHT_LANES; for the cache writes, the generic
+kernels).  Each is compared with the oracle (fp32 gate) and with the other bit for bit, in place and
+out of place, on strided views, and past the size from which in-place stores take the non-temporal
+hint."""
 import numpy as np
 import pytest
 import torch
@@ -116,3 +118,62 @@ def test_f32_fused_layouts_match_oracle_and_each_other(seed, n_seqs, max_len, pl
         compare_heads(k, kn, epl, "f32", what=f"fused {kernel} {name} k")
     for a, c in zip(res["sixteen"], res["eight"]):
         np.testing.assert_array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+def _kv_case(b, slots_seed, block_size, with_v, fused):
+    """One fp32 cache-writing call on fresh device copies of seeded inputs: returns the inputs (q, k,
+    v, slots, cache blocks) and the device results (q, k cache, v cache or None)."""
+    from test_gpu_kv import make_slots, new_cache, v_heads
+    qn, kn = b.qk()
+    vn = v_heads(b)
+    slots, nb = make_slots(slots_seed, b.n_tokens, block_size=block_size)
+    q, k, v = dev_heads(qn, "f32"), dev_heads(kn, "f32"), dev_heads(vn, "f32")
+    kc = new_cache(nb, block_size, 2, 256, "f32", -7.0)
+    vc = new_cache(nb, block_size, 2, 256, "f32", -7.0) if with_v else None
+    sl = torch.from_numpy(slots).cuda()
+    if fused:
+        mr.apply_ids_kv(q, k, v if with_v else None, i32(b.ids), i32(b.cu_seqlens), kc, vc, sl, MARKER)
+    else:
+        pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
+        mr.apply_kv(q, k, v if with_v else None, pl, kc, vc, sl)
+    np.testing.assert_array_equal(host_heads(k), kn, err_msg="k input changed")
+    np.testing.assert_array_equal(host_heads(v), vn, err_msg="v input changed")
+    return (qn, kn, vn, slots, nb), q, kc, vc
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("with_v,block_size", [(True, 16), (False, 5)])
+def test_f32_cache_writes_layouts_match_oracle_and_each_other(fused, with_v, block_size):
+    """mrope_apply_kv and mrope_apply_ids_kv in fp32: the sixteen-lane kernels (the default for 8 Q +
+    2 K heads of 256) and the generic eight-lane path (the hook) against the oracle -- Q in place, K
+    rows in the paged cache, V rows bit-exact, rows no valid slot points at untouched, negative slots
+    and slots past the cache skipped -- and bit for bit against each other; a block size of 5 takes
+    the division path."""
+    from test_gpu_kv import check_caches
+    b = synth.random_batch(641 + block_size, 40, max_len=700, dtype="f32")
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    say(f"case: fp32 cache writes fused={fused} v={with_v} block={block_size} tokens={b.n_tokens}")
+    res = _both_layouts(lambda: _kv_case(b, 642, block_size, with_v, fused))
+    for name, ((qn, kn, vn, slots, nb), q, kc, vc) in res.items():
+        compare_heads(host_heads(q), qn, epl, "f32", what=f"{name} q")
+        n = check_caches(kc, vc, slots, nb, block_size, kn, vn, epl, "f32", -7.0, f"{name} cache")
+        assert n > 0.9 * b.n_tokens
+    _, q16, kc16, vc16 = res["sixteen"]
+    _, q8, kc8, vc8 = res["eight"]
+    assert torch.equal(q16.view(torch.int32), q8.view(torch.int32))
+    assert torch.equal(kc16.view(torch.int32), kc8.view(torch.int32))
+    if with_v:
+        assert torch.equal(vc16.view(torch.int32), vc8.view(torch.int32))
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_f32_cache_writes_past_the_store_hint_size(fused):
+    """48 x 4,096 fp32 tokens with V: Q written in place past the size from which its stores take
+    the non-temporal hint; every Q element and every K cache row against the oracle."""
+    from test_gpu_kv import check_caches
+    b = synth.random_batch(651, 48, max_len=4096, min_len=4096, dtype="f32")
+    epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
+    say(f"case: fp32 cache writes past the hint size fused={fused} tokens={b.n_tokens}")
+    (qn, kn, vn, slots, nb), q, kc, vc = _kv_case(b, 652, 16, True, fused)
+    compare_heads_all(q, qn, epl, "f32", what="q")
+    check_caches(kc, vc, slots, nb, 16, kn, vn, epl, "f32", -7.0, "cache")
