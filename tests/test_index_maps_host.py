@@ -1,11 +1,12 @@
-"""Index arithmetic of two kernels, restated in Python and checked on the CPU over many shapes.
+"""Index arithmetic of the kernels, restated in Python and checked on the CPU over many shapes.
 
 decode_kernel maps (lane, round, item slot) to a chunk of Q, K or V; copy_rest_kernel maps
-(workgroup, lane, chunk) to bytes of an out-of-place head.  Both map with arithmetic that a GPU
-test exercises for a few shapes only, and a mistake there reads or writes outside a buffer.  These
-tests restate each mapping as the kernel source computes it (the two must be changed together)
-and check, for every shape in a grid, that every access stays inside its buffer and that each
-output byte is written exactly once.
+(workgroup, lane, chunk) to bytes of an out-of-place head; the scan-first grid maps workgroups to
+scans and parts; the sixteen-lane fp32 cache write maps (token group, lane, vector) to Q, K and V
+elements and cache rows.  They map with arithmetic that a GPU test exercises for a few shapes only,
+and a mistake there reads or writes outside a buffer.  These tests restate each mapping as the
+kernel source computes it (the two must be changed together) and check that every access stays
+inside its buffer and that each output element is written exactly once.
 """
 import itertools
 
@@ -213,3 +214,61 @@ def test_scan_first_scans_run_ahead_of_their_parts():
                 continue
             chunk = i * 32 // 512
             assert pos_scan[chunk // 4] < b, (n, i)
+
+
+# ------------------------------------------------------------------ fp32 cache writes, sixteen lanes
+
+
+def _kv_w_lane_elements(l):
+    """kv_token_w for lane l of a token's sixteen: (rotated dims of each Q/K head, K pass-through
+    dims, V dims), each a list of the first elements of the lane's 4-element vectors."""
+    m, half = l >> 1, l & 1
+    e0 = 32 * half + 4 * m
+    kpass = [64 + 4 * (l + 16 * i) for i in range(3)]
+    vdims = [4 * (l + 16 * i) for i in range(4)]
+    return [e0], kpass, vdims
+
+
+def test_f32_cache_write_lane_map_covers_each_head_once():
+    """Over a token's sixteen lanes: the rotated vectors tile dims 0..63 of a head, the K
+    pass-through vectors dims 64..255 and the V vectors dims 0..255, each element exactly once; a
+    lane's rotate-half partner (l ^ 1) holds the dims 32 away (x_j against x_{j+32})."""
+    rot = np.zeros(64, int)
+    kp = np.zeros(256, int)
+    vv = np.zeros(256, int)
+    for l in range(16):
+        r, k, v = _kv_w_lane_elements(l)
+        for e in r:
+            rot[e:e + 4] += 1
+        for e in k:
+            kp[e:e + 4] += 1
+        for e in v:
+            vv[e:e + 4] += 1
+        (rp,), _, _ = _kv_w_lane_elements(l ^ 1)
+        assert abs(rp - r[0]) == 32 and (r[0] < 32) == (l % 2 == 0)
+    assert (rot == 1).all()
+    assert (kp[:64] == 0).all() and (kp[64:] == 1).all()
+    assert (vv == 1).all()
+    # one instruction (fixed vector index) of the sixteen lanes covers 256 contiguous bytes
+    for i in range(3):
+        firsts = sorted(64 + 4 * (l + 16 * i) for l in range(16))
+        assert firsts == list(range(firsts[0], firsts[0] + 64, 4))
+
+
+def test_f32_cache_write_grid_covers_every_token_once():
+    """apply_kv_f32w_kernel: workgroup b, thread t, step s -> token b * 16 + (t >> 6) * 4 +
+    ((t & 63) >> 4) + s * stride; with the host's grid (one step per workgroup) every token is
+    taken by exactly one sixteen-lane group and no group reads past the last token."""
+    for n in (1, 15, 16, 17, 255, 4096, 100003):
+        blocks = (n + 15) // 16
+        seen = np.zeros(n, int)
+        for b in range(blocks):
+            for t in range(0, 256, 16):  # one thread per sixteen-lane group
+                G = b * 16 + (t >> 6) * 4
+                stride = blocks * 16
+                while G < n:
+                    g = G + ((t & 63) >> 4)
+                    if g < n:
+                        seen[g] += 1
+                    G += stride
+        assert (seen == 1).all(), n
