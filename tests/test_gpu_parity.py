@@ -548,24 +548,26 @@ def test_fp32_past_the_store_hint_size(fused):
     _full_prefill(_image_batch("40x4096-image-f32", 12, 40, 4096, "f32"), fused=fused)
 
 
-@pytest.mark.parametrize("seed,total,hi", [(12, 333333, 3000), (15, 1 << 19, 300)])
-def test_ragged_past_the_size_thresholds(seed, total, hi):
-    """Ragged batches past the sizes where the fused kernel splits every chunk in two, where
-    planes_out makes mrope_apply_ids two launches and where stores take the non-temporal hint: a
-    total that leaves the last chunk partial (333,333 tokens, 408 sequences) and 3,426 short
-    sequences (more than one 64-sequence window per chunk).  Scalars, planes and every rotated
-    element in full, for the fused call with and without planes_out, out of place (inputs
-    untouched), and for planes + apply."""
+@pytest.mark.parametrize("seed,total,hi,dtype", [(12, 333333, 3000, "bf16"), (15, 1 << 19, 300, "bf16"),
+                                                  (16, 400_001, 2000, "f16")])
+def test_ragged_past_the_size_thresholds(seed, total, hi, dtype):
+    """Ragged batches past the sizes where mrope_apply takes one-step workgroups and
+    mrope_apply_ids the scan-first kernel, where planes_out makes mrope_apply_ids two launches and
+    where stores take the non-temporal hint: a total that leaves the last chunk partial (333,333
+    tokens, 408 sequences), 3,426 short sequences (more than one 64-sequence window per chunk), and
+    the same kernels in fp16 (400,001 tokens).  Scalars, planes and every rotated element in full,
+    for the fused call with and without planes_out, out of place (inputs untouched), and for
+    planes + apply."""
     lengths, kinds = synth.ragged_lengths(seed, total, hi=hi)
     g = np.random.default_rng(seed)
     placed = [int(g.integers(0, max(1, n - 67))) if k else None for n, k in zip(lengths, kinds)]
-    b = synth._batch(f"ragged{seed}", seed, lengths, placed, "bf16")
+    b = synth._batch(f"ragged{seed}-{dtype}", seed, lengths, placed, dtype)
     say(f"case: {b.name} tokens={b.n_tokens} seqs={b.n_seqs}")
     qn, kn = b.qk()
     ids, cu = i32(b.ids), i32(b.cu_seqlens)
     epl, est, eam, eog = _oracle_planes(b)
     for mode in ("fused", "fused_planes_out", "fused_out_of_place", "planes_apply"):
-        q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+        q, k = dev_heads(qn, dtype), dev_heads(kn, dtype)
         pl = torch.full((3, b.n_tokens), -9, dtype=torch.int32, device="cuda")
         if mode == "fused":
             st, am, og, fl, _ = mr.apply_ids(q, k, ids, cu, MARKER)
@@ -585,8 +587,8 @@ def test_ragged_past_the_size_thresholds(seed, total, hi):
         np.testing.assert_array_equal(fl.cpu().numpy(), expected_flags(b, eog), err_msg=f"{mode} flags")
         if mode in ("fused_planes_out", "planes_apply"):
             np.testing.assert_array_equal(pl.cpu().numpy(), epl, err_msg=f"{mode} planes")
-        compare_heads_all(q, qn, epl, "bf16", what=f"{mode} q")
-        compare_heads_all(k, kn, epl, "bf16", what=f"{mode} k")
+        compare_heads_all(q, qn, epl, dtype, what=f"{mode} q")
+        compare_heads_all(k, kn, epl, dtype, what=f"{mode} k")
         del q, k, pl
         torch.cuda.empty_cache()
 
