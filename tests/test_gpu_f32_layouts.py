@@ -79,17 +79,32 @@ def test_f32_layouts_on_strided_views():
         compare_heads(k, kn, epl, "f32", what=f"{name} view k")
 
 
-def test_f32_sixteen_lanes_past_the_store_hint_size():
-    """48 x 4,096 fp32 tokens write 402 MB in place: the hinted stores; every element compared."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_f32_layouts_past_the_store_hint_size(fused):
+    """48 x 4,096 fp32 tokens write 402 MB in place: the hinted stores of both layouts, through
+    mrope_apply and mrope_apply_ids; the default layout's every element against the oracle, the
+    other's bit for bit against it."""
     b = synth.random_batch(621, 48, max_len=4096, min_len=4096, dtype="f32")
     qn, kn = b.qk()
     pl, *_ = mr.planes(i32(b.ids), i32(b.cu_seqlens), MARKER)
     epl, *_ = oracle.planes(b.ids, b.cu_seqlens, MARKER)
-    q, k = dev_heads(qn, "f32"), dev_heads(kn, "f32")
-    say(f"case: fp32 sixteen lanes, {b.n_tokens} tokens")
-    mr.apply(q, k, pl)
+    say(f"case: fp32 layouts past the hint size, fused={fused}, {b.n_tokens} tokens")
+
+    def run():
+        q, k = dev_heads(qn, "f32"), dev_heads(kn, "f32")
+        if fused:
+            mr.apply_ids(q, k, i32(b.ids), i32(b.cu_seqlens), MARKER)
+        else:
+            mr.apply(q, k, pl)
+        torch.cuda.synchronize()
+        return q, k
+
+    res = _both_layouts(run)
+    q, k = res["sixteen"]
     compare_heads_all(q, qn, epl, "f32", what="q")
     compare_heads_all(k, kn, epl, "f32", what="k")
+    for a, c in zip(res["sixteen"], res["eight"]):
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32)), "layouts differ"
 
 
 @pytest.mark.parametrize("seed,n_seqs,max_len", [(631, 1, 110), (632, 40, 900), (633, 6, 4096)])
