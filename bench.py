@@ -556,6 +556,51 @@ def f32_mode(args, dev, stream):
                       "kernels": out}), flush=True)
 
 
+def kv_mode(args, dev, stream):
+    """The prefill cache writes in bf16 -- mrope_apply_kv (planes given) and mrope_apply_ids_kv
+    (planes from ids): Q rotated in place, K rotated and V copied whole into 16-token paged K/V
+    caches through a random permutation of the slots -- on 64 x 4,096 image prompts and on the
+    1,048,576-token ragged batch.  Per-launch events, three rounds of `steps` launches after 5
+    untimed ones each."""
+    import numpy as np
+    import torch
+
+    import canvas_rope_rotary_amd as mr
+    from canvas_rope_rotary_amd import synth
+
+    # per token: Q's rotated dims read and written, K and V heads read whole and written whole into
+    # the cache, the slot, and the planes (12 B) or the id (4 B)
+    kv_bytes = 8 * 64 * 2 * 2 + 2 * (2 * 256 * 2) * 2 + 8
+    res = {}
+    for cfg in (synth.config2(), synth.config5()):
+        L = cfg.n_tokens
+        log(f"kv: {cfg.name}")
+        b = Batch(cfg, dev)
+        b.make_planes()
+        v = torch.from_numpy(synth.to_dtype(synth.normal(cfg.seed, 77, L * 2 * 256), "bf16").view(np.int16)
+                             ).view(torch.bfloat16).view(L, 2, 256).to(dev)
+        nb = (L + 15) // 16
+        kc = torch.zeros((nb, 16, 2, 256), dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros_like(kc)
+        slots = torch.from_numpy(np.random.default_rng(cfg.seed).permutation(nb * 16)[:L].astype(np.int64)).to(dev)
+        calls = {"mrope_apply_kv": (lambda: mr.apply_kv(b.q, b.k, v, b.planes, kc, vc, slots), L * (kv_bytes + 12)),
+                 "mrope_apply_ids_kv": (lambda: mr.apply_ids_kv(b.q, b.k, v, b.ids, b.cu, kc, vc, slots,
+                                                                synth.IMAGE_ID, workspace=b.ws), L * (kv_bytes + 4))}
+        durs = {c: [] for c in calls}
+        for rnd in range(3):
+            for c, (fn, _) in calls.items():
+                for _ in range(5):
+                    fn()
+                d, _ = per_launch(fn, args.steps, stream)
+                durs[c] += d
+        res[cfg.name] = {"tokens": L, "algorithmic_bytes_per_launch": {c: v_[1] for c, v_ in calls.items()},
+                         "kernels": {c: dict(summary(durs[c]), gbs_p50=calls[c][1] / pct(durs[c], 0.5) / 1e9)
+                                     for c in calls}}
+        del b, v, kc, vc, slots
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "kv", "workloads": res}), flush=True)
+
+
 def small_config_bench(args, dev, stream):
     """Configs 1 (one fp32 image prompt through mrope_apply_ids) and 4 (a decode step of 4,096
     sequences): launch- and latency-bound steps, shorter than the host's time to launch them, so
@@ -752,12 +797,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--extras", action="store_true",
                     help="also time L=110 fp32, fp16/fp32 I/O, out of place, the K/V cache write and decode")
-    ap.add_argument("--mode", choices=("bench", "copy", "counters", "pattern", "f32"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "copy", "counters", "pattern", "f32", "kv"), default="bench",
                     help="copy: only a plain 1 GiB device copy, repeated (calibrates rocprofv3 HBM counters); "
                          "counters: summarize four rocprofv3 --pmc run directories (no GPU) into "
                          "profiles/hbm_counters.json; pattern: the rotary kernels beside reference kernels "
                          "that move the same bytes without the arithmetic (bench_pattern.hip); f32: "
-                         "mrope_apply in fp32 in both lane layouts")
+                         "the rotary calls and the cache writes in fp32 in both lane layouts; kv: the "
+                         "cache writes in bf16")
     ap.add_argument("--fetch", help="counters mode: FETCH_SIZE run of the bench")
     ap.add_argument("--write", help="counters mode: WRITE_SIZE run of the bench")
     ap.add_argument("--fetch-copy", help="counters mode: FETCH_SIZE run of --mode copy")
@@ -796,6 +842,9 @@ def main():
         return
     if args.mode == "f32":
         f32_mode(args, dev, stream)
+        return
+    if args.mode == "kv":
+        kv_mode(args, dev, stream)
         return
     if args.config in (1, 4):
         small_config_bench(args, dev, stream)
