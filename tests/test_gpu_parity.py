@@ -677,6 +677,82 @@ def test_device_epoch_mode_through_c_abi():
     assert hdr == 4
 
 
+def _fused_device_epoch(lib, ws, q, k, b, stream):
+    """mrope_apply_ids through the C ABI with epoch 0 (the workspace's device counter), in place;
+    returns (start, amount, origin, seq_flags)."""
+    p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    ids, cu = i32(b.ids), i32(b.cu_seqlens)
+    n = b.n_seqs
+    st, am, og, fl = (torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(4))
+    dt = {torch.bfloat16: 1, torch.float16: 2, torch.float32: 0}[q.dtype]
+    ws.ensure(b.n_tokens)
+    rc = lib.mrope_apply_ids(p(q), q.stride(0), q.stride(1), q.shape[1], p(k), k.stride(0), k.stride(1), k.shape[1],
+                             b.n_tokens, q.shape[2], 64, dt, 1e7, None, None, p(ids), p(cu), n, MARKER, 67, None,
+                             None, None, None, 0, p(st), p(am), p(og), p(fl), ws.ptr, ws.capacity, 0, stream)
+    assert rc == 0, mr._lib.load().mrope_last_error()
+    return st, am, og, fl
+
+
+def test_device_epoch_advances_once_per_call():
+    """epoch = 0 on one workspace, a mix of calls -- mrope_planes and the chunked fused kernel on
+    small batches, the chunked kernel with other head shapes on 300,000 tokens (1,172 workgroups),
+    the scan-first kernel forced on a small batch: each gives the oracle's scalars and rotation, and
+    afterwards the device counter has advanced exactly once per call (the header's next word, which
+    the library does not use, stays zero)."""
+    lib = mr._lib.load()
+    ws = mr.Workspace(300_000)  # sized once: a larger workspace would start a new counter
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = 0
+
+    def fused(b, nq=8, nk=2, D=256, hooks=0):
+        nonlocal calls
+        x = synth.normal(b.seed, 91, b.n_tokens * (nq + nk) * D).reshape(b.n_tokens, nq + nk, D)
+        xb = synth.to_dtype(x, "bf16")
+        qn, kn = np.ascontiguousarray(xb[:, :nq]), np.ascontiguousarray(xb[:, nq:])
+        q, k = dev_heads(qn, "bf16"), dev_heads(kn, "bf16")
+        prev = mr._lib.set_test_hooks(hooks)
+        try:
+            st, am, og, fl = _fused_device_epoch(lib, ws, q, k, b, stream)
+        finally:
+            mr._lib.set_test_hooks(prev)
+        calls += 1
+        epl, est, eam, eog = _oracle_planes(b)
+        for got, want, what in ((st, est, "start"), (am, eam, "amount"), (og, eog, "origin")):
+            np.testing.assert_array_equal(got.cpu().numpy(), want, err_msg=f"call {calls} {what}")
+        compare_heads_all(q, qn, epl, "bf16", what=f"call {calls} q")
+        compare_heads_all(k, kn, epl, "bf16", what=f"call {calls} k")
+
+    def planes(b):
+        nonlocal calls
+        ids, cu = i32(b.ids), i32(b.cu_seqlens)
+        L, n = b.n_tokens, b.n_seqs
+        pl = torch.empty((3, L), dtype=torch.int32, device="cuda")
+        st, am, og, fl = (torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(4))
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        ws.ensure(L)
+        assert lib.mrope_planes(p(ids), p(cu), n, L, MARKER, 0, None, None, None, p(pl), L, p(st), p(am), p(og),
+                                p(fl), ws.ptr, ws.capacity, 0, stream) == 0
+        calls += 1
+        _check_scan(b, pl, st, am, og, fl, f"call {calls} planes")
+
+    say("case: device epochs, small planes and fused calls")
+    planes(synth.random_batch(71, 40, max_len=700))
+    fused(synth.random_batch(72, 30, max_len=900))
+    say("case: device epochs, 300,000 tokens with 4 Q + 1 K heads of 128 (large grid)")
+    lengths, kinds = synth.ragged_lengths(73, 300_000, hi=3000)
+    g = np.random.default_rng(73)
+    placed = [int(g.integers(0, max(1, n - 67))) if kd else None for n, kd in zip(lengths, kinds)]
+    fused(synth._batch("ragged73", 73, lengths, placed, "bf16"), nq=4, nk=1, D=128)
+    say("case: device epochs, scan-first kernel forced on a small batch")
+    fused(synth.random_batch(74, 20, max_len=1500), hooks=mr._lib.HOOK_FUSED_SCAN_FIRST)
+    fused(synth.random_batch(75, 1, max_len=110, min_len=110))
+    planes(synth.random_batch(76, 3, max_len=300))
+    torch.cuda.synchronize()
+    hdr = ws.view[:8].view(torch.int32).cpu().numpy()
+    assert hdr[0] == calls, f"device epoch {hdr[0]} after {calls} calls"
+    assert hdr[1] == 0, f"header word 1 changed to {hdr[1]}"
+
+
 def test_graph_replays_with_new_inputs():
     """planes + apply captured in a HIP graph; between replays new ids and Q/K are copied into the
     captured buffers (eager work in between); every replay matches the oracle."""
